@@ -1,0 +1,239 @@
+"""Benchmark: paged MLA decode on one MI355X.
+
+Workload (default): long-context decode, batch 16, q_len 1, 16 heads, 65,536
+cached tokens per sequence in 64-token pages of 576 bf16 (512 latent + 64
+rope), random page table, N(0,1) values, scale 1/sqrt(192), bf16 out.
+
+A step is one mla_decode call (split-decode kernel + merge kernel) over inputs
+already resident in HBM.  Prints one JSON line:
+  value      = algorithmic bytes per call / wall time per call  (GB/s, whole job)
+  roofline   = the split-decode kernel alone: algorithmic bytes / its mean
+               duration (HIP events on the launch stream) vs 8 TB/s HBM
+  cpu_baseline = the fp64 oracle on a bounded sample of the same workload, on
+               this host's cores (context only)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", f)
+                  for f in ("mla_kernels.hip", "mla_internal.h", "plan.cpp", "mla_api.cpp")]
+
+WORKLOAD_TEXT = {
+    "tiny": "MLA decode: batch 1, q_len 1, 16 heads, one contiguous 1024-token page, fp32 out",
+    "paged": "paged MLA decode: batch 16, q_len 1, 16 heads, 4096 tokens each, page 64, bf16 out",
+    "two_token": "paged MLA decode: batch 32, q_len 2 (no mask), 16 heads, 16384 tokens each, page 64, bf16 out",
+    "long": "long-context paged MLA decode: batch 16, q_len 1, 16 heads, 65536 tokens each, page 64, bf16 out",
+    "ragged": "ragged paged MLA decode: batch 64, q_len 1, 128 heads, lengths U[1024, 65536], page 64, bf16 out",
+}
+
+
+def algorithmic_bytes(prob) -> int:
+    """Bytes the decode must move at least once: every cached row once (K and V share it),
+    the query, the output, the lse, and the used block-table entries."""
+    L = prob.cache_seqlens.astype(np.int64)
+    R = prob.q_len * prob.num_heads
+    out_elem = 4 if prob.out_fp32 else 2
+    pages = ((L + prob.page_size - 1) // prob.page_size).sum()
+    return int(L.sum() * 576 * 2 + prob.batch * R * 576 * 2 + prob.batch * R * 512 * out_elem
+               + prob.batch * R * 4 + pages * 4)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config: str):
+    """HBM bytes per split-decode launch from the committed counter summary, or None when
+    the summary is missing, for another workload, or older than the kernel sources."""
+    try:
+        with open(PROFILE_COUNTERS) as fh:
+            c = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    entry = c.get(config)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(prob, budget_s: float = 15.0):
+    """Time the oracle on whole sequences of the workload until about budget_s seconds."""
+    from oracle import mla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    order = list(range(prob.batch))
+    done, t_total, tokens, rows_bytes = [], 0.0, 0, 0
+    for b in order:
+        t0 = time.perf_counter()
+        orc.decode_sequence(prob.q[b], prob.kv_cache, prob.block_table[b], int(prob.cache_seqlens[b]),
+                            prob.softmax_scale, prob.page_size)
+        t_total += time.perf_counter() - t0
+        done.append(b)
+        tokens += int(prob.cache_seqlens[b])
+        if t_total >= budget_s:
+            break
+    frac = tokens / max(1, int(prob.cache_seqlens.sum()))
+    sample_bytes = algorithmic_bytes(prob) * frac
+    return {
+        "value": round(sample_bytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {prob.batch} sequences ({tokens} tokens, {100 * frac:.1f}% of the call), "
+                  f"fp64 NumPy, {t_total:.2f} s; extrapolated {t_total / frac * 1e6:.0f} us/call",
+        "us_per_call_extrapolated": round(t_total / frac * 1e6, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="long", choices=list(WORKLOAD_TEXT))
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this build runs the decode "
+              "on a single MI355X and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_decode_attention_paged_amd import binding as B
+    from mla_decode_attention_paged_amd import inputs as gen
+    from mla_decode_attention_paged_amd.device import Runner
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()  # fail loudly if the HIP library is missing
+    print(f"[bench] generating {args.config} inputs", file=sys.stderr, flush=True)
+    prob = gen.make_config(args.config, seed=args.seed)
+    algo = algorithmic_bytes(prob)
+
+    t0 = time.perf_counter()
+    plan_probe = B.Plan(__import__("mla_decode_attention_paged_amd.device", fromlist=["x"]).problem_struct(prob),
+                        prob.cache_seqlens)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    del plan_probe
+    r = Runner(prob)
+    stream = torch.cuda.current_stream()
+    info = r.plan.info()
+
+    for _ in range(args.warmup):
+        r()
+    torch.cuda.synchronize()
+
+    # whole-call throughput: K back-to-back calls
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        r()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+
+    # per-call event timing (same stream), and the split-decode kernel alone
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        r()
+        b.record(stream)
+    torch.cuda.synchronize()
+    call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        r(stages=B.MLA_STAGE_SPLIT)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    split_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    e0.record(stream)
+    for _ in range(args.steps):
+        r(stages=B.MLA_STAGE_MERGE)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    merge_us = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    # flushed per-call time: a 512 MB fill between calls evicts the 256 MB last-level cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    fl = []
+    for _ in range(min(args.steps, 20)):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        r()
+        b.record(stream)
+        torch.cuda.synchronize()
+        fl.append(a.elapsed_time(b) * 1e3)
+    del flush
+
+    status = B.mla_read_status(r.ws)
+    value = algo / wall / 1e9
+    achieved = algo / (split_us * 1e-6) / 1e9
+    traffic = measured_traffic(args.config)
+    result = {
+        "metric": "µs/call and achieved HBM GB/s (% of peak), MLA decode bs=16 H=16 ctx=64K",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 5),
+        "us_per_call": round(wall * 1e6, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "batch": prob.batch,
+                   "q_len": prob.q_len, "heads": prob.num_heads, "page_size": prob.page_size,
+                   "ctx_tokens_total": int(prob.cache_seqlens.sum()), "seed": prob.seed,
+                   "parallelism": "single GPU, split-KV over 256 CUs"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "split_decode_kernel", "kernel_us": round(split_us, 2),
+                     "algorithmic_bytes_per_launch": algo},
+        "timing_us": {"call_event_p10": round(float(np.percentile(call_us, 10)), 2),
+                      "call_event_p50": round(float(np.percentile(call_us, 50)), 2),
+                      "call_event_p90": round(float(np.percentile(call_us, 90)), 2),
+                      "call_flushed_p50": round(float(np.median(fl)), 2),
+                      "split_kernel_mean": round(split_us, 2), "merge_kernel_mean": round(merge_us, 2),
+                      "plan_host_us": round(plan_us, 1)},
+        "plan": {k: info[k] for k in ("num_workers", "grid_size", "num_segments", "num_partials", "num_combine")},
+        "status_word": status,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(prob, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

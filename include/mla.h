@@ -1,0 +1,185 @@
+/*
+ * mla.h -- paged Multi-Head Latent Attention (MLA) decode for AMD MI355X (gfx950).
+ *
+ * What is computed.  For every sequence b, query token i < q_len and head
+ * h < num_heads, with L = cache_seqlens[b] and R = q_len * num_heads rows
+ * (row r = i * num_heads + h):
+ *
+ *     k_t      = kv_cache[block_table[b][t / page_size]][t % page_size][0:576]
+ *     v_t      = k_t[0:512]
+ *     s_t      = softmax_scale * sum_d q[b][i][h][d] * k_t[d]        (d < 576)
+ *     lse      = log sum_{t<L} exp(s_t)                               (natural log)
+ *     out[:]   = sum_{t<L} exp(s_t - lse) * v_t
+ *
+ * This is standard attention S = Q K^T, P = softmax(S), O = P V ("Core
+ * mechanism", FlashMLA-ETAP summary on gist.science), in the absorbed MLA form
+ * where every head reads the same 576-wide cached row: 512 latent columns that
+ * double as V plus 64 rope columns (16 heads and 576-dim heads as in that
+ * page's "Limitations noted by the authors"; low-rank joint compression of the
+ * KV cache as in its "Implementation details").  Queries are 1-2 tokens over a
+ * context of up to 64K tokens ("Problem statement" on the same page).  The
+ * kernels evaluate it in the transposed order the page describes,
+ * S^T = K Q^T, P^T = softmax(S^T), O^T = V^T P^T, so the context length is the
+ * large matrix dimension and the R query rows the small one.
+ *
+ * The context of each sequence is split across compute units by a host-side
+ * planner (mla_plan); per-split partial results (out normalised over the
+ * split, and its lse) are merged by the log-sum-exp rule in a second kernel.
+ * Rows t >= L are never used, even if they hold NaN; block_table entries past
+ * ceil(L / page_size) are never read.
+ *
+ * Conventions for every function:
+ *   - extern "C", never throws, returns mla_status_t (except the few getters
+ *     documented otherwise);
+ *   - on any error nothing is launched and no output or workspace byte is
+ *     written; mla_last_error() then returns a message for this thread;
+ *   - device pointers are plain HIP device addresses; "stream" is a
+ *     hipStream_t passed as void* (NULL = the default stream); launches are
+ *     asynchronous on that stream;
+ *   - the library allocates no device memory; the caller owns every device
+ *     buffer (q, kv_cache, block_table, cache_seqlens, out, lse, workspace).
+ *
+ * bf16 values are IEEE-754 binary32 truncated to the upper 16 bits (bfloat16).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad shape, negative length, ... */
+  MLA_ERR_UNSUPPORTED = 2,        /* valid but not implemented (head dims, R, page size) */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MLA_ERR_HIP = 4,                /* a HIP runtime call failed; see mla_last_error() */
+  MLA_ERR_PLAN_MISMATCH = 5       /* plan used with a problem it was not made for */
+} mla_status_t;
+
+typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype_t;
+
+/* Shapes of one decode call. */
+typedef struct {
+  int32_t batch;              /* B >= 1 */
+  int32_t q_len;              /* S_q >= 1 query tokens per sequence (no mask between them) */
+  int32_t num_heads;          /* H >= 1; R = q_len * num_heads must be a multiple of 16, <= 128 */
+  int32_t head_dim_qk;        /* must be 576 (512 latent + 64 rope) */
+  int32_t head_dim_v;         /* must be 512 */
+  int32_t page_size;          /* P: tokens per cache page, a positive multiple of 16 */
+  int32_t num_pages;          /* physical pages in kv_cache (dimension 0) */
+  int32_t max_pages_per_seq;  /* row stride of block_table, in int32 entries */
+  mla_dtype_t out_dtype;      /* dtype of `out`: BF16 (round to nearest even) or FP32 */
+} mla_problem_t;
+
+/* Planner options.  Zero-initialise for defaults. */
+typedef struct {
+  int32_t num_cus;            /* compute units to plan for; 0 = ask the current HIP device */
+  int32_t force_splits;       /* 0 = cost model; k > 0 = cut every sequence into min(k, blocks)
+                                 near-equal parts, one work-group each (testing the merge) */
+  int32_t reserved[6];        /* must be zero */
+} mla_plan_options_t;
+
+/* Read-only summary of a plan (for tests and diagnostics). */
+typedef struct {
+  int32_t num_workers;        /* work-groups in the split-decode launch that have work */
+  int32_t grid_size;          /* work-groups launched (num_workers padded, times row groups) */
+  int32_t num_segments;       /* (sequence, token range) pieces over all workers */
+  int32_t num_partials;       /* partial-result slots (pieces of split sequences) */
+  int32_t num_combine;        /* sequences that need the merge kernel */
+  int32_t rows_per_group;     /* query rows one work-group handles (16 or 32) */
+  int32_t row_groups;         /* R / rows_per_group */
+  int32_t granule;            /* token granularity of split boundaries */
+  int64_t max_worker_cost;    /* planner cost units (16-token blocks + per-piece overhead) */
+  int64_t min_worker_cost;
+  int64_t metadata_bytes;     /* bytes uploaded by mla_plan_upload */
+  int64_t workspace_bytes;    /* == mla_plan_workspace_bytes() */
+} mla_plan_info_t;
+
+typedef struct mla_plan_s* mla_plan_t;   /* opaque, host memory only */
+
+/* Build a split-KV schedule for `problem` and the given context lengths.
+ * Host only; launches nothing.  cache_seqlens_host: B int32 values, each in
+ * [0, max_pages_per_seq * page_size].  The plan copies everything it needs.
+ * A plan is valid for the same problem and the same cache_seqlens values. */
+mla_status_t mla_plan(const mla_problem_t* problem, const int32_t* cache_seqlens_host,
+                      const mla_plan_options_t* options /* may be NULL */, mla_plan_t* plan_out);
+
+mla_status_t mla_plan_get_info(mla_plan_t plan, mla_plan_info_t* info);
+
+/* Copy the plan's pieces as int32 quadruples (seq, tok_begin, tok_end, slot; slot -1 =
+ * written straight to out/lse) in work-group order, followed by nothing else.
+ * `worker_offsets` (num_workers + 1 entries, may be NULL) receives each
+ * work-group's first piece index.  Capacities are in int32 elements. */
+mla_status_t mla_plan_get_segments(mla_plan_t plan, int32_t* segments, int64_t segments_capacity,
+                                   int32_t* worker_offsets, int64_t offsets_capacity);
+
+/* Device workspace the caller must provide to mla_plan_upload / mla_decode
+ * (schedule + fp32 partial results + a status word).  Returns 0 for a NULL plan. */
+size_t mla_plan_workspace_bytes(mla_plan_t plan);
+
+/* Copy the schedule into `workspace` (device, >= mla_plan_workspace_bytes bytes, 256-B
+ * aligned) and clear its status word, asynchronously on `stream`.  Must run once
+ * before the first mla_decode with this plan and workspace; the plan must stay
+ * alive until the copy has completed on the stream. */
+mla_status_t mla_plan_upload(mla_plan_t plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Paged MLA decode (two launches on `stream`: split decode, then the merge of
+ * split sequences).
+ *   q             [B, q_len, H, 576] bf16, contiguous, 16-B aligned
+ *   kv_cache      [num_pages, page_size, 576] bf16, contiguous, 16-B aligned
+ *   block_table   [B, max_pages_per_seq] int32; entries < ceil(L_b/page_size) must lie in
+ *                 [0, num_pages).  An entry outside that range is not dereferenced: its
+ *                 tokens are dropped and the workspace status word gets bit 0 set.
+ *   cache_seqlens [B] int32 on the device, the values the plan was made with (a smaller
+ *                 device value shortens the context; a larger one is clipped to the plan)
+ *   softmax_scale multiplies q . k before the softmax
+ *   out           [B, q_len, H, 512] of problem->out_dtype, 16-B aligned
+ *   lse           [B, q_len, H] fp32 natural-log LSE, or NULL
+ *   workspace     as uploaded by mla_plan_upload for this plan
+ * Sequences with L = 0 get out = 0 and lse = -inf.
+ * Calls that share a workspace must not overlap in time. */
+mla_status_t mla_decode(mla_plan_t plan, const void* q, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* cache_seqlens,
+                        float softmax_scale, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Launch only some of mla_decode's kernels (profiling aid): stages is a bit mask,
+ * MLA_STAGE_SPLIT runs the split-decode kernel, MLA_STAGE_MERGE the merge of split
+ * sequences (which reads the partials the last split stage wrote).
+ * mla_decode == mla_decode_stages(..., MLA_STAGE_ALL).  Same arguments and errors
+ * as mla_decode; stages outside MLA_STAGE_ALL is MLA_ERR_INVALID_ARGUMENT. */
+#define MLA_STAGE_SPLIT 1u
+#define MLA_STAGE_MERGE 2u
+#define MLA_STAGE_ALL 3u
+mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_cache,
+                               const int32_t* block_table, const int32_t* cache_seqlens,
+                               float softmax_scale, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               uint32_t stages);
+
+/* Test aid: write every sequence's logical rows, in token order, to rows_out
+ * [sum_b L_b, 576] bf16 (sequence b starts at row sum_{b'<b} L_b'), using the
+ * same page walk as mla_decode.  Bit-exact copy; async on `stream`. */
+mla_status_t mla_debug_gather(mla_plan_t plan, const void* kv_cache, const int32_t* block_table,
+                              void* rows_out, void* stream);
+
+/* Read the workspace status word (synchronises `stream`).  Bit 0: a block_table
+ * entry was out of range in some mla_decode since the last mla_plan_upload. */
+mla_status_t mla_read_status(const void* workspace, void* stream, int32_t* status_out);
+
+void mla_plan_destroy(mla_plan_t plan);            /* NULL is a no-op */
+const char* mla_status_string(mla_status_t status); /* static string */
+const char* mla_last_error(void);                  /* thread-local detail of the last failure */
+int32_t mla_abi_version(void);                     /* MLA_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,277 @@
+// C-ABI entry points: argument validation, workspace layout, launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "mla.h"
+#include "mla_internal.h"
+
+struct mla_plan_s {
+  mla::PlanImpl impl;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status_t fail(mla_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mla_status_t check_problem(const mla_problem_t* p) {
+  if (!p) return fail(MLA_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->batch < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", p->batch);
+  if (p->q_len < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "q_len must be >= 1 (got %d)", p->q_len);
+  if (p->num_heads < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_heads must be >= 1 (got %d)", p->num_heads);
+  if (p->page_size < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "page_size must be >= 1 (got %d)", p->page_size);
+  if (p->num_pages < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_pages must be >= 0 (got %d)", p->num_pages);
+  if (p->max_pages_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq must be >= 1 (got %d)", p->max_pages_per_seq);
+  if (p->out_dtype != MLA_DTYPE_BF16 && p->out_dtype != MLA_DTYPE_FP32)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "out_dtype must be MLA_DTYPE_BF16 or MLA_DTYPE_FP32");
+  if (p->head_dim_qk != mla::kDqk || p->head_dim_v != mla::kDv)
+    return fail(MLA_ERR_UNSUPPORTED, "head dims must be 576/512 (got %d/%d)", p->head_dim_qk, p->head_dim_v);
+  if (p->page_size % mla::kBlock != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "page_size must be a multiple of 16 (got %d)", p->page_size);
+  const int64_t R = (int64_t)p->q_len * p->num_heads;
+  if (R % 16 != 0 || R > mla::kMaxRows)
+    return fail(MLA_ERR_UNSUPPORTED, "q_len*num_heads must be a multiple of 16 and <= 128 (got %lld)",
+                (long long)R);
+  if ((int64_t)p->max_pages_per_seq * p->page_size > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "max_pages_per_seq * page_size exceeds int32");
+  return MLA_OK;
+}
+
+mla_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_PLAN_MISMATCH: return "plan does not match the call";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+mla_status_t mla_plan(const mla_problem_t* problem, const int32_t* cache_seqlens_host,
+                      const mla_plan_options_t* options, mla_plan_t* plan_out) {
+  if (!plan_out) return fail(MLA_ERR_INVALID_ARGUMENT, "plan_out is NULL");
+  *plan_out = nullptr;
+  mla_status_t s = check_problem(problem);
+  if (s != MLA_OK) return s;
+  if (!cache_seqlens_host) return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seqlens_host is NULL");
+  mla_plan_options_t opt{};
+  if (options) opt = *options;
+  for (int i = 0; i < 6; ++i)
+    if (opt.reserved[i] != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "options.reserved must be zero");
+  if (opt.num_cus < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "options.num_cus must be >= 0");
+  if (opt.force_splits < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "options.force_splits must be >= 0");
+  const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
+  for (int b = 0; b < problem->batch; ++b) {
+    int32_t L = cache_seqlens_host[b];
+    if (L < 0 || L > cap)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seqlens[%d] = %d outside [0, %lld]", b, L, (long long)cap);
+    if (L > 0 && problem->num_pages == 0)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seqlens[%d] = %d but num_pages is 0", b, L);
+  }
+  int32_t cus = opt.num_cus;
+  if (cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice (set options.num_cus to plan without a device)");
+    hipDeviceProp_t pr;
+    e = hipGetDeviceProperties(&pr, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    cus = pr.multiProcessorCount;
+  }
+  mla_plan_s* pl = new (std::nothrow) mla_plan_s();
+  if (!pl) return fail(MLA_ERR_INVALID_ARGUMENT, "out of host memory");
+  std::string err;
+  s = mla::build_plan(*problem, cache_seqlens_host, cus, opt.force_splits, pl->impl, err);
+  if (s != MLA_OK) {
+    delete pl;
+    return fail(s, "%s", err.c_str());
+  }
+  *plan_out = pl;
+  return MLA_OK;
+}
+
+mla_status_t mla_plan_get_info(mla_plan_t plan, mla_plan_info_t* info) {
+  if (!plan || !info) return fail(MLA_ERR_INVALID_ARGUMENT, "plan or info is NULL");
+  const mla::PlanImpl& p = plan->impl;
+  mla_plan_info_t r{};
+  r.num_workers = p.num_workers;
+  r.grid_size = p.grid;
+  r.num_segments = (int32_t)p.pieces.size();
+  r.num_partials = p.num_partials;
+  r.num_combine = (int32_t)p.merges.size();
+  r.rows_per_group = p.rows_per_group;
+  r.row_groups = p.row_groups;
+  r.granule = p.granule;
+  int64_t mx = 0, mn = INT64_MAX;
+  for (int64_t c : p.worker_cost) {
+    mx = c > mx ? c : mx;
+    mn = c < mn ? c : mn;
+  }
+  r.max_worker_cost = mx;
+  r.min_worker_cost = p.worker_cost.empty() ? 0 : mn;
+  r.metadata_bytes = (int64_t)p.meta_end;
+  r.workspace_bytes = (int64_t)p.ws_bytes;
+  *info = r;
+  return MLA_OK;
+}
+
+mla_status_t mla_plan_get_segments(mla_plan_t plan, int32_t* segments, int64_t segments_capacity,
+                                   int32_t* worker_offsets, int64_t offsets_capacity) {
+  if (!plan || !segments) return fail(MLA_ERR_INVALID_ARGUMENT, "plan or segments is NULL");
+  const mla::PlanImpl& p = plan->impl;
+  if (segments_capacity < 4 * (int64_t)p.pieces.size())
+    return fail(MLA_ERR_INVALID_ARGUMENT, "segments capacity %lld < %lld", (long long)segments_capacity,
+                (long long)(4 * p.pieces.size()));
+  if (worker_offsets && offsets_capacity < (int64_t)p.worker_off.size())
+    return fail(MLA_ERR_INVALID_ARGUMENT, "worker_offsets capacity too small");
+  for (size_t i = 0; i < p.pieces.size(); ++i) {
+    segments[4 * i + 0] = p.pieces[i].seq;
+    segments[4 * i + 1] = p.pieces[i].tok_begin;
+    segments[4 * i + 2] = p.pieces[i].tok_end;
+    segments[4 * i + 3] = p.pieces[i].slot;
+  }
+  if (worker_offsets)
+    for (size_t i = 0; i < p.worker_off.size(); ++i) worker_offsets[i] = p.worker_off[i];
+  return MLA_OK;
+}
+
+size_t mla_plan_workspace_bytes(mla_plan_t plan) { return plan ? plan->impl.ws_bytes : 0; }
+
+mla_status_t mla_plan_upload(mla_plan_t plan, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-B aligned");
+  if (workspace_bytes < plan->impl.ws_bytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < required %zu B", workspace_bytes,
+                plan->impl.ws_bytes);
+  hipError_t e = hipMemcpyAsync(workspace, plan->impl.meta_host.data(), plan->impl.meta_end,
+                                hipMemcpyHostToDevice, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan upload)");
+  return MLA_OK;
+}
+
+mla_status_t mla_decode(mla_plan_t plan, const void* q, const void* kv_cache, const int32_t* block_table,
+                        const int32_t* cache_seqlens, float softmax_scale, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_stages(plan, q, kv_cache, block_table, cache_seqlens, softmax_scale, out, lse, workspace,
+                           workspace_bytes, stream, MLA_STAGE_ALL);
+}
+
+mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_cache, const int32_t* block_table,
+                               const int32_t* cache_seqlens, float softmax_scale, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream, uint32_t stages) {
+  if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (stages == 0 || (stages & ~MLA_STAGE_ALL) != 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "stages must be a non-empty subset of MLA_STAGE_ALL");
+  const mla::PlanImpl& p = plan->impl;
+  if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if ((uintptr_t)q % 16 || (uintptr_t)kv_cache % 16 || (uintptr_t)out % 16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "q, kv_cache and out must be 16-B aligned");
+  if ((uintptr_t)block_table % 4 || (uintptr_t)cache_seqlens % 4 || (uintptr_t)lse % 4)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "block_table, cache_seqlens and lse must be 4-B aligned");
+  if ((uintptr_t)workspace % 256 != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-B aligned");
+  if (workspace_bytes < p.ws_bytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < required %zu B", workspace_bytes, p.ws_bytes);
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+
+  char* ws = (char*)workspace;
+  mla::DecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.kv = (const uint16_t*)kv_cache;
+  a.block_table = block_table;
+  a.seqlens = cache_seqlens;
+  a.worker_off = (const int32_t*)(ws + p.off_worker);
+  a.pieces = (const int32_t*)(ws + p.off_pieces);
+  a.out = out;
+  a.lse = lse;
+  a.part_lse = (float*)(ws + p.off_lse);
+  a.part_o = (float*)(ws + p.off_o);
+  a.status = (int32_t*)ws;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  a.rows = p.rows;
+  a.page_size = p.prob.page_size;
+  a.num_pages = p.prob.num_pages;
+  a.bt_stride = p.prob.max_pages_per_seq;
+  a.num_workers = p.num_workers;
+  a.row_groups = p.row_groups;
+  const bool f32 = p.prob.out_dtype == MLA_DTYPE_FP32;
+  if ((stages & MLA_STAGE_SPLIT) && p.grid > 0) {
+    int e = mla::launch_decode(a, p.rows_per_group, f32, p.grid, stream);
+    if (e) return fail(MLA_ERR_HIP, "split-decode launch: %s", mla::hip_error_string(e));
+  }
+  if ((stages & MLA_STAGE_MERGE) && !p.merges.empty()) {
+    mla::MergeArgs m{};
+    m.merges = (const int32_t*)(ws + p.off_merges);
+    m.part_lse = a.part_lse;
+    m.part_o = a.part_o;
+    m.out = out;
+    m.lse = lse;
+    m.rows = p.rows;
+    m.num_merges = (int32_t)p.merges.size();
+    int e = mla::launch_merge(m, f32, stream);
+    if (e) return fail(MLA_ERR_HIP, "merge launch: %s", mla::hip_error_string(e));
+  }
+  return MLA_OK;
+}
+
+mla_status_t mla_debug_gather(mla_plan_t plan, const void* kv_cache, const int32_t* block_table, void* rows_out,
+                              void* stream) {
+  if (!plan || !kv_cache || !block_table || !rows_out)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if ((uintptr_t)kv_cache % 16 || (uintptr_t)rows_out % 16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "kv_cache and rows_out must be 16-B aligned");
+  const mla::PlanImpl& p = plan->impl;
+  for (int b = 0; b < p.prob.batch; ++b) {
+    if (p.seqlens[b] == 0) continue;
+    int e = mla::launch_gather((const uint16_t*)kv_cache, block_table, (uint16_t*)rows_out, b, p.seqlens[b],
+                               p.row_offsets[b], p.prob.page_size, p.prob.max_pages_per_seq,
+                               p.prob.num_pages, stream);
+    if (e) return fail(MLA_ERR_HIP, "gather launch: %s", mla::hip_error_string(e));
+  }
+  return MLA_OK;
+}
+
+mla_status_t mla_read_status(const void* workspace, void* stream, int32_t* status_out) {
+  if (!workspace || !status_out) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace or status_out is NULL");
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, workspace, sizeof v, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (status)");
+  e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (status)");
+  *status_out = v;
+  return MLA_OK;
+}
+
+void mla_plan_destroy(mla_plan_t plan) { delete plan; }
+
+}  // extern "C"

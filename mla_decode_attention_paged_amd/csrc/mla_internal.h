@@ -1,0 +1,101 @@
+// Internal declarations shared by the C-ABI layer, the planner and the kernels.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "mla.h"
+
+namespace mla {
+
+constexpr int kDqk = 576;          // cached row width: 512 latent + 64 rope
+constexpr int kDv = 512;           // latent columns, also V
+constexpr int kBlock = 16;         // tokens per KV block (one MFMA M tile)
+constexpr int kWaves = 4;          // waves per work-group in the split-decode kernel
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxRows = 128;
+
+// Workspace layout (byte offsets from the workspace base).
+//   [0, 256)              status word (int32) + padding
+//   [kMetaOffset, ...)    worker offsets, pieces, merge items (int32)
+//   [off_lse, ...)        partial lse   [num_partials][R] fp32
+//   [off_o, ...)          partial out   [num_partials][R][512] fp32
+constexpr size_t kMetaOffset = 256;
+
+struct Piece {            // one (sequence, token range) handled by one work-group
+  int32_t seq, tok_begin, tok_end, slot;   // slot -1: write out/lse directly
+};
+
+struct MergeItem {        // one split sequence for the merge kernel
+  int32_t seq, slot_begin, num_slots, pad;
+};
+
+struct PlanImpl {
+  mla_problem_t prob{};
+  std::vector<int32_t> seqlens;
+  std::vector<int64_t> row_offsets;        // prefix sums of seqlens (debug gather)
+  int32_t num_cus = 0;
+  int32_t rows = 0;                        // R
+  int32_t rows_per_group = 16;             // 16 * NB
+  int32_t row_groups = 1;
+  int32_t granule = kBlock;
+  int32_t num_workers = 0;                 // with work
+  int32_t grid = 0;                        // launched work-groups
+  std::vector<int32_t> worker_off;         // num_workers + 1
+  std::vector<Piece> pieces;
+  std::vector<MergeItem> merges;
+  std::vector<int64_t> worker_cost;
+  int32_t num_partials = 0;
+  // workspace layout
+  size_t off_worker = 0, off_pieces = 0, off_merges = 0, meta_end = 0;
+  size_t off_lse = 0, off_o = 0, ws_bytes = 0;
+  std::vector<uint8_t> meta_host;          // bytes [0, meta_end) as uploaded
+};
+
+// Planner (pure host code).  Returns MLA_OK or an error with `err` filled.
+mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t num_cus,
+                        int32_t force_splits, PlanImpl& out, std::string& err);
+
+// Parameters of the split-decode kernel.
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* worker_off;
+  const int32_t* pieces;         // int32 quadruples
+  void* out;
+  float* lse;                    // may be null
+  float* part_lse;
+  float* part_o;
+  int32_t* status;
+  float scale_log2;              // softmax_scale * log2(e)
+  int32_t rows;                  // R
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t bt_stride;
+  int32_t num_workers;
+  int32_t row_groups;
+};
+
+struct MergeArgs {
+  const int32_t* merges;         // int32 quadruples
+  const float* part_lse;
+  const float* part_o;
+  void* out;
+  float* lse;
+  int32_t rows;
+  int32_t num_merges;
+};
+
+// Kernel launchers (mla_kernels.hip).  Return a HIP error code (0 = success).
+int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream);
+int launch_merge(const MergeArgs& a, bool out_fp32, void* stream);
+int launch_gather(const uint16_t* kv, const int32_t* block_table, uint16_t* rows_out, int32_t seq,
+                  int32_t length, int64_t row_offset, int32_t page_size, int32_t bt_stride,
+                  int32_t num_pages, void* stream);
+const char* hip_error_string(int code);
+
+}  // namespace mla

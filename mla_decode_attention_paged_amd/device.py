@@ -1,0 +1,48 @@
+"""Move a host problem (see inputs.py) to torch device tensors and run the library on it."""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as B
+
+
+def to_device(prob, device="cuda"):
+    """Host Problem -> dict of contiguous device tensors (bf16 bit patterns reinterpreted)."""
+    import torch
+    q = torch.from_numpy(prob.q.view(np.int16)).to(device).view(torch.bfloat16)
+    kv = torch.from_numpy(prob.kv_cache.view(np.int16)).to(device).view(torch.bfloat16)
+    bt = torch.from_numpy(prob.block_table).to(device)
+    sl = torch.from_numpy(prob.cache_seqlens.astype(np.int32)).to(device)
+    return {"q": q, "kv_cache": kv, "block_table": bt, "cache_seqlens": sl}
+
+
+def problem_struct(prob):
+    return B.make_problem(prob.batch, prob.q_len, prob.num_heads, prob.page_size, prob.num_pages,
+                          prob.max_pages_per_seq, out_fp32=prob.out_fp32)
+
+
+class Runner:
+    """Plan + workspace + outputs for one problem on one device; call() launches the decode."""
+
+    def __init__(self, prob, dev=None, num_cus=0, force_splits=0, device="cuda"):
+        import torch
+        self.prob = prob
+        self.dev = dev if dev is not None else to_device(prob, device)
+        self.plan = B.Plan(problem_struct(prob), prob.cache_seqlens, num_cus=num_cus, force_splits=force_splits)
+        self.ws = B.alloc_workspace(self.plan, device)
+        self.plan.upload(self.ws)
+        odt = torch.float32 if prob.out_fp32 else torch.bfloat16
+        self.out = torch.empty((prob.batch, prob.q_len, prob.num_heads, 512), dtype=odt, device=device)
+        self.lse = torch.empty((prob.batch, prob.q_len, prob.num_heads), dtype=torch.float32, device=device)
+
+    def __call__(self, stream=None, stages=B.MLA_STAGE_ALL):
+        d = self.dev
+        B.mla_decode(self.plan, d["q"], d["kv_cache"], d["block_table"], d["cache_seqlens"],
+                     self.prob.softmax_scale, self.out, self.lse, self.ws, stream=stream, stages=stages)
+        return self.out, self.lse
+
+    def results(self):
+        """(out as float64 numpy, lse as float64 numpy) after synchronising."""
+        import torch
+        torch.cuda.synchronize()
+        return self.out.float().cpu().numpy().astype(np.float64), self.lse.cpu().numpy().astype(np.float64)

@@ -1,0 +1,126 @@
+"""C-ABI library: loads, exports what include/mla.h declares, validates arguments (CPU only)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from mla_decode_attention_paged_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "mla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = B.lib()
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"libmla.so does not export {n}"
+    assert B.abi_version() == 1
+
+
+def test_status_strings():
+    lib = B.lib()
+    for s in range(6):
+        assert lib.mla_status_string(s)
+    assert lib.mla_status_string(99) == b"unknown status"
+
+
+def _plan(batch=2, q_len=1, heads=16, page=64, lens=(100, 200), num_pages=None, maxp=None, out_fp32=False,
+          num_cus=256, force=0, **kw):
+    lens = np.asarray(lens, dtype=np.int32)
+    if maxp is None:
+        maxp = max([1] + [int((l + page - 1) // page) for l in lens])
+    if num_pages is None:
+        num_pages = int(sum((l + page - 1) // page for l in lens)) or 1
+    prob = B.make_problem(batch, q_len, heads, page, num_pages, maxp, out_fp32=out_fp32, **kw)
+    if batch == 0:   # the binding checks shapes first; go to the library directly
+        h = C.c_void_p()
+        st = B.lib().mla_plan(C.byref(prob), (C.c_int32 * 1)(), None, C.byref(h))
+        raise B.MlaError(st, "mla_plan", B.last_error())
+    return B.Plan(prob, lens, num_cus=num_cus, force_splits=force)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=8), B.MLA_ERR_UNSUPPORTED),                 # R = 8
+    (dict(heads=16, q_len=9), B.MLA_ERR_UNSUPPORTED),       # R = 144 > 128
+    (dict(page=8), B.MLA_ERR_UNSUPPORTED),
+    (dict(page=24), B.MLA_ERR_UNSUPPORTED),
+    (dict(head_dim_qk=512), B.MLA_ERR_UNSUPPORTED),
+    (dict(head_dim_v=576), B.MLA_ERR_UNSUPPORTED),
+    (dict(batch=0, lens=()), B.MLA_ERR_INVALID_ARGUMENT),
+    (dict(q_len=0), B.MLA_ERR_INVALID_ARGUMENT),
+    (dict(lens=(100, -1)), B.MLA_ERR_INVALID_ARGUMENT),
+    (dict(lens=(100, 200), maxp=2), B.MLA_ERR_INVALID_ARGUMENT),  # 200 > 2*64
+    (dict(num_cus=-1), B.MLA_ERR_INVALID_ARGUMENT),
+    (dict(force=-2), B.MLA_ERR_INVALID_ARGUMENT),
+])
+def test_plan_rejects_bad_problems(kw, status):
+    with pytest.raises(B.MlaError) as ei:
+        _plan(**kw)
+    assert ei.value.status == status
+    assert B.last_error()
+
+
+def test_plan_null_pointers():
+    lib = B.lib()
+    h = C.c_void_p()
+    assert lib.mla_plan(None, None, None, C.byref(h)) == B.MLA_ERR_INVALID_ARGUMENT
+    prob = B.make_problem(1, 1, 16, 64, 1, 1)
+    assert lib.mla_plan(C.byref(prob), None, None, C.byref(h)) == B.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_plan(C.byref(prob), None, None, None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_plan_workspace_bytes(None) == 0
+    lib.mla_plan_destroy(None)
+
+
+def test_reserved_options_must_be_zero():
+    lib = B.lib()
+    prob = B.make_problem(1, 1, 16, 64, 1, 1)
+    sl = (C.c_int32 * 1)(10)
+    opt = B.mla_plan_options_t(256, 0)
+    opt.reserved[3] = 1
+    h = C.c_void_p()
+    assert lib.mla_plan(C.byref(prob), sl, C.byref(opt), C.byref(h)) == B.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_decode_validation_happens_before_any_launch():
+    """Bad arguments come back as status codes; nothing touches a device (none here)."""
+    lib = B.lib()
+    plan = _plan()
+    h = plan.handle
+    ws_bytes = plan.workspace_bytes
+    fake = 1 << 20  # aligned non-null stand-in pointers; validation must reject before use
+    call = lambda **o: lib.mla_decode_stages(
+        h, o.get("q", fake), o.get("kv", fake), o.get("bt", fake), o.get("sl", fake), o.get("scale", 0.1),
+        o.get("out", fake), o.get("lse", fake), o.get("ws", fake), o.get("wsb", ws_bytes), None, o.get("stages", 3))
+    assert call(q=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(kv=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(out=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(ws=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(q=fake + 2) == B.MLA_ERR_INVALID_ARGUMENT          # misaligned
+    assert call(ws=fake + 16) == B.MLA_ERR_INVALID_ARGUMENT        # workspace alignment
+    assert call(wsb=ws_bytes - 1) == B.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert call(scale=float("nan")) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(stages=0) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(stages=4) == B.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_decode(None, fake, fake, fake, fake, 0.1, fake, fake, fake, ws_bytes, None) == \
+        B.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_plan_upload(h, None, ws_bytes, None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_plan_upload(h, fake, ws_bytes - 1, None) == B.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.mla_debug_gather(h, None, fake, fake, None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_read_status(None, None, None) == B.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_layout_scales_with_partials():
+    p1 = _plan(lens=(4096,) * 16, batch=16, maxp=64)
+    info = p1.info()
+    R = 16
+    assert info["workspace_bytes"] >= info["metadata_bytes"] + info["num_partials"] * R * (512 + 1) * 4
+    assert info["workspace_bytes"] % 256 == 0

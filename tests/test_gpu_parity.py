@@ -1,0 +1,244 @@
+"""HIP path (through the C-ABI) against the fp64 oracle.  Needs an MI355X.
+
+Tolerances (pooled over all compared elements of a call):
+  out: RMSE <= 1e-3 and max |err| <= 1e-2;   lse: max |err| <= 1e-3.
+The bf16 output rounding alone contributes about 2e-4 RMSE / 2e-3 max on
+N(0,1) inputs; bf16 P in the PV product adds a little more.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from mla_decode_attention_paged_amd import binding as B
+from mla_decode_attention_paged_amd import inputs as gen
+from mla_decode_attention_paged_amd.device import Runner, to_device
+from oracle import mla_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+RMSE_TOL, MAX_TOL, LSE_TOL = 1e-3, 1e-2, 1e-3
+# fp32 output: the kernel keeps ~16-bit weights (bf16 hi + lo) and fp32 sums
+F32_RMSE_TOL, F32_MAX_TOL, F32_LSE_TOL = 1e-5, 1e-4, 1e-5
+
+
+def bf16_half_ulp(x):
+    """Half a bf16 unit in the last place at |x| (the most round-to-nearest can move x)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(ax)) - 8)
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def compare(out, lse, ref_out, ref_lse, batch_idx=None, what="", tol=(RMSE_TOL, MAX_TOL, LSE_TOL)):
+    if batch_idx is not None:
+        out, lse, ref_out, ref_lse = out[batch_idx], lse[batch_idx], ref_out[batch_idx], ref_lse[batch_idx]
+    err = out - ref_out
+    rmse = float(np.sqrt(np.mean(err ** 2)))
+    mx = float(np.max(np.abs(err)))
+    finite = np.isfinite(ref_lse)
+    lerr = float(np.max(np.abs(lse[finite] - ref_lse[finite]))) if finite.any() else 0.0
+    assert np.array_equal(np.isfinite(lse), finite), f"{what}: lse finiteness differs"
+    _say(f"  {what}: rmse {rmse:.3e} max {mx:.3e} lse {lerr:.3e}")
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    assert rmse <= tol[0] and mx <= tol[1] and lerr <= tol[2], (what, rmse, mx, lerr)
+    return rmse, mx, lerr
+
+
+def check_short_contexts(out, lse, ref_o, ref_l, out_fp32, what):
+    """Contexts of a few tokens give |out| up to ~4, where bf16 output rounding alone moves a
+    value by up to 2^-7 (more than the pooled max-abs bound for long N(0,1) contexts).  fp32
+    output is held to the fp32-path bounds; bf16 output to its rounding plus that bound."""
+    if out_fp32:
+        compare(out, lse, ref_o, ref_l, what=what + " fp32", tol=(F32_RMSE_TOL, F32_MAX_TOL, F32_LSE_TOL))
+    else:
+        err = np.abs(out - ref_o)
+        excess = float(np.max(err - bf16_half_ulp(ref_o)))
+        _say(f"  {what} bf16: max error beyond bf16 rounding {excess:.3e}")
+        assert excess <= F32_MAX_TOL, (what, excess)
+        assert np.max(np.abs(lse - ref_l)) <= F32_LSE_TOL
+
+
+def run(prob, **kw):
+    r = Runner(prob, **kw)
+    r()
+    return r.results()
+
+
+def oracle(prob, batch_idx=None):
+    return orc.decode(prob.q, prob.kv_cache, prob.block_table, prob.cache_seqlens, prob.softmax_scale,
+                      prob.page_size, batch_indices=batch_idx)
+
+
+# ----------------------------------------------------------------------------- gather
+@pytest.mark.parametrize("page", [16, 64, 1024])
+def test_gather_bit_exact(page):
+    import torch
+    prob = gen.make_problem(batch=5, q_len=1, num_heads=16, page_size=page, lengths=[1, 15, page, page + 1, 3000],
+                            seed=3, tail="nan", extra_pages=2)
+    dev = to_device(prob)
+    r = Runner(prob, dev=dev)
+    rows = torch.empty((int(prob.cache_seqlens.sum()), 576), dtype=torch.int16, device="cuda")
+    B.mla_debug_gather(r.plan, dev["kv_cache"], dev["block_table"], rows)
+    got = rows.cpu().numpy().view(np.uint16)
+    off = 0
+    for b in range(prob.batch):
+        L = int(prob.cache_seqlens[b])
+        ref = orc.gather_sequence(prob.kv_cache, prob.block_table[b], L, page)
+        assert np.array_equal(got[off:off + L], ref), f"seq {b}"
+        off += L
+
+
+# ----------------------------------------------------------------------------- the five workloads
+def test_parity_tiny():
+    prob = gen.make_config("tiny")          # fp32 out
+    out, lse = run(prob)
+    ref_o, ref_l = oracle(prob)
+    compare(out, lse, ref_o, ref_l, what="tiny")
+    compare(out, lse, ref_o, ref_l, what="tiny (fp32 bound)", tol=(F32_RMSE_TOL, F32_MAX_TOL, F32_LSE_TOL))
+
+
+def test_parity_paged():
+    prob = gen.make_config("paged")
+    out, lse = run(prob)
+    ref_o, ref_l = oracle(prob)
+    compare(out, lse, ref_o, ref_l, what="paged")
+
+
+@pytest.mark.parametrize("name,sample", [("two_token", [0, 31]), ("long", [0, 9]), ("ragged", None)])
+def test_parity_full_size_sampled(name, sample):
+    _say(f"generating {name}")
+    prob = gen.make_config(name)
+    if sample is None:   # ragged: the longest, the shortest and one in the middle
+        order = np.argsort(prob.cache_seqlens)
+        sample = [int(order[-1]), int(order[0]), int(order[len(order) // 2])]
+    _say(f"running {name} on the GPU")
+    out, lse = run(prob)
+    _say(f"oracle on sequences {sample}")
+    ref_o, ref_l = oracle(prob, sample)
+    compare(out, lse, ref_o, ref_l, batch_idx=sample, what=name)
+    # every other sequence at least produced finite values
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+# ----------------------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("page", [16, 64, 1024])
+@pytest.mark.parametrize("out_fp32", [True, False])
+def test_edge_lengths_nan_tails(page, out_fp32):
+    lengths = [1, 15, 16, 17, 63, 64, 65, 1000]
+    prob = gen.make_problem(batch=len(lengths), q_len=1, num_heads=16, page_size=page, lengths=lengths, seed=5,
+                            tail="nan", extra_pages=3, out_fp32=out_fp32)
+    out, lse = run(prob)
+    ref_o, ref_l = oracle(prob)
+    check_short_contexts(out, lse, ref_o, ref_l, out_fp32, f"edges P={page}")
+
+
+@pytest.mark.parametrize("out_fp32", [False, True])
+def test_single_token_returns_v_row(out_fp32):
+    prob = gen.make_problem(batch=4, q_len=2, num_heads=16, page_size=64, lengths=[1, 1, 1, 1], seed=6,
+                            tail="nan", out_fp32=out_fp32)
+    out, lse = run(prob)
+    for b in range(prob.batch):
+        v = gen.bf16_bits_to_f32(prob.kv_cache[prob.block_table[b, 0], 0, :512]).astype(np.float64)
+        assert np.array_equal(out[b], np.broadcast_to(v, out[b].shape)), f"seq {b}: out != V row"
+    ref_o, ref_l = oracle(prob)
+    assert np.max(np.abs(lse - ref_l)) <= LSE_TOL
+
+
+def test_empty_context():
+    prob = gen.make_problem(batch=3, q_len=1, num_heads=16, page_size=64, lengths=[0, 100, 0], seed=7)
+    out, lse = run(prob)
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+    assert np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2]))
+    ref_o, ref_l = oracle(prob, [1])
+    compare(out, lse, ref_o, ref_l, batch_idx=[1], what="L=0 neighbours")
+
+
+def test_page_permutation_bit_identical():
+    rng = np.random.default_rng(8)
+    prob = gen.make_problem(batch=4, q_len=1, num_heads=16, page_size=64, lengths=[3000, 64, 5000, 17], seed=8,
+                            extra_pages=5)
+    out1, lse1 = run(prob)
+    perm = rng.permutation(prob.num_pages)
+    kv2 = np.empty_like(prob.kv_cache)
+    kv2[perm] = prob.kv_cache
+    bt2 = np.where(prob.block_table >= 0, perm[np.maximum(prob.block_table, 0)], -1).astype(np.int32)
+    prob2 = gen.Problem(q=prob.q, kv_cache=kv2, block_table=bt2, cache_seqlens=prob.cache_seqlens,
+                        softmax_scale=prob.softmax_scale, page_size=64)
+    out2, lse2 = run(prob2)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("force", [1, 2, 3, 1000])
+def test_forced_split_counts_agree(force):
+    prob = gen.make_problem(batch=3, q_len=1, num_heads=16, page_size=64, lengths=[4096, 100, 2500], seed=9)
+    out, lse = run(prob, force_splits=force)
+    ref_o, ref_l = oracle(prob)
+    compare(out, lse, ref_o, ref_l, what=f"force_splits={force}")
+
+
+@pytest.mark.parametrize("out_fp32", [True, False])
+def test_many_pieces_per_work_group(out_fp32):
+    prob = gen.make_problem(batch=700, q_len=1, num_heads=16, page_size=16, lengths=None, ragged_range=(1, 80),
+                            seed=10, out_fp32=out_fp32)
+    r = Runner(prob, num_cus=16)            # 16 work-groups: each walks many sequences
+    assert max(np.diff(r.plan.segments()[1])) > 10
+    r()
+    out, lse = r.results()
+    ref_o, ref_l = oracle(prob)
+    check_short_contexts(out, lse, ref_o, ref_l, out_fp32, "many pieces")
+
+
+@pytest.mark.parametrize("heads,q_len", [(16, 2), (32, 1), (128, 1), (64, 2)])
+def test_more_query_rows(heads, q_len):
+    prob = gen.make_problem(batch=3, q_len=q_len, num_heads=heads, page_size=64, lengths=[700, 2000, 33], seed=11)
+    out, lse = run(prob)
+    ref_o, ref_l = oracle(prob)
+    compare(out, lse, ref_o, ref_l, what=f"H={heads} S_q={q_len}")
+
+
+def test_two_token_query_equals_two_single_token_calls():
+    prob = gen.make_problem(batch=2, q_len=2, num_heads=16, page_size=64, lengths=[1500, 300], seed=12,
+                            out_fp32=True)
+    out, lse = run(prob)
+    for i in range(2):
+        p1 = gen.Problem(q=np.ascontiguousarray(prob.q[:, i:i + 1]), kv_cache=prob.kv_cache,
+                         block_table=prob.block_table, cache_seqlens=prob.cache_seqlens,
+                         softmax_scale=prob.softmax_scale, page_size=64, out_fp32=True)
+        o1, l1 = run(p1)
+        assert np.max(np.abs(o1[:, 0] - out[:, i])) <= 1e-5 and np.max(np.abs(l1[:, 0] - lse[:, i])) <= 1e-5
+
+
+def test_out_of_range_block_table_entry_is_flagged():
+    import torch
+    prob = gen.make_problem(batch=2, q_len=1, num_heads=16, page_size=64, lengths=[640, 640], seed=13)
+    good = Runner(prob)
+    assert B.mla_read_status(good.ws) == 0
+    good()
+    torch.cuda.synchronize()
+    assert B.mla_read_status(good.ws) == 0
+    bt = prob.block_table.copy()
+    bt[1, 3] = prob.num_pages + 7            # outside [0, num_pages): its 64 tokens are dropped
+    bad = gen.Problem(q=prob.q, kv_cache=prob.kv_cache, block_table=bt, cache_seqlens=prob.cache_seqlens,
+                      softmax_scale=prob.softmax_scale, page_size=64)
+    r = Runner(bad)
+    r()
+    out, lse = r.results()
+    assert B.mla_read_status(r.ws) & 1
+    ref_o, ref_l = oracle(prob, [0])
+    compare(out, lse, ref_o, ref_l, batch_idx=[0], what="unaffected sequence")
+    assert np.all(np.isfinite(out[1]))
+
+
+def test_repeated_calls_are_deterministic():
+    prob = gen.make_problem(batch=4, q_len=1, num_heads=16, page_size=64, lengths=[9000, 100, 5000, 64], seed=14)
+    r = Runner(prob)
+    r()
+    o1, l1 = r.results()
+    for _ in range(3):
+        r()
+        o2, l2 = r.results()
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
