@@ -17,7 +17,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,8 +29,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "mla_decode_attention_paged_amd", "csrc", f)
-                  for f in ("mla_kernels.hip", "mla_internal.h", "plan.cpp", "mla_api.cpp")]
 
 WORKLOAD_TEXT = {
     "tiny": "MLA decode: batch 1, q_len 1, 16 heads, one contiguous 1024-token page, fp32 out",
@@ -53,14 +50,6 @@ def algorithmic_bytes(prob) -> int:
                + prob.batch * R * 4 + pages * 4)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(config: str):
     """HBM bytes per split-decode launch from the committed counter summary, or None when
     the summary is missing, for another workload, or older than the kernel sources."""
@@ -69,6 +58,7 @@ def measured_traffic(config: str):
             c = json.load(fh)
     except (OSError, ValueError):
         return None
+    from mla_decode_attention_paged_amd.profiling import kernel_source_hash
     entry = c.get(config)
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
         return None
@@ -171,18 +161,13 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     split_us = e0.elapsed_time(e1) * 1e3 / args.steps
-    e0.record(stream)
-    for _ in range(args.steps):
-        r(stages=B.MLA_STAGE_MERGE)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    merge_us = e0.elapsed_time(e1) * 1e3 / args.steps
 
-    # flushed per-call time: a 512 MB fill between calls evicts the 256 MB last-level cache
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    # flushed per-call time: reading 512 MB between calls evicts the 256 MB last-level cache
+    # (a read, so no dirty lines are left to be written back during the timed call)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     fl = []
     for _ in range(min(args.steps, 20)):
-        flush.fill_(1)
+        flush.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         r()
@@ -222,7 +207,8 @@ def main():
                       "call_event_p50": round(float(np.percentile(call_us, 50)), 2),
                       "call_event_p90": round(float(np.percentile(call_us, 90)), 2),
                       "call_flushed_p50": round(float(np.median(fl)), 2),
-                      "split_kernel_mean": round(split_us, 2), "merge_kernel_mean": round(merge_us, 2),
+                      "split_kernel_mean": round(split_us, 2),
+                      "merge_and_gap_p50": round(float(np.percentile(call_us, 50)) - split_us, 2),
                       "plan_host_us": round(plan_us, 1)},
         "plan": {k: info[k] for k in ("num_workers", "grid_size", "num_segments", "num_partials", "num_combine")},
         "status_word": status,

@@ -379,47 +379,68 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   }
 }
 
-// Merge of split sequences: one work-group per (sequence, 16 query rows).
+// Merge of split sequences.  One work-group per (sequence, 16 query rows, 64
+// output columns): thread (r, q) merges row r, columns 4q..4q+3 of the slice over
+// all of the sequence's partial results, so every partial byte is read once and
+// all loads of a thread are independent.
+constexpr int kMergeCols = 64;
+constexpr int kMergeBatch = 8;
 template <bool OUT_F32>
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
-  const int groups = a.rows / 16;
-  const int item = blockIdx.x / groups, rg = blockIdx.x % groups;
-  const int b = a.merges[4 * item + 0];
-  const int s0 = a.merges[4 * item + 1];
-  const int ns = a.merges[4 * item + 2];
   const int R = a.rows;
-  const int r = rg * 16 + (threadIdx.x >> 4), dseg = threadIdx.x & 15;
+  const int col_groups = kDv / kMergeCols;
+  const int per_item = (R / 16) * col_groups;
+  const int item = blockIdx.x / per_item;
+  const int rem = blockIdx.x % per_item;
+  const int rg = rem / col_groups, cg = rem % col_groups;
+  const CST_AS int32_t* merges = as_const(a.merges);
+  const int b = merges[4 * item + 0];
+  const int s0 = merges[4 * item + 1];
+  const int ns = merges[4 * item + 2];
+  const int r = rg * 16 + (threadIdx.x >> 4);
+  const int d = cg * kMergeCols + 4 * (threadIdx.x & 15);
+  const float* lse_col = a.part_lse + (int64_t)s0 * R + r;                 // stride R per slot
+  const float* o_col = a.part_o + ((int64_t)s0 * R + r) * kDv + d;         // stride R*512 per slot
+  // loads are issued kMergeBatch at a time so their latencies overlap
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[(int64_t)(s0 + s) * R + r]);
-  f32x4_t acc[kDv / 64];
+  for (int s = 0; s < ns; s += kMergeBatch) {
+    float l[kMergeBatch];
 #pragma unroll
-  for (int j = 0; j < kDv / 64; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kMergeBatch; ++u) l[u] = (s + u < ns) ? lse_col[(int64_t)(s + u) * R] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) M = fmaxf(M, l[u]);
+  }
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M > -INFINITY) {
-    for (int s = 0; s < ns; ++s) {
-      const float ls = a.part_lse[(int64_t)(s0 + s) * R + r];
-      const float w = (ls > -INFINITY) ? __expf(ls - M) : 0.f;
-      L += w;
-      const float* src = a.part_o + ((int64_t)(s0 + s) * R + r) * kDv + 4 * dseg;
+    for (int s = 0; s < ns; s += kMergeBatch) {
+      float l[kMergeBatch];
+      f32x4_t v[kMergeBatch];
 #pragma unroll
-      for (int j = 0; j < kDv / 64; ++j) acc[j] += w * *(const f32x4_t*)(src + 64 * j);
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const bool in = s + u < ns;
+        l[u] = in ? lse_col[(int64_t)(s + u) * R] : -INFINITY;
+        v[u] = in ? *(const f32x4_t*)(o_col + (int64_t)(s + u) * R * kDv) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float w = (l[u] > -INFINITY) ? __expf(l[u] - M) : 0.f;
+        L += w;
+        acc += w * v[u];
+      }
     }
   }
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
-  const int64_t off = ((int64_t)b * R + r) * kDv + 4 * dseg;
-#pragma unroll
-  for (int j = 0; j < kDv / 64; ++j) {
-    f32x4_t v = acc[j] * inv;
-    if (OUT_F32) {
-      *(f32x4_t*)((float*)a.out + off + 64 * j) = v;
-    } else {
-      u32x2_t pkd;
-      pkd[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-      pkd[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-      *(u32x2_t*)((uint16_t*)a.out + off + 64 * j) = pkd;
-    }
+  const f32x4_t v = acc * (L > 0.f ? 1.0f / L : 0.f);
+  const int64_t off = ((int64_t)b * R + r) * kDv + d;
+  if (OUT_F32) {
+    *(f32x4_t*)((float*)a.out + off) = v;
+  } else {
+    u32x2_t pkd;
+    pkd[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+    pkd[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+    *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
   }
-  if (dseg == 0 && a.lse) a.lse[(int64_t)b * R + r] = L > 0.f ? M + __logf(L) : -INFINITY;
+  if (cg == 0 && (threadIdx.x & 15) == 0 && a.lse) a.lse[(int64_t)b * R + r] = L > 0.f ? M + __logf(L) : -INFINITY;
 }
 
 // Debug gather: one thread per 16-B chunk of a sequence's logical rows.
@@ -449,7 +470,7 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
 
 int launch_merge(const MergeArgs& a, bool out_fp32, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const int grid = a.num_merges * (a.rows / 16);
+  const int grid = a.num_merges * (a.rows / 16) * (kDv / kMergeCols);
   if (out_fp32)
     hipLaunchKernelGGL((merge_kernel<true>), dim3(grid), dim3(256), 0, s, a);
   else
