@@ -48,6 +48,13 @@ constexpr float kRescaleSlack = 8.0f;              // lazy rescale threshold (lo
 constexpr float kNegBig = -1.0e30f;                // running-max start value (finite)
 constexpr int kMergeStride = kDv + 4;              // floats per row in the merge buffer
 
+#ifndef MLA_PROGRESSIVE_REFILL
+#define MLA_PROGRESSIVE_REFILL 1   // refill a stage part by part as its bytes are consumed
+#endif
+#ifndef MLA_CONTIG_BLOCKS
+#define MLA_CONTIG_BLOCKS 0        // 0: wave w takes blocks w, w+4, ...; 1: a contiguous quarter
+#endif
+
 // Physical row of logical token t of sequence b (the page walk).  Returns -1
 // when the block-table entry is outside [0, num_pages).
 template <class TablePtr>
@@ -182,7 +189,14 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     const int te = min(pieces[4 * pi + 2], seqlens[b]);
     const int slot = pieces[4 * pi + 3];
     const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
+#if MLA_CONTIG_BLOCKS
+    const int blk_first = (wave * nblk) / kWaves;
+    const int my_n = ((wave + 1) * nblk) / kWaves - blk_first;
+    auto blk_of = [&](int k) { return blk_first + k; };
+#else
     const int my_n = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+    auto blk_of = [&](int k) { return wave + kWaves * k; };
+#endif
 
     // query rows as MFMA B operands (Q^T): lane (n, g) holds row n, columns 32*kk + 8*g .. +8
     bf16x8_t qf[kKSteps];
@@ -198,32 +212,28 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
 #pragma unroll
     for (int mb = 0; mb < kVBlocks; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // DMA loads of this wave's k-th block into a stage; false for an out-of-range table entry
-    auto issue = [&](int k, LDS_AS uint8_t* stage) -> bool {
-      const int tok0 = tb + kBlock * (wave + kWaves * k);
+    // Source row of this lane for the DMA of the wave's k-th block; `ok` is false for an
+    // out-of-range table entry (then page 0 is read, in bounds, and the block is skipped).
+    auto source = [&](int k, bool& ok) -> const uint16_t* {
+      const int tok0 = tb + kBlock * blk_of(k);
       int64_t base = kv_row_of(block_table, a.bt_stride, a.page_size, a.num_pages, b, tok0);
-      const bool ok = base >= 0;
-      if (!ok) base = 0;  // bad entry: load page 0 (in bounds); the block is skipped
+      ok = base >= 0;
+      if (!ok) base = 0;
       const int t = min(ld_token, te - 1 - tok0);   // rows past the end re-read the last valid row
-      const uint16_t* src = a.kv + (base + t) * kDqk + 8 * g;
-#pragma unroll
-      for (int j = 0; j < kLoadsPerBlock; ++j)
-        __builtin_amdgcn_global_load_lds((GLB_AS void*)(src + 32 * j), (LDS_AS void*)(stage + 1024 * j), 16, 0, 0);
-      return ok;
+      return a.kv + (base + t) * kDqk + 8 * g;
     };
-    bool ok0 = true, ok1 = true;   // table entry of the block now in each stage was in range
-    auto refill = [&](int k, LDS_AS uint8_t* st) {
-      if (k + 2 < my_n) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of the stage done before refill
-        const bool ok = issue(k + 2, st);
-        if (k & 1) ok1 = ok; else ok0 = ok;
-      }
+    // DMA loads j0..j1-1 (1 KB each: 16-B column chunks 4j..4j+3 of the 16 rows) into a stage
+    auto issue = [&](const uint16_t* src, LDS_AS uint8_t* stage, int j0, int j1) {
+#pragma unroll
+      for (int j = j0; j < j1; ++j)
+        __builtin_amdgcn_global_load_lds((GLB_AS void*)(src + 32 * j), (LDS_AS void*)(stage + 1024 * j), 16, 0, 0);
     };
     // O^T += V^T P^T for one block, p = exp2(s - m_ref).  p is split into two bf16
     // terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)), and both go through the
     // MFMA, so the weights carry ~16 mantissa bits instead of bf16's 8; the running
-    // sum l takes p in fp32.
-    auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[4]) {
+    // sum l takes p in fp32.  As each half of V^T has been read, the matching part of
+    // the stage is refilled with the block after next (`nsrc`, if any).
+    auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[4], const uint16_t* nsrc) {
       uint32_t hb[4], lb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -235,14 +245,22 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       const i16x4_t ph = i16x4_t{(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
       const i16x4_t pl = i16x4_t{(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
       u32x2_t vf[16];
-      lds_read_vt_lo(vf, st + v_lane);
+      lds_read_vt_lo(vf, st + v_lane);           // columns 0..255 = stage bytes [0, 8 KB)
+#if MLA_PROGRESSIVE_REFILL
+      if (nsrc) issue(nsrc, st, 0, 8);
+#endif
 #pragma unroll
       for (int mb = 0; mb < 16; ++mb) {
         const i16x4_t v = __builtin_bit_cast(i16x4_t, vf[mb]);
         o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, ph, o[mb], 0, 0, 0);
         o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pl, o[mb], 0, 0, 0);
       }
-      lds_read_vt_hi(vf, st + v_lane);
+      lds_read_vt_hi(vf, st + v_lane);           // columns 256..511 = stage bytes [8 KB, 16 KB)
+#if MLA_PROGRESSIVE_REFILL
+      if (nsrc) issue(nsrc, st, 8, 16);
+#else
+      if (nsrc) issue(nsrc, st, 0, kLoadsPerBlock);
+#endif
 #pragma unroll
       for (int mb = 0; mb < 16; ++mb) {
         const i16x4_t v = __builtin_bit_cast(i16x4_t, vf[mb]);
@@ -251,27 +269,33 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       }
     };
 
-    if (my_n > 0) ok0 = issue(0, stage0);
-    if (my_n > 1) ok1 = issue(1, stage1);
+    bool ok0 = true, ok1 = true;   // table entry of the block now in each stage was in range
+    if (my_n > 0) issue(source(0, ok0), stage0, 0, kLoadsPerBlock);
+    if (my_n > 1) issue(source(1, ok1), stage1, 0, kLoadsPerBlock);
 
     int k = 0;
     while (k < my_n) {
       float s[4], mx = 0.f;
       bool rescale = false;
+      const uint16_t* nsrc = nullptr;
       // hot loop: o is only touched by MFMA here
       for (; k < my_n; ++k) {
         LDS_AS uint8_t* st = (k & 1) ? stage1 : stage0;
+        bool nok = true;
+        nsrc = (k + 2 < my_n) ? source(k + 2, nok) : nullptr;
         if (k + 1 < my_n) {
           asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        if (!((k & 1) ? ok1 : ok0)) {
+        const bool ok = (k & 1) ? ok1 : ok0;
+        if (k & 1) ok1 = nok; else ok0 = nok;   // the stage's next occupant
+        if (!ok) {
           if (lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          refill(k, st);
+          if (nsrc) issue(nsrc, st, 0, kLoadsPerBlock);
           continue;
         }
-        const int nvalid = te - (tb + kBlock * (wave + kWaves * k));   // >= 1
+        const int nvalid = te - (tb + kBlock * blk_of(k));   // >= 1
         // S^T = K Q^T: 16 tokens x 16 rows, lane holds tokens 4g..4g+3 of row n
         f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, sacc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
         {
@@ -281,6 +305,9 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           for (int kk = 0; kk < 9; ++kk)
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]), qf[kk], sacc, 0, 0, 0);
           lds_read_k_hi(kf, st + k_lane);
+#if MLA_PROGRESSIVE_REFILL
+          if (nsrc) issue(nsrc, st, 16, kLoadsPerBlock);   // rope columns: stage bytes [16 KB, 18 KB)
+#endif
 #pragma unroll
           for (int kk = 0; kk < 9; ++kk)
             sacc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]), qf[9 + kk], sacc2, 0,
@@ -294,8 +321,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           rescale = true;
           break;
         }
-        accumulate(st, s);
-        refill(k, st);
+        accumulate(st, s, nsrc);
       }
       if (!rescale) break;
       // rare path: the running max grew past the slack; move the reference and rescale
@@ -307,8 +333,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         lsum *= f;
 #pragma unroll
         for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
-        accumulate(st, s);
-        refill(k, st);
+        accumulate(st, s, nsrc);
         ++k;
       }
     }
