@@ -92,7 +92,7 @@ typedef struct {
   int32_t num_segments;       /* (sequence, token range) pieces over all workers */
   int32_t num_partials;       /* partial-result slots (pieces of split sequences) */
   int32_t num_combine;        /* sequences that need the merge kernel */
-  int32_t rows_per_group;     /* query rows one work-group handles (16 or 32) */
+  int32_t rows_per_group;     /* query rows one work-group handles (16, 32 or 64) */
   int32_t row_groups;         /* R / rows_per_group */
   int32_t granule;            /* token granularity of split boundaries */
   int64_t max_worker_cost;    /* planner cost units (16-token blocks + per-piece overhead) */

@@ -97,52 +97,63 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_
 // ends.  Issuing a batch back to back (instead of one read, one wait) keeps many
 // LDS requests in flight; doing it in asm also keeps the compiler from adding a
 // wait for the in-flight global->LDS prefetch of the other stage before every read.
-#define MLA_RD128(i, off) "ds_read_b128 %" #i ", %9 offset:" #off "\n\t"
-#define MLA_RDTR(i, off) "ds_read_b64_tr_b16 %" #i ", %16 offset:" #off "\n\t"
+#define MLA_O4(b, s) "i"(b), "i"(b + s), "i"(b + 2 * s), "i"(b + 3 * s)
 
-// Nine 16-B reads at p + 1024*i (i = 0..8) and at p + 9216 + 1024*i.
-__device__ __forceinline__ void lds_read_k_lo(u32x4_t (&r)[9], LDS_AS const uint8_t* p) {
-  asm volatile(MLA_RD128(0, 0) MLA_RD128(1, 1024) MLA_RD128(2, 2048) MLA_RD128(3, 3072) MLA_RD128(4, 4096)
-               MLA_RD128(5, 5120) MLA_RD128(6, 6144) MLA_RD128(7, 7168) MLA_RD128(8, 8192) "s_waitcnt lgkmcnt(0)"
-               : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
-                 "=v"(r[8])
-               : "v"(p)
-               : "memory");
+// 16-B reads at p + OFF + 1024*i
+template <int OFF>
+__device__ __forceinline__ void lds_read_b128x6(u32x4_t (&r)[6], LDS_AS const uint8_t* p) {
+  asm volatile(
+      "ds_read_b128 %0, %6 offset:%7\n\tds_read_b128 %1, %6 offset:%8\n\tds_read_b128 %2, %6 offset:%9\n\t"
+      "ds_read_b128 %3, %6 offset:%10\n\tds_read_b128 %4, %6 offset:%11\n\tds_read_b128 %5, %6 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5])
+      : "v"(p), MLA_O4(OFF, 1024), "i"(OFF + 4096), "i"(OFF + 5120)
+      : "memory");
 }
-__device__ __forceinline__ void lds_read_k_hi(u32x4_t (&r)[9], LDS_AS const uint8_t* p) {
-  asm volatile(MLA_RD128(0, 9216) MLA_RD128(1, 10240) MLA_RD128(2, 11264) MLA_RD128(3, 12288) MLA_RD128(4, 13312)
-               MLA_RD128(5, 14336) MLA_RD128(6, 15360) MLA_RD128(7, 16384) MLA_RD128(8, 17408)
-               "s_waitcnt lgkmcnt(0)"
-               : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
-                 "=v"(r[8])
-               : "v"(p)
-               : "memory");
+template <int OFF>
+__device__ __forceinline__ void lds_read_b128x9(u32x4_t (&r)[9], LDS_AS const uint8_t* p) {
+  asm volatile(
+      "ds_read_b128 %0, %9 offset:%10\n\tds_read_b128 %1, %9 offset:%11\n\tds_read_b128 %2, %9 offset:%12\n\t"
+      "ds_read_b128 %3, %9 offset:%13\n\tds_read_b128 %4, %9 offset:%14\n\tds_read_b128 %5, %9 offset:%15\n\t"
+      "ds_read_b128 %6, %9 offset:%16\n\tds_read_b128 %7, %9 offset:%17\n\tds_read_b128 %8, %9 offset:%18\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]), "=v"(r[8])
+      : "v"(p), MLA_O4(OFF, 1024), MLA_O4(OFF + 4096, 1024), "i"(OFF + 8192)
+      : "memory");
 }
-// Sixteen transpose reads at p + 512*i (i = 0..15) and at p + 8192 + 512*i.
-__device__ __forceinline__ void lds_read_vt_lo(u32x2_t (&r)[16], LDS_AS const uint8_t* p) {
-  asm volatile(MLA_RDTR(0, 0) MLA_RDTR(1, 512) MLA_RDTR(2, 1024) MLA_RDTR(3, 1536) MLA_RDTR(4, 2048)
-               MLA_RDTR(5, 2560) MLA_RDTR(6, 3072) MLA_RDTR(7, 3584) MLA_RDTR(8, 4096) MLA_RDTR(9, 4608)
-               MLA_RDTR(10, 5120) MLA_RDTR(11, 5632) MLA_RDTR(12, 6144) MLA_RDTR(13, 6656) MLA_RDTR(14, 7168)
-               MLA_RDTR(15, 7680) "s_waitcnt lgkmcnt(0)"
-               : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
-                 "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11]), "=v"(r[12]), "=v"(r[13]), "=v"(r[14]),
-                 "=v"(r[15])
-               : "v"(p)
-               : "memory");
+// transpose reads (4 tokens x 16 columns per 16 lanes) at p + OFF + 512*i
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr8(u32x2_t (&r)[8], LDS_AS const uint8_t* p) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%9\n\tds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:%11\n\tds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\tds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:%15\n\tds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
+      : "v"(p), MLA_O4(OFF, 512), MLA_O4(OFF + 2048, 512)
+      : "memory");
 }
-__device__ __forceinline__ void lds_read_vt_hi(u32x2_t (&r)[16], LDS_AS const uint8_t* p) {
-  asm volatile(MLA_RDTR(0, 8192) MLA_RDTR(1, 8704) MLA_RDTR(2, 9216) MLA_RDTR(3, 9728) MLA_RDTR(4, 10240)
-               MLA_RDTR(5, 10752) MLA_RDTR(6, 11264) MLA_RDTR(7, 11776) MLA_RDTR(8, 12288) MLA_RDTR(9, 12800)
-               MLA_RDTR(10, 13312) MLA_RDTR(11, 13824) MLA_RDTR(12, 14336) MLA_RDTR(13, 14848)
-               MLA_RDTR(14, 15360) MLA_RDTR(15, 15872) "s_waitcnt lgkmcnt(0)"
-               : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
-                 "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11]), "=v"(r[12]), "=v"(r[13]), "=v"(r[14]),
-                 "=v"(r[15])
-               : "v"(p)
-               : "memory");
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr16(u32x2_t (&r)[16], LDS_AS const uint8_t* p) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%17\n\tds_read_b64_tr_b16 %1, %16 offset:%18\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:%19\n\tds_read_b64_tr_b16 %3, %16 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:%21\n\tds_read_b64_tr_b16 %5, %16 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %6, %16 offset:%23\n\tds_read_b64_tr_b16 %7, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%25\n\tds_read_b64_tr_b16 %9, %16 offset:%26\n\t"
+      "ds_read_b64_tr_b16 %10, %16 offset:%27\n\tds_read_b64_tr_b16 %11, %16 offset:%28\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:%29\n\tds_read_b64_tr_b16 %13, %16 offset:%30\n\t"
+      "ds_read_b64_tr_b16 %14, %16 offset:%31\n\tds_read_b64_tr_b16 %15, %16 offset:%32\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
+        "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11]), "=v"(r[12]), "=v"(r[13]), "=v"(r[14]), "=v"(r[15])
+      : "v"(p), MLA_O4(OFF, 512), MLA_O4(OFF + 2048, 512), MLA_O4(OFF + 4096, 512), MLA_O4(OFF + 6144, 512)
+      : "memory");
 }
 
-template <bool OUT_F32>
+// NB = 16-row groups of query rows each wave carries (R = 16 * NB * row groups).
+template <int NB, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
@@ -163,7 +174,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     worker = (y / a.row_groups) * 8 + x;
   }
   if (worker >= a.num_workers) return;
-  const int row0 = rgroup * 16;
+  const int row0 = rgroup * 16 * NB;
   const int R = a.rows;
 
   // LDS block layout (16-B units): position = chunk*16 + (token ^ ((chunk & 1) << 2)),
@@ -198,19 +209,25 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     auto blk_of = [&](int k) { return wave + kWaves * k; };
 #endif
 
-    // query rows as MFMA B operands (Q^T): lane (n, g) holds row n, columns 32*kk + 8*g .. +8
-    bf16x8_t qf[kKSteps];
-    {
-      const uint16_t* qrow = a.q + ((int64_t)b * R + row0 + n) * kDqk + 8 * g;
+    // query rows as MFMA B operands (Q^T): lane (n, g) holds row 16*nb + n, columns 32*kk + 8*g .. +8
+    bf16x8_t qf[NB][kKSteps];
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint16_t* qrow = a.q + ((int64_t)b * R + row0 + 16 * nb + n) * kDqk + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) qf[nb][kk] = *(const bf16x8_t*)(qrow + 32 * kk);
     }
 
-    float m_ref = kNegBig;   // reference max (log2 units) the p values are taken against
-    float lsum = 0.f;        // this lane's share of sum_t p_t (tokens 4g..4g+3 of each block)
-    f32x4_t o[kVBlocks];     // O^T: lane (n, g) holds dims 16*mb + 4*g + i of row n
+    float m_ref[NB];         // reference max (log2 units) the p values are taken against
+    float lsum[NB];          // this lane's share of sum_t p_t (tokens 4g..4g+3 of each block)
+    f32x4_t o[NB][kVBlocks]; // O^T: lane (n, g) holds dims 16*mb + 4*g + i of row 16*nb + n
 #pragma unroll
-    for (int mb = 0; mb < kVBlocks; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb) {
+      m_ref[nb] = kNegBig;
+      lsum[nb] = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < kVBlocks; ++mb) o[nb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     // Source row of this lane for the DMA of the wave's k-th block; `ok` is false for an
     // out-of-range table entry (then page 0 is read, in bounds, and the block is skipped).
@@ -228,45 +245,102 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       for (int j = j0; j < j1; ++j)
         __builtin_amdgcn_global_load_lds((GLB_AS void*)(src + 32 * j), (LDS_AS void*)(stage + 1024 * j), 16, 0, 0);
     };
+    // O^T += V^T P^T for the 32-column slab starting at column 16*MB0 (VB transpose reads)
+    auto pv_part = [&](const u32x2_t* vf, int mb0, int cnt, const i16x4_t (&ph)[NB], const i16x4_t (&pl)[NB]) {
+#pragma unroll
+      for (int i = 0; i < cnt; ++i) {
+        const i16x4_t v = __builtin_bit_cast(i16x4_t, vf[i]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          o[nb][mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, ph[nb], o[nb][mb0 + i], 0, 0, 0);
+          o[nb][mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pl[nb], o[nb][mb0 + i], 0, 0, 0);
+        }
+      }
+    };
     // O^T += V^T P^T for one block, p = exp2(s - m_ref).  p is split into two bf16
     // terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)), and both go through the
     // MFMA, so the weights carry ~16 mantissa bits instead of bf16's 8; the running
-    // sum l takes p in fp32.  As each half of V^T has been read, the matching part of
+    // sum l takes p in fp32.  As each part of V^T has been read, the matching part of
     // the stage is refilled with the block after next (`nsrc`, if any).
-    auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[4], const uint16_t* nsrc) {
-      uint32_t hb[4], lb[4];
+    auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[NB][4], const uint16_t* nsrc) {
+      i16x4_t ph[NB], pl[NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[i] - m_ref);
-        hb[i] = bf16_rne(p);
-        lb[i] = bf16_rne(p - bf16_bits_to_float(hb[i]));
-        lsum += p;
-      }
-      const i16x4_t ph = i16x4_t{(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
-      const i16x4_t pl = i16x4_t{(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
-      u32x2_t vf[16];
-      lds_read_vt_lo(vf, st + v_lane);           // columns 0..255 = stage bytes [0, 8 KB)
-#if MLA_PROGRESSIVE_REFILL
-      if (nsrc) issue(nsrc, st, 0, 8);
-#endif
+      for (int nb = 0; nb < NB; ++nb) {
+        uint32_t hb[4], lb[4];
 #pragma unroll
-      for (int mb = 0; mb < 16; ++mb) {
-        const i16x4_t v = __builtin_bit_cast(i16x4_t, vf[mb]);
-        o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, ph, o[mb], 0, 0, 0);
-        o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pl, o[mb], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(s[nb][i] - m_ref[nb]);
+          hb[i] = bf16_rne(p);
+          lb[i] = bf16_rne(p - bf16_bits_to_float(hb[i]));
+          lsum[nb] += p;
+        }
+        ph[nb] = i16x4_t{(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
+        pl[nb] = i16x4_t{(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
       }
-      lds_read_vt_hi(vf, st + v_lane);           // columns 256..511 = stage bytes [8 KB, 16 KB)
-#if MLA_PROGRESSIVE_REFILL
-      if (nsrc) issue(nsrc, st, 8, 16);
-#else
-      if (nsrc) issue(nsrc, st, 0, kLoadsPerBlock);
-#endif
+      LDS_AS const uint8_t* vp = st + v_lane;
+      if constexpr (NB == 1) {
+        u32x2_t vf[16];
+        lds_read_tr16<0>(vf, vp);                // columns 0..255 = stage bytes [0, 8 KB)
+        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 0, 8);
+        pv_part(vf, 0, 16, ph, pl);
+        lds_read_tr16<8192>(vf, vp);             // columns 256..511 = stage bytes [8 KB, 16 KB)
+        if (nsrc) issue(nsrc, st, MLA_PROGRESSIVE_REFILL ? 8 : 0, MLA_PROGRESSIVE_REFILL ? 16 : kLoadsPerBlock);
+        pv_part(vf, 16, 16, ph, pl);
+      } else {
+        u32x2_t vf[8];
+        lds_read_tr8<0>(vf, vp);                 // columns 128*i .. +127 = stage bytes [4i KB, 4i+4 KB)
+        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 0, 4);
+        pv_part(vf, 0, 8, ph, pl);
+        lds_read_tr8<4096>(vf, vp);
+        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 4, 8);
+        pv_part(vf, 8, 8, ph, pl);
+        lds_read_tr8<8192>(vf, vp);
+        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 8, 12);
+        pv_part(vf, 16, 8, ph, pl);
+        lds_read_tr8<12288>(vf, vp);
+        if (nsrc) issue(nsrc, st, MLA_PROGRESSIVE_REFILL ? 12 : 0, MLA_PROGRESSIVE_REFILL ? 16 : kLoadsPerBlock);
+        pv_part(vf, 24, 8, ph, pl);
+      }
+    };
+    // S^T = K Q^T for one block: 16 tokens x 16*NB rows; lane holds tokens 4g..4g+3 of each row
+    auto scores = [&](LDS_AS uint8_t* st, f32x4_t (&sacc)[NB], const uint16_t* nsrc) {
+      LDS_AS const uint8_t* kp = st + k_lane;
+      f32x4_t acc2[NB];
 #pragma unroll
-      for (int mb = 0; mb < 16; ++mb) {
-        const i16x4_t v = __builtin_bit_cast(i16x4_t, vf[mb]);
-        o[16 + mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, ph, o[16 + mb], 0, 0, 0);
-        o[16 + mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pl, o[16 + mb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) {
+        sacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc2[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
+      auto mma = [&](const u32x4_t* kf, int kk0, int cnt) {
+#pragma unroll
+        for (int i = 0; i < cnt; ++i) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            f32x4_t& acc = ((kk0 + i) & 1) ? acc2[nb] : sacc[nb];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[i]), qf[nb][kk0 + i], acc,
+                                                          0, 0, 0);
+          }
+        }
+      };
+      if constexpr (NB == 1) {
+        u32x4_t kf[9];
+        lds_read_b128x9<0>(kf, kp);
+        mma(kf, 0, 9);
+        lds_read_b128x9<9216>(kf, kp);
+        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 16, kLoadsPerBlock);   // rope: bytes [16 KB, 18 KB)
+        mma(kf, 9, 9);
+      } else {
+        u32x4_t kf[6];
+        lds_read_b128x6<0>(kf, kp);
+        mma(kf, 0, 6);
+        lds_read_b128x6<6144>(kf, kp);
+        mma(kf, 6, 6);
+        lds_read_b128x6<12288>(kf, kp);
+        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 16, kLoadsPerBlock);
+        mma(kf, 12, 6);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sacc[nb] += acc2[nb];
     };
 
     bool ok0 = true, ok1 = true;   // table entry of the block now in each stage was in range
@@ -275,7 +349,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
 
     int k = 0;
     while (k < my_n) {
-      float s[4], mx = 0.f;
+      float s[NB][4], mx[NB];
       bool rescale = false;
       const uint16_t* nsrc = nullptr;
       // hot loop: o is only touched by MFMA here
@@ -296,65 +370,58 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           continue;
         }
         const int nvalid = te - (tb + kBlock * blk_of(k));   // >= 1
-        // S^T = K Q^T: 16 tokens x 16 rows, lane holds tokens 4g..4g+3 of row n
-        f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, sacc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        {
-          u32x4_t kf[9];
-          lds_read_k_lo(kf, st + k_lane);
+        f32x4_t sacc[NB];
+        scores(st, sacc, nsrc);
+        bool grow = false;
 #pragma unroll
-          for (int kk = 0; kk < 9; ++kk)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]), qf[kk], sacc, 0, 0, 0);
-          lds_read_k_hi(kf, st + k_lane);
-#if MLA_PROGRESSIVE_REFILL
-          if (nsrc) issue(nsrc, st, 16, kLoadsPerBlock);   // rope columns: stage bytes [16 KB, 18 KB)
-#endif
+        for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-          for (int kk = 0; kk < 9; ++kk)
-            sacc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]), qf[9 + kk], sacc2, 0,
-                                                            0, 0);
+          for (int i = 0; i < 4; ++i) s[nb][i] = (4 * g + i < nvalid) ? sacc[nb][i] * a.scale_log2 : -INFINITY;
+          mx[nb] = wave_max_over_groups(fmaxf(fmaxf(s[nb][0], s[nb][1]), fmaxf(s[nb][2], s[nb][3])));
+          grow |= mx[nb] > m_ref[nb] + kRescaleSlack;
         }
-        sacc += sacc2;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
-        mx = wave_max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-        if (__any(mx > m_ref + kRescaleSlack)) {
+        if (__any(grow)) {
           rescale = true;
           break;
         }
         accumulate(st, s, nsrc);
       }
       if (!rescale) break;
-      // rare path: the running max grew past the slack; move the reference and rescale
+      // rare path: a running max grew past the slack; move the reference and rescale
       {
         LDS_AS uint8_t* st = (k & 1) ? stage1 : stage0;
-        const bool need = mx > m_ref + kRescaleSlack;
-        const float f = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
-        m_ref = need ? mx : m_ref;
-        lsum *= f;
 #pragma unroll
-        for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
+        for (int nb = 0; nb < NB; ++nb) {
+          const bool need = mx[nb] > m_ref[nb] + kRescaleSlack;
+          const float f = need ? __builtin_amdgcn_exp2f(m_ref[nb] - mx[nb]) : 1.0f;
+          m_ref[nb] = need ? mx[nb] : m_ref[nb];
+          lsum[nb] *= f;
+#pragma unroll
+          for (int mb = 0; mb < kVBlocks; ++mb) o[nb][mb] *= f;
+        }
         accumulate(st, s, nsrc);
         ++k;
       }
     }
 
-    // ---- merge the four waves' states and write
-    const float lrow = wave_sum_over_groups(lsum);
-    __syncthreads();
-    LDS_AS float* buf = (LDS_AS float*)smem;                     // [4 waves][16 rows][516]
-    LDS_AS float* sm_m = buf + kWaves * 16 * kMergeStride;       // [4][16]
-    LDS_AS float* sm_l = sm_m + kWaves * 16;                     // [4][16]
-    if (g == 0) {
-      sm_m[wave * 16 + n] = m_ref;
-      sm_l[wave * 16 + n] = lrow;
-    }
-    {
-      LDS_AS float* my = buf + (wave * 16 + n) * kMergeStride + 4 * g;
+    // ---- merge the four waves' states and write, 16 rows at a time
 #pragma unroll
-      for (int mb = 0; mb < kVBlocks; ++mb) *(LDS_AS f32x4_t*)(my + 16 * mb) = o[mb];
-    }
-    __syncthreads();
-    {
+    for (int nb = 0; nb < NB; ++nb) {
+      const float lrow = wave_sum_over_groups(lsum[nb]);
+      __syncthreads();   // stages (or the previous round's buffer) no longer read
+      LDS_AS float* buf = (LDS_AS float*)smem;                     // [4 waves][16 rows][516]
+      LDS_AS float* sm_m = buf + kWaves * 16 * kMergeStride;       // [4][16]
+      LDS_AS float* sm_l = sm_m + kWaves * 16;                     // [4][16]
+      if (g == 0) {
+        sm_m[wave * 16 + n] = m_ref[nb];
+        sm_l[wave * 16 + n] = lrow;
+      }
+      {
+        LDS_AS float* my = buf + (wave * 16 + n) * kMergeStride + 4 * g;
+#pragma unroll
+        for (int mb = 0; mb < kVBlocks; ++mb) *(LDS_AS f32x4_t*)(my + 16 * mb) = o[nb][mb];
+      }
+      __syncthreads();
       const int r = threadIdx.x >> 4, dseg = threadIdx.x & 15;
       float mw[kWaves], M = kNegBig;
 #pragma unroll
@@ -369,7 +436,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         L += fw[w] * sm_l[w * 16 + r];
       }
       const float inv = L > 0.f ? 1.0f / L : 0.f;
-      const int grow = row0 + r;
+      const int grow = row0 + 16 * nb + r;
 #pragma unroll
       for (int j = 0; j < kDv / 64; ++j) {
         const int d = 4 * dseg + 64 * j;
@@ -392,6 +459,300 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         }
       }
       if (dseg == 0) {
+        const float lse = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
+        if (slot < 0) {
+          if (a.lse) a.lse[(int64_t)b * R + grow] = lse;
+        } else {
+          a.part_lse[(int64_t)slot * R + grow] = lse;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Grouped split-decode kernel for 32 or 64 query rows per work-group.  GS waves
+// (one per 16 query rows) form a stream that consumes the same KV blocks; the
+// 4 / GS streams of a work-group take interleaved blocks of the piece.  A stream
+// owns 4 LDS step slots (8 blocks per work-group in all) that its waves fill
+// together with global->LDS DMA (each wave issues 9 of the loads of a step), and
+// the work-group moves from step to step behind one barrier, which both publishes
+// the step's DMA data to every wave and frees the slot read in the previous step
+// for the prefetch that is issued right after it.  Per block and wave the
+// arithmetic is that of split_decode_kernel with 16 rows.
+template <int GS, bool OUT_F32>
+__global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a) {
+  constexpr int NG = kWaves / GS;                       // streams per work-group
+  constexpr int SB = 2;                                  // blocks per stream and step (32 tokens)
+  constexpr int SLOTS = kWaves * kStages / (NG * SB);   // step slots per stream (2 or 4)
+  constexpr int LOADS = kLoadsPerBlock * SB / GS;       // DMA instructions per wave and step (18 or 9)
+  static_assert(LOADS * GS == kLoadsPerBlock * SB, "loads must split evenly over the stream");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
+  LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int gi = wave / GS, wi = wave % GS;             // stream, row group within the stream
+
+  int worker, rgroup;
+  if (a.row_groups == 1) {
+    worker = blockIdx.x;
+    rgroup = 0;
+  } else {
+    const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+    rgroup = y % a.row_groups;
+    worker = (y / a.row_groups) * 8 + x;
+  }
+  if (worker >= a.num_workers) return;
+  const int R = a.rows;
+  const int row0 = rgroup * 16 * GS + 16 * wi;
+
+  const int k_lane = (g * 16 + (n ^ ((g & 1) << 2))) * 16;
+  const int e = n >> 2, qq = n & 3;
+  const int v_lane = ((qq >> 1) * 16 + ((4 * g + e) ^ ((qq >> 1) << 2))) * 16 + (qq & 1) * 8;
+  const int ld_token = n ^ ((g & 1) << 2);
+  LDS_AS uint8_t* sbase = lds + gi * (SLOTS * SB * kBlockBytes);
+
+  const CST_AS int32_t* worker_off = as_const(a.worker_off);
+  const CST_AS int32_t* pieces = as_const(a.pieces);
+  const CST_AS int32_t* seqlens = as_const(a.seqlens);
+  const CST_AS int32_t* block_table = as_const(a.block_table);
+
+  const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
+  for (int pi = p_begin; pi < p_end; ++pi) {
+    const int b = pieces[4 * pi + 0];
+    const int tb = pieces[4 * pi + 1];
+    const int te = min(pieces[4 * pi + 2], seqlens[b]);
+    const int slot = pieces[4 * pi + 3];
+    const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
+    const int steps = (nblk + NG * SB - 1) / (NG * SB);
+
+    bf16x8_t qf[kKSteps];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)b * R + row0 + n) * kDqk + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
+    }
+    float m_ref = kNegBig, lsum = 0.f;
+    f32x4_t o[kVBlocks];
+#pragma unroll
+    for (int mb = 0; mb < kVBlocks; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // this lane's DMA source row for block blk of the piece (blocks past the end and
+    // out-of-range table entries read an in-bounds row; their compute is skipped)
+    auto source = [&](int blk) -> const uint16_t* {
+      const int bb = min(blk, nblk - 1);
+      const int tok0 = tb + kBlock * bb;
+      int64_t base = kv_row_of(block_table, a.bt_stride, a.page_size, a.num_pages, b, tok0);
+      if (base < 0) base = 0;
+      const int t = min(ld_token, te - 1 - tok0);
+      return a.kv + (base + t) * kDqk + 8 * g;
+    };
+    auto issue_step = [&](int k) {
+      LDS_AS uint8_t* dst = sbase + (k % SLOTS) * (SB * kBlockBytes);
+      const uint16_t* src0 = source((k * NG + gi) * SB);
+      const uint16_t* src1 = SB > 1 ? source((k * NG + gi) * SB + 1) : src0;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int I = wi + GS * i;                      // the stream's I-th DMA of this step
+        const int j = I / kLoadsPerBlock, jj = I % kLoadsPerBlock;
+        const uint16_t* src = j ? src1 : src0;
+        __builtin_amdgcn_global_load_lds((GLB_AS void*)(src + 32 * jj),
+                                         (LDS_AS void*)(dst + j * kBlockBytes + 1024 * jj), 16, 0, 0);
+      }
+    };
+    // S^T = K Q^T for one 16-token block: this lane's 4 scaled scores (log2 units)
+    auto scores = [&](LDS_AS uint8_t* st, int nvalid, float* s) {
+      f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      u32x4_t kf[6];
+      LDS_AS const uint8_t* kp = st + k_lane;
+      auto mma = [&](int kk0) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          f32x4_t& acc = (i & 1) ? acc2 : sacc;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[i]), qf[kk0 + i], acc, 0, 0, 0);
+        }
+      };
+      lds_read_b128x6<0>(kf, kp);
+      mma(0);
+      lds_read_b128x6<6144>(kf, kp);
+      mma(6);
+      lds_read_b128x6<12288>(kf, kp);
+      mma(12);
+      sacc += acc2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
+    };
+    // O^T += V^T P^T over the step's 32 tokens on 16x16x32 MFMA.  The contraction index
+    // k = 8g + j is token 4g + j of the first block (j < 4) or 4g + j - 4 of the second,
+    // which is both what the S^T layout leaves in this lane and what one transpose read
+    // per block delivers; a block that is not used contributes a zero V^T half.
+    // p = exp2(s - m_ref) goes in as bf16 hi + lo (about 16 mantissa bits).
+    auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[8], bool use0, bool use1) {
+      uint32_t hb[8], lb[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[i] - m_ref);
+        hb[i] = bf16_rne(p);
+        lb[i] = bf16_rne(p - bf16_bits_to_float(hb[i]));
+        lsum += p;
+      }
+      u32x4_t ph, pl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ph[i] = hb[2 * i] | (hb[2 * i + 1] << 16);
+        pl[i] = lb[2 * i] | (lb[2 * i + 1] << 16);
+      }
+      const uint32_t keep0 = use0 ? 0xFFFFFFFFu : 0u, keep1 = use1 ? 0xFFFFFFFFu : 0u;
+      LDS_AS const uint8_t* vp0 = st + v_lane;
+      LDS_AS const uint8_t* vp1 = st + kBlockBytes + v_lane;
+      u32x2_t va[8], vb[8];
+      auto pv = [&](int mb0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          u32x4_t v;
+          v[0] = va[i][0] & keep0;
+          v[1] = va[i][1] & keep0;
+          v[2] = vb[i][0] & keep1;
+          v[3] = vb[i][1] & keep1;
+          const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, v);
+          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, ph), o[mb0 + i], 0,
+                                                               0, 0);
+          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, pl), o[mb0 + i], 0,
+                                                               0, 0);
+        }
+      };
+      lds_read_tr8<0>(va, vp0);
+      lds_read_tr8<0>(vb, vp1);
+      pv(0);
+      lds_read_tr8<4096>(va, vp0);
+      lds_read_tr8<4096>(vb, vp1);
+      pv(8);
+      lds_read_tr8<8192>(va, vp0);
+      lds_read_tr8<8192>(vb, vp1);
+      pv(16);
+      lds_read_tr8<12288>(va, vp0);
+      lds_read_tr8<12288>(vb, vp1);
+      pv(24);
+    };
+
+    for (int k = 0; k < SLOTS - 1 && k < steps; ++k) issue_step(k);
+    int k = 0;
+    while (k < steps) {
+      float s[8], mx = 0.f;
+      bool rescale = false, use0 = false, use1 = false;
+      LDS_AS uint8_t* st = sbase;
+      for (; k < steps; ++k) {
+        if (SLOTS > 2 && steps - 1 - k >= 2) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+        } else if (SLOTS > 2 && steps - 1 - k == 1) {
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        // step k is in LDS (each wave waited for its own DMA) and every wave is done with
+        // step k-1, whose slot the prefetch below overwrites.  A bare s_barrier: a fenced
+        // __syncthreads would also wait for the prefetches still in flight.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (k + SLOTS - 1 < steps) issue_step(k + SLOTS - 1);
+        const int blk0 = (k * NG + gi) * SB;
+        const int tok0 = tb + kBlock * blk0, tok1 = tok0 + kBlock;
+        use0 = blk0 < nblk;
+        use1 = blk0 + 1 < nblk;
+        if (use0 && kv_row_of(block_table, a.bt_stride, a.page_size, a.num_pages, b, tok0) < 0) use0 = false;
+        if (use1 && kv_row_of(block_table, a.bt_stride, a.page_size, a.num_pages, b, tok1) < 0) use1 = false;
+        if ((blk0 < nblk && !use0) || (blk0 + 1 < nblk && !use1)) {
+          if (lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (!use0 && !use1) continue;
+        st = sbase + (k % SLOTS) * (SB * kBlockBytes);
+        scores(st, use0 ? te - tok0 : 0, s);
+        scores(st + kBlockBytes, use1 ? te - tok1 : 0, s + 4);
+        float m8 = s[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, s[i]);
+        mx = wave_max_over_groups(m8);
+        if (__any(mx > m_ref + kRescaleSlack)) {
+          rescale = true;
+          break;
+        }
+        accumulate(st, s, use0, use1);
+      }
+      if (!rescale) break;
+      // rare path: the running max grew past the slack; move the reference and rescale
+      {
+        const bool need = mx > m_ref + kRescaleSlack;
+        const float f = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
+        m_ref = need ? mx : m_ref;
+        lsum *= f;
+#pragma unroll
+        for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
+        accumulate(st, s, use0, use1);
+        ++k;
+      }
+    }
+
+    // ---- merge the NG streams' states per query row and write
+    const float lrow = wave_sum_over_groups(lsum);
+    __syncthreads();
+    LDS_AS float* buf = (LDS_AS float*)smem;                     // [stream][row group][16 rows][516]
+    LDS_AS float* sm_m = buf + kWaves * 16 * kMergeStride;       // [stream][row group][16]
+    LDS_AS float* sm_l = sm_m + kWaves * 16;
+    {
+      const int cell = gi * GS + wi;
+      if (g == 0) {
+        sm_m[cell * 16 + n] = m_ref;
+        sm_l[cell * 16 + n] = lrow;
+      }
+      LDS_AS float* my = buf + (cell * 16 + n) * kMergeStride + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < kVBlocks; ++mb) *(LDS_AS f32x4_t*)(my + 16 * mb) = o[mb];
+    }
+    __syncthreads();
+    {
+      constexpr int TPR = kThreads / (16 * GS);        // threads per query row
+      const int lr = threadIdx.x / TPR, part = threadIdx.x % TPR;
+      const int rgi = lr / 16, r = lr % 16;            // row group within the stream, row
+      float mw[NG], M = kNegBig;
+#pragma unroll
+      for (int s2 = 0; s2 < NG; ++s2) {
+        mw[s2] = sm_m[(s2 * GS + rgi) * 16 + r];
+        M = fmaxf(M, mw[s2]);
+      }
+      float fw[NG], L = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < NG; ++s2) {
+        fw[s2] = (mw[s2] <= kNegBig) ? 0.f : __builtin_amdgcn_exp2f(mw[s2] - M);
+        L += fw[s2] * sm_l[(s2 * GS + rgi) * 16 + r];
+      }
+      const float inv = L > 0.f ? 1.0f / L : 0.f;
+      const int grow = rgroup * 16 * GS + lr;
+#pragma unroll
+      for (int j = 0; j < kDv / (4 * TPR); ++j) {
+        const int d = 4 * part + 4 * TPR * j;
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < NG; ++s2)
+          acc += fw[s2] * *(LDS_AS const f32x4_t*)(buf + ((s2 * GS + rgi) * 16 + r) * kMergeStride + d);
+        acc *= inv;
+        if (slot < 0) {
+          const int64_t off = ((int64_t)b * R + grow) * kDv + d;
+          if (OUT_F32) {
+            *(f32x4_t*)((float*)a.out + off) = acc;
+          } else {
+            u32x2_t pkd;
+            pkd[0] = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
+            pkd[1] = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
+            *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
+          }
+        } else {
+          *(f32x4_t*)(a.part_o + ((int64_t)slot * R + grow) * kDv + d) = acc;
+        }
+      }
+      if (part == 0) {
         const float lse = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
         if (slot < 0) {
           if (a.lse) a.lse[(int64_t)b * R + grow] = lse;
@@ -485,11 +846,24 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint16_t* kv, const i
 
 int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (rows_per_group != 16) return (int)hipErrorInvalidValue;
-  if (out_fp32)
-    hipLaunchKernelGGL((split_decode_kernel<true>), dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((split_decode_kernel<false>), dim3(grid), dim3(kThreads), 0, s, a);
+  if (rows_per_group == 16) {
+    if (out_fp32)
+      hipLaunchKernelGGL((split_decode_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((split_decode_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else if (rows_per_group == 32) {
+    if (out_fp32)
+      hipLaunchKernelGGL((group_decode_kernel<2, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((group_decode_kernel<2, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else if (rows_per_group == 64) {
+    if (out_fp32)
+      hipLaunchKernelGGL((group_decode_kernel<4, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((group_decode_kernel<4, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else {
+    return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 

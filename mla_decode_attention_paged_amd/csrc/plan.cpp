@@ -34,7 +34,15 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
   const int32_t B = p.batch;
   const int64_t R = (int64_t)p.q_len * p.num_heads;
   pl.rows = (int32_t)R;
-  pl.rows_per_group = 16;   // query rows per work-group; more rows run as more row groups
+  // query rows per work-group: 16 (one wave each), 32 or 64 (grouped waves sharing KV);
+  // more rows run as several row groups over the same token ranges
+  if (R % 64 == 0) {
+    pl.rows_per_group = 64;
+  } else if (R == 32) {
+    pl.rows_per_group = 32;
+  } else {
+    pl.rows_per_group = 16;
+  }
   pl.row_groups = (int32_t)(R / pl.rows_per_group);
   pl.granule = kBlock;
 

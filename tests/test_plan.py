@@ -65,7 +65,9 @@ def test_plan_covers_every_token_once(name):
     for heads, q_len in ((16, 1), (16, 2), (128, 1)):
         plan = make_plan(lens, heads=heads, q_len=q_len)
         seg, off, info = check_plan(plan, lens)
-        assert info["row_groups"] == heads * q_len // 16
+        R = heads * q_len
+        assert info["rows_per_group"] == (64 if R % 64 == 0 else 32 if R == 32 else 16)
+        assert info["row_groups"] == R // info["rows_per_group"]
         workers = 256 // info["row_groups"]
         assert info["num_workers"] <= max(1, workers)
 
@@ -111,8 +113,8 @@ def test_empty_sequence_gets_an_empty_piece():
 
 
 def test_grid_padding_for_row_groups():
-    plan = make_plan([5000] * 3, heads=128)
+    plan = make_plan([5000] * 3, heads=48)
     info = plan.info()
-    assert info["row_groups"] == 8
+    assert info["row_groups"] == 3 and info["rows_per_group"] == 16
     assert info["grid_size"] % 8 == 0
-    assert info["grid_size"] == ((info["num_workers"] + 7) // 8 * 8) * 8
+    assert info["grid_size"] == ((info["num_workers"] + 7) // 8 * 8) * 3
