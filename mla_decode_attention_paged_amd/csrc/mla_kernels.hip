@@ -51,9 +51,13 @@ constexpr int kMergeStride = kDv + 4;              // floats per row in the merg
 #ifndef MLA_PROGRESSIVE_REFILL
 #define MLA_PROGRESSIVE_REFILL 1   // refill a stage part by part as its bytes are consumed
 #endif
+#ifndef MLA_LDS_SWIZZLE
+#define MLA_LDS_SWIZZLE 8          // token xor applied to odd 16-B column chunks in LDS
+#endif
 #ifndef MLA_CONTIG_BLOCKS
 #define MLA_CONTIG_BLOCKS 0        // 0: wave w takes blocks w, w+4, ...; 1: a contiguous quarter
 #endif
+constexpr int kSwz = MLA_LDS_SWIZZLE;
 
 // Physical row of logical token t of sequence b (the page walk).  Returns -1
 // when the block-table entry is outside [0, num_pages).
@@ -180,10 +184,10 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   // LDS block layout (16-B units): position = chunk*16 + (token ^ ((chunk & 1) << 2)),
   // chunk = 16-B column chunk 0..71, token 0..15.  K-operand reads are then 1 KB
   // contiguous and the V^T transpose reads touch all banks once per 16 lanes.
-  const int k_lane = (g * 16 + (n ^ ((g & 1) << 2))) * 16;
+  const int k_lane = (g * 16 + (n ^ ((g & 1) * kSwz))) * 16;
   const int e = n >> 2, qq = n & 3;
-  const int v_lane = ((qq >> 1) * 16 + ((4 * g + e) ^ ((qq >> 1) << 2))) * 16 + (qq & 1) * 8;
-  const int ld_token = n ^ ((g & 1) << 2);    // token this lane fetches for chunk 4*j + g
+  const int v_lane = ((qq >> 1) * 16 + ((4 * g + e) ^ ((qq >> 1) * kSwz))) * 16 + (qq & 1) * 8;
+  const int ld_token = n ^ ((g & 1) * kSwz);  // token this lane fetches for chunk 4*j + g
 
   LDS_AS uint8_t* stage0 = lds + (wave * kStages + 0) * kBlockBytes;
   LDS_AS uint8_t* stage1 = lds + (wave * kStages + 1) * kBlockBytes;
@@ -471,29 +475,30 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   }
 }
 
-// Grouped split-decode kernel for 32 or 64 query rows per work-group.  GS waves
-// (one per 16 query rows) form a stream that consumes the same KV blocks; the
-// 4 / GS streams of a work-group take interleaved blocks of the piece.  A stream
-// owns 4 LDS step slots (8 blocks per work-group in all) that its waves fill
-// together with global->LDS DMA (each wave issues 9 of the loads of a step), and
-// the work-group moves from step to step behind one barrier, which both publishes
-// the step's DMA data to every wave and frees the slot read in the previous step
-// for the prefetch that is issued right after it.  Per block and wave the
-// arithmetic is that of split_decode_kernel with 16 rows.
-template <int GS, bool OUT_F32>
+// Grouped split-decode kernel for 16 * RG query rows per work-group.  The four
+// waves consume the same KV stream: wave (rg, dh) owns query rows 16*rg..16*rg+15
+// and output columns [512*dh/DH, 512*(dh+1)/DH) with DH = 4 / RG.  Each step is
+// 32 tokens (two 16-token blocks); the work-group keeps four step slots in LDS
+// (three steps in flight), filled by global->LDS DMA split evenly over the waves
+// (9 loads each per step), and moves from step to step behind one barrier that
+// publishes the step's data and frees the slot read in the previous step.  Every
+// wave computes S^T for its rows over all 576 columns (the waves of a row group
+// repeat it) and O^T += V^T P^T for its columns on 16x16x32 MFMA with K = 32 tokens.
+template <int RG, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a) {
-  constexpr int NG = kWaves / GS;                       // streams per work-group
-  constexpr int SB = 2;                                  // blocks per stream and step (32 tokens)
-  constexpr int SLOTS = kWaves * kStages / (NG * SB);   // step slots per stream (2 or 4)
-  constexpr int LOADS = kLoadsPerBlock * SB / GS;       // DMA instructions per wave and step (18 or 9)
-  static_assert(LOADS * GS == kLoadsPerBlock * SB, "loads must split evenly over the stream");
+  constexpr int DH = kWaves / RG;                       // column parts
+  constexpr int SB = 2;                                 // blocks per step
+  constexpr int SLOTS = kWaves * kStages / SB;          // step slots (4)
+  constexpr int LOADS = kLoadsPerBlock * SB / kWaves;   // DMA instructions per wave and step (9)
+  constexpr int MBW = kVBlocks / DH;                    // 16-column output blocks per wave
+  static_assert(LOADS * kWaves == kLoadsPerBlock * SB && MBW % 8 == 0, "layout");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int gi = wave / GS, wi = wave % GS;             // stream, row group within the stream
+  const int rg = wave / DH, dh = wave % DH;
 
   int worker, rgroup;
   if (a.row_groups == 1) {
@@ -506,13 +511,13 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
   }
   if (worker >= a.num_workers) return;
   const int R = a.rows;
-  const int row0 = rgroup * 16 * GS + 16 * wi;
+  const int row0 = rgroup * 16 * RG + 16 * rg;
+  const int mb0 = dh * MBW;
 
-  const int k_lane = (g * 16 + (n ^ ((g & 1) << 2))) * 16;
+  const int k_lane = (g * 16 + (n ^ ((g & 1) * kSwz))) * 16;
   const int e = n >> 2, qq = n & 3;
-  const int v_lane = ((qq >> 1) * 16 + ((4 * g + e) ^ ((qq >> 1) << 2))) * 16 + (qq & 1) * 8;
-  const int ld_token = n ^ ((g & 1) << 2);
-  LDS_AS uint8_t* sbase = lds + gi * (SLOTS * SB * kBlockBytes);
+  const int v_lane = ((qq >> 1) * 16 + ((4 * g + e) ^ ((qq >> 1) * kSwz))) * 16 + (qq & 1) * 8 + mb0 * 512;
+  const int ld_token = n ^ ((g & 1) * kSwz);
 
   const CST_AS int32_t* worker_off = as_const(a.worker_off);
   const CST_AS int32_t* pieces = as_const(a.pieces);
@@ -526,7 +531,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
     const int te = min(pieces[4 * pi + 2], seqlens[b]);
     const int slot = pieces[4 * pi + 3];
     const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
-    const int steps = (nblk + NG * SB - 1) / (NG * SB);
+    const int steps = (nblk + SB - 1) / SB;
 
     bf16x8_t qf[kKSteps];
     {
@@ -535,12 +540,12 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
       for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
     }
     float m_ref = kNegBig, lsum = 0.f;
-    f32x4_t o[kVBlocks];
+    f32x4_t o[MBW];
 #pragma unroll
-    for (int mb = 0; mb < kVBlocks; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MBW; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // this lane's DMA source row for block blk of the piece (blocks past the end and
-    // out-of-range table entries read an in-bounds row; their compute is skipped)
+    // out-of-range table entries read an in-bounds row; they are not used)
     auto source = [&](int blk) -> const uint16_t* {
       const int bb = min(blk, nblk - 1);
       const int tok0 = tb + kBlock * bb;
@@ -550,12 +555,12 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
       return a.kv + (base + t) * kDqk + 8 * g;
     };
     auto issue_step = [&](int k) {
-      LDS_AS uint8_t* dst = sbase + (k % SLOTS) * (SB * kBlockBytes);
-      const uint16_t* src0 = source((k * NG + gi) * SB);
-      const uint16_t* src1 = SB > 1 ? source((k * NG + gi) * SB + 1) : src0;
+      LDS_AS uint8_t* dst = lds + (k % SLOTS) * (SB * kBlockBytes);
+      const uint16_t* src0 = source(k * SB);
+      const uint16_t* src1 = source(k * SB + 1);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int I = wi + GS * i;                      // the stream's I-th DMA of this step
+        const int I = wave + kWaves * i;                // the step's I-th DMA (of 36)
         const int j = I / kLoadsPerBlock, jj = I % kLoadsPerBlock;
         const uint16_t* src = j ? src1 : src0;
         __builtin_amdgcn_global_load_lds((GLB_AS void*)(src + 32 * jj),
@@ -584,10 +589,10 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
     };
-    // O^T += V^T P^T over the step's 32 tokens on 16x16x32 MFMA.  The contraction index
-    // k = 8g + j is token 4g + j of the first block (j < 4) or 4g + j - 4 of the second,
-    // which is both what the S^T layout leaves in this lane and what one transpose read
-    // per block delivers; a block that is not used contributes a zero V^T half.
+    // O^T += V^T P^T for this wave's columns over the step's 32 tokens.  The contraction
+    // index k = 8g + j is token 4g + j of the first block (j < 4) or 4g + j - 4 of the
+    // second: what the S^T layout leaves in this lane and what one transpose read per
+    // block delivers.  A block that is not used contributes a zero V^T half.
     // p = exp2(s - m_ref) goes in as bf16 hi + lo (about 16 mantissa bits).
     auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[8], bool use0, bool use1) {
       uint32_t hb[8], lb[8];
@@ -608,7 +613,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
       LDS_AS const uint8_t* vp0 = st + v_lane;
       LDS_AS const uint8_t* vp1 = st + kBlockBytes + v_lane;
       u32x2_t va[8], vb[8];
-      auto pv = [&](int mb0) {
+      auto pv = [&](int mbl) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           u32x4_t v;
@@ -617,24 +622,28 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
           v[2] = vb[i][0] & keep1;
           v[3] = vb[i][1] & keep1;
           const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, v);
-          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, ph), o[mb0 + i], 0,
+          o[mbl + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, ph), o[mbl + i], 0,
                                                                0, 0);
-          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, pl), o[mb0 + i], 0,
+          o[mbl + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, pl), o[mbl + i], 0,
                                                                0, 0);
         }
       };
       lds_read_tr8<0>(va, vp0);
       lds_read_tr8<0>(vb, vp1);
       pv(0);
-      lds_read_tr8<4096>(va, vp0);
-      lds_read_tr8<4096>(vb, vp1);
-      pv(8);
-      lds_read_tr8<8192>(va, vp0);
-      lds_read_tr8<8192>(vb, vp1);
-      pv(16);
-      lds_read_tr8<12288>(va, vp0);
-      lds_read_tr8<12288>(vb, vp1);
-      pv(24);
+      if constexpr (MBW > 8) {
+        lds_read_tr8<4096>(va, vp0);
+        lds_read_tr8<4096>(vb, vp1);
+        pv(8);
+      }
+      if constexpr (MBW > 16) {
+        lds_read_tr8<8192>(va, vp0);
+        lds_read_tr8<8192>(vb, vp1);
+        pv(16);
+        lds_read_tr8<12288>(va, vp0);
+        lds_read_tr8<12288>(vb, vp1);
+        pv(24);
+      }
     };
 
     for (int k = 0; k < SLOTS - 1 && k < steps; ++k) issue_step(k);
@@ -642,11 +651,11 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
     while (k < steps) {
       float s[8], mx = 0.f;
       bool rescale = false, use0 = false, use1 = false;
-      LDS_AS uint8_t* st = sbase;
+      LDS_AS uint8_t* st = lds;
       for (; k < steps; ++k) {
-        if (SLOTS > 2 && steps - 1 - k >= 2) {
+        if (steps - 1 - k >= 2) {
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
-        } else if (SLOTS > 2 && steps - 1 - k == 1) {
+        } else if (steps - 1 - k == 1) {
           asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -658,7 +667,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (k + SLOTS - 1 < steps) issue_step(k + SLOTS - 1);
-        const int blk0 = (k * NG + gi) * SB;
+        const int blk0 = k * SB;
         const int tok0 = tb + kBlock * blk0, tok1 = tok0 + kBlock;
         use0 = blk0 < nblk;
         use1 = blk0 + 1 < nblk;
@@ -668,7 +677,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
           if (lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (!use0 && !use1) continue;
-        st = sbase + (k % SLOTS) * (SB * kBlockBytes);
+        st = lds + (k % SLOTS) * (SB * kBlockBytes);
         scores(st, use0 ? te - tok0 : 0, s);
         scores(st + kBlockBytes, use1 ? te - tok1 : 0, s + 4);
         float m8 = s[0];
@@ -689,71 +698,38 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         m_ref = need ? mx : m_ref;
         lsum *= f;
 #pragma unroll
-        for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
+        for (int mb = 0; mb < MBW; ++mb) o[mb] *= f;
         accumulate(st, s, use0, use1);
         ++k;
       }
     }
 
-    // ---- merge the NG streams' states per query row and write
-    const float lrow = wave_sum_over_groups(lsum);
-    __syncthreads();
-    LDS_AS float* buf = (LDS_AS float*)smem;                     // [stream][row group][16 rows][516]
-    LDS_AS float* sm_m = buf + kWaves * 16 * kMergeStride;       // [stream][row group][16]
-    LDS_AS float* sm_l = sm_m + kWaves * 16;
+    // ---- write: every wave holds complete rows for its columns (all waves of a row
+    // group agree on m_ref and l, having computed the same scores)
     {
-      const int cell = gi * GS + wi;
-      if (g == 0) {
-        sm_m[cell * 16 + n] = m_ref;
-        sm_l[cell * 16 + n] = lrow;
-      }
-      LDS_AS float* my = buf + (cell * 16 + n) * kMergeStride + 4 * g;
+      const float l = wave_sum_over_groups(lsum);
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      const int grow = row0 + n;
 #pragma unroll
-      for (int mb = 0; mb < kVBlocks; ++mb) *(LDS_AS f32x4_t*)(my + 16 * mb) = o[mb];
-    }
-    __syncthreads();
-    {
-      constexpr int TPR = kThreads / (16 * GS);        // threads per query row
-      const int lr = threadIdx.x / TPR, part = threadIdx.x % TPR;
-      const int rgi = lr / 16, r = lr % 16;            // row group within the stream, row
-      float mw[NG], M = kNegBig;
-#pragma unroll
-      for (int s2 = 0; s2 < NG; ++s2) {
-        mw[s2] = sm_m[(s2 * GS + rgi) * 16 + r];
-        M = fmaxf(M, mw[s2]);
-      }
-      float fw[NG], L = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < NG; ++s2) {
-        fw[s2] = (mw[s2] <= kNegBig) ? 0.f : __builtin_amdgcn_exp2f(mw[s2] - M);
-        L += fw[s2] * sm_l[(s2 * GS + rgi) * 16 + r];
-      }
-      const float inv = L > 0.f ? 1.0f / L : 0.f;
-      const int grow = rgroup * 16 * GS + lr;
-#pragma unroll
-      for (int j = 0; j < kDv / (4 * TPR); ++j) {
-        const int d = 4 * part + 4 * TPR * j;
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s2 = 0; s2 < NG; ++s2)
-          acc += fw[s2] * *(LDS_AS const f32x4_t*)(buf + ((s2 * GS + rgi) * 16 + r) * kMergeStride + d);
-        acc *= inv;
+      for (int mb = 0; mb < MBW; ++mb) {
+        const int d = 16 * (mb0 + mb) + 4 * g;
+        const f32x4_t v = o[mb] * inv;
         if (slot < 0) {
           const int64_t off = ((int64_t)b * R + grow) * kDv + d;
           if (OUT_F32) {
-            *(f32x4_t*)((float*)a.out + off) = acc;
+            *(f32x4_t*)((float*)a.out + off) = v;
           } else {
             u32x2_t pkd;
-            pkd[0] = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
-            pkd[1] = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
+            pkd[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+            pkd[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
             *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
           }
         } else {
-          *(f32x4_t*)(a.part_o + ((int64_t)slot * R + grow) * kDv + d) = acc;
+          *(f32x4_t*)(a.part_o + ((int64_t)slot * R + grow) * kDv + d) = v;
         }
       }
-      if (part == 0) {
-        const float lse = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
+      if (dh == 0 && g == 0) {
+        const float lse = l > 0.f ? (m_ref + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
         if (slot < 0) {
           if (a.lse) a.lse[(int64_t)b * R + grow] = lse;
         } else {
@@ -761,7 +737,10 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         }
       }
     }
-    __syncthreads();
+    // the next piece's prefetch reuses the slots: every wave must be done reading them
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
 }
 
