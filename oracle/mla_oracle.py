@@ -29,7 +29,10 @@ What is computed (plain definitions, written out; every float op in float64):
 Readings where the pages are silent (each is listed in the design notes):
   - lse is the natural log of sum_t exp(s_t) with s_t = scale * q . k_t;
   - an empty context (L = 0) gives out = 0 and lse = -inf;
-  - both query tokens of a two-token query see all L cached tokens (no mask);
+  - by default both query tokens of a two-token query see all L cached tokens
+    (no mask); with ``causal=True`` query token i of S_q sits at position
+    L - S_q + i and sees tokens t <= L - S_q + i (the S_q new tokens' rows are
+    already in the cache, as for speculative / multi-token decode);
   - rows past L and unmapped block_table entries are never read.
 """
 from __future__ import annotations
@@ -79,19 +82,26 @@ def attend(q_rows: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, scale: fl
 
 
 def decode_sequence(q_b: np.ndarray, kv_cache: np.ndarray, block_table_row: np.ndarray,
-                    length: int, softmax_scale: float, page_size: int):
+                    length: int, softmax_scale: float, page_size: int, causal: bool = False):
     """One sequence: q_b [S_q, H, 576] bits -> (out [S_q, H, 512], lse [S_q, H]) float64."""
     s_q, h = q_b.shape[0], q_b.shape[1]
     rows = gather_sequence(kv_cache, block_table_row, length, page_size)
     k = widen_bf16(rows)
-    q = widen_bf16(q_b).reshape(s_q * h, D_QK)
-    out, lse = attend(q, k, k[:, :D_V], softmax_scale)
-    return out.reshape(s_q, h, D_V), lse.reshape(s_q, h)
+    if not causal:
+        q = widen_bf16(q_b).reshape(s_q * h, D_QK)
+        out, lse = attend(q, k, k[:, :D_V], softmax_scale)
+        return out.reshape(s_q, h, D_V), lse.reshape(s_q, h)
+    out = np.empty((s_q, h, D_V))
+    lse = np.empty((s_q, h))
+    for i in range(s_q):
+        visible = max(0, int(length) - s_q + i + 1)       # tokens t <= L - S_q + i
+        out[i], lse[i] = attend(widen_bf16(q_b[i]), k[:visible], k[:visible, :D_V], softmax_scale)
+    return out, lse
 
 
 def decode(q: np.ndarray, kv_cache: np.ndarray, block_table: np.ndarray,
            cache_seqlens: np.ndarray, softmax_scale: float, page_size: int,
-           batch_indices=None):
+           batch_indices=None, causal: bool = False):
     """Paged MLA decode for every (or the listed) sequence.
 
     q [B, S_q, H, 576] bf16 bits; kv_cache [num_pages, page_size, 576] bf16 bits;
@@ -105,7 +115,7 @@ def decode(q: np.ndarray, kv_cache: np.ndarray, block_table: np.ndarray,
     idx = range(B) if batch_indices is None else batch_indices
     for b in idx:
         out[b], lse[b] = decode_sequence(q[b], kv_cache, block_table[b], int(cache_seqlens[b]),
-                                         softmax_scale, page_size)
+                                         softmax_scale, page_size, causal)
     return out, lse
 
 

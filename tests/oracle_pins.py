@@ -53,8 +53,9 @@ def _bf16_to_decimal(bits: int) -> Decimal:
         return sign * v
 
 
-def decimal_decode(q, kv, block_table, seqlens, scale, page_size, rows=None):
-    """Brute-force paged MLA decode at 40 significant digits. Returns nested lists."""
+def decimal_decode(q, kv, block_table, seqlens, scale, page_size, rows=None, causal=False):
+    """Brute-force paged MLA decode at 40 significant digits. Returns nested lists.
+    causal: query token i of S_q sees tokens t <= L - S_q + i."""
     results = {}
     with localcontext() as ctx:
         ctx.prec = 40
@@ -71,12 +72,16 @@ def decimal_decode(q, kv, block_table, seqlens, scale, page_size, rows=None):
                     if rows is not None and (b, i, h) not in rows:
                         continue
                     qv = [_bf16_to_decimal(x) for x in q[b, i, h].tolist()]
-                    s = [sc * sum(qd * kd for qd, kd in zip(qv, k)) for k in keys]
+                    vis = keys if not causal else keys[:max(0, L - S + i + 1)]
+                    if not vis:
+                        results[(b, i, h)] = ([0.0] * D_V, float("-inf"))
+                        continue
+                    s = [sc * sum(qd * kd for qd, kd in zip(qv, k)) for k in vis]
                     m = max(s)
                     z = sum((st - m).exp() for st in s)
                     lse = m + z.ln()
                     w = [(st - lse).exp() for st in s]
-                    out = [sum(w[t] * keys[t][d] for t in range(L)) for d in range(D_V)]
+                    out = [sum(w[t] * vis[t][d] for t in range(len(vis))) for d in range(D_V)]
                     results[(b, i, h)] = ([float(x) for x in out], float(lse))
     return results
 
@@ -255,5 +260,40 @@ def split_combine(attend_fn, combine_fn):
         assert np.max(np.abs(o - o_ref)) <= TOL and np.max(np.abs(l - l_ref)) <= TOL, f"split/combine at {cuts}"
 
 
+
+
+def causal_decimal(decode_fn):
+    """Causal two-token queries against the decimal brute force (including L = 1, where
+    the first query token sees nothing)."""
+    for c in (dict(batch=3, q_len=2, num_heads=2, page_size=16, lengths=[1, 2, 18], seed=91),
+              dict(batch=1, q_len=3, num_heads=2, page_size=16, lengths=[5], seed=92)):
+        p = gen.make_problem(**c)
+        out, lse = decode_fn(p.q, p.kv_cache, p.block_table, p.cache_seqlens, p.softmax_scale, p.page_size,
+                             causal=True)
+        ref = decimal_decode(p.q, p.kv_cache, p.block_table, p.cache_seqlens, p.softmax_scale, p.page_size,
+                             causal=True)
+        for (b, i, h), (o_ref, l_ref) in ref.items():
+            if l_ref == float("-inf"):
+                assert np.all(out[b, i, h] == 0) and lse[b, i, h] == -np.inf, "causal: empty row"
+                continue
+            assert np.max(np.abs(out[b, i, h] - np.asarray(o_ref))) <= TOL and abs(lse[b, i, h] - l_ref) <= TOL
+
+
+def causal_decomposition(decode_fn):
+    """Causal query token i of S_q == a one-token query over the first L - S_q + i + 1 tokens."""
+    P = 16
+    p = gen.make_problem(batch=3, q_len=2, num_heads=16, page_size=P, lengths=[40, 17, 2], seed=93)
+    o, l = decode_fn(p.q, p.kv_cache, p.block_table, p.cache_seqlens, p.softmax_scale, P, causal=True)
+    for i in range(2):
+        lens = np.maximum(p.cache_seqlens - 2 + i + 1, 0).astype(np.int32)
+        oi, li = decode_fn(np.ascontiguousarray(p.q[:, i:i + 1]), p.kv_cache, p.block_table, lens,
+                           p.softmax_scale, P)
+        assert np.max(np.abs(oi[:, 0] - o[:, i])) <= TOL and np.max(np.abs(li[:, 0] - l[:, i])) <= TOL
+    # and the last query token sees everything: same as the unmasked call
+    o2, l2 = decode_fn(p.q, p.kv_cache, p.block_table, p.cache_seqlens, p.softmax_scale, P)
+    assert np.max(np.abs(o2[:, 1] - o[:, 1])) <= TOL
+    assert np.max(np.abs(o2[:, 0] - o[:, 0])) > 1e-6, "mask had no effect"
+
+
 ALL_DECODE_PINS = [decimal_brute_force, single_token, equal_scores, shift_invariance, page_permutation,
-                   decomposition, sdpa_special_case]
+                   decomposition, sdpa_special_case, causal_decimal, causal_decomposition]

@@ -150,3 +150,11 @@ def test_ragged_lengths_drawn_in_range():
     assert p.cache_seqlens.min() >= 16 and p.cache_seqlens.max() <= 1024
     used = np.sort(p.block_table[p.block_table >= 0])
     assert np.array_equal(used, np.arange(p.num_pages))
+
+
+def test_pin_causal_decimal():
+    pins.causal_decimal(orc.decode)
+
+
+def test_pin_causal_decomposition():
+    pins.causal_decomposition(orc.decode)

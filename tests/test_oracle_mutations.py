@@ -54,10 +54,24 @@ def _gather_reversed_row(kv_cache, block_table_row, length, page_size):
 
 
 def _decode_sequence_variant(kind):
-    def decode_sequence(q_b, kv_cache, block_table_row, length, softmax_scale, page_size):
+    def decode_sequence(q_b, kv_cache, block_table_row, length, softmax_scale, page_size, causal=False):
         s_q, h = q_b.shape[0], q_b.shape[1]
         rows = orc.gather_sequence(kv_cache, block_table_row, length, page_size)
         k = orc.widen_bf16(rows)
+        if causal:
+            out = np.empty((s_q, h, 512))
+            lse = np.empty((s_q, h))
+            for i in range(s_q):
+                if kind == "causal_off_by_one":
+                    vis = max(0, int(length) - s_q + i)
+                elif kind == "causal_reversed":
+                    vis = max(0, int(length) - i)
+                elif kind == "causal_ignored":
+                    vis = int(length)
+                else:
+                    vis = max(0, int(length) - s_q + i + 1)
+                out[i], lse[i] = orc.attend(orc.widen_bf16(q_b[i]), k[:vis], k[:vis, :512], softmax_scale)
+            return out, lse
         if kind == "heads_tokens_swapped":
             q = orc.widen_bf16(q_b).transpose(1, 0, 2).reshape(s_q * h, 576)
         else:
@@ -95,6 +109,9 @@ MUTANTS = {
     "reversed_row": ("gather_sequence", _gather_reversed_row),
     "v_last_columns": ("decode_sequence", _decode_sequence_variant("v_last_columns")),
     "heads_tokens_swapped": ("decode_sequence", _decode_sequence_variant("heads_tokens_swapped")),
+    "causal_off_by_one": ("decode_sequence", _decode_sequence_variant("causal_off_by_one")),
+    "causal_reversed": ("decode_sequence", _decode_sequence_variant("causal_reversed")),
+    "causal_ignored": ("decode_sequence", _decode_sequence_variant("causal_ignored")),
     "combine_sign": ("combine", _combine_variant("sign")),
     "combine_unnormalised": ("combine", _combine_variant("unnormalised")),
 }
