@@ -8,8 +8,14 @@
  *     k_t      = kv_cache[block_table[b][t / page_size]][t % page_size][0:576]
  *     v_t      = k_t[0:512]
  *     s_t      = softmax_scale * sum_d q[b][i][h][d] * k_t[d]        (d < 576)
- *     lse      = log sum_{t<L} exp(s_t)                               (natural log)
- *     out[:]   = sum_{t<L} exp(s_t - lse) * v_t
+ *     lse      = log sum_{t<E} exp(s_t)                               (natural log)
+ *     out[:]   = sum_{t<E} exp(s_t - lse) * v_t
+ *
+ * where E = L, or, for a causal problem, E = max(0, L - (q_len - 1 - i)): query
+ * token i then sits at position L - q_len + i of a context whose last q_len
+ * rows are the query tokens' own (multi-token / speculative decode), and sees
+ * only the tokens up to and including itself.  A row with E = 0 gets out = 0
+ * and lse = -inf.
  *
  * This is standard attention S = Q K^T, P = softmax(S), O = P V ("Core
  * mechanism", FlashMLA-ETAP summary on gist.science), in the absorbed MLA form
@@ -51,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum {
   MLA_OK = 0,
@@ -67,7 +73,7 @@ typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype_t;
 /* Shapes of one decode call. */
 typedef struct {
   int32_t batch;              /* B >= 1 */
-  int32_t q_len;              /* S_q >= 1 query tokens per sequence (no mask between them) */
+  int32_t q_len;              /* S_q >= 1 query tokens per sequence */
   int32_t num_heads;          /* H >= 1; R = q_len * num_heads must be a multiple of 16, <= 128 */
   int32_t head_dim_qk;        /* must be 576 (512 latent + 64 rope) */
   int32_t head_dim_v;         /* must be 512 */
@@ -75,6 +81,8 @@ typedef struct {
   int32_t num_pages;          /* physical pages in kv_cache (dimension 0) */
   int32_t max_pages_per_seq;  /* row stride of block_table, in int32 entries */
   mla_dtype_t out_dtype;      /* dtype of `out`: BF16 (round to nearest even) or FP32 */
+  int32_t causal;             /* 0: every query token sees all L tokens; 1: token i sees the
+                                 first L - (q_len - 1 - i) (see the definition above) */
 } mla_problem_t;
 
 /* Planner options.  Zero-initialise for defaults. */

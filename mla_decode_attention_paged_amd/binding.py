@@ -34,7 +34,8 @@ class MlaError(RuntimeError):
 class mla_problem_t(C.Structure):
     _fields_ = [("batch", C.c_int32), ("q_len", C.c_int32), ("num_heads", C.c_int32),
                 ("head_dim_qk", C.c_int32), ("head_dim_v", C.c_int32), ("page_size", C.c_int32),
-                ("num_pages", C.c_int32), ("max_pages_per_seq", C.c_int32), ("out_dtype", C.c_int32)]
+                ("num_pages", C.c_int32), ("max_pages_per_seq", C.c_int32), ("out_dtype", C.c_int32),
+                ("causal", C.c_int32)]
 
 
 class mla_plan_options_t(C.Structure):
@@ -105,9 +106,9 @@ def abi_version() -> int:
 
 
 def make_problem(batch, q_len, num_heads, page_size, num_pages, max_pages_per_seq, out_fp32=False,
-                 head_dim_qk=576, head_dim_v=512) -> mla_problem_t:
+                 head_dim_qk=576, head_dim_v=512, causal=False) -> mla_problem_t:
     return mla_problem_t(batch, q_len, num_heads, head_dim_qk, head_dim_v, page_size, num_pages,
-                         max_pages_per_seq, MLA_DTYPE_FP32 if out_fp32 else MLA_DTYPE_BF16)
+                         max_pages_per_seq, MLA_DTYPE_FP32 if out_fp32 else MLA_DTYPE_BF16, int(causal))
 
 
 class Plan:

@@ -39,6 +39,8 @@ mla_status_t check_problem(const mla_problem_t* p) {
     return fail(MLA_ERR_INVALID_ARGUMENT, "max_pages_per_seq must be >= 1 (got %d)", p->max_pages_per_seq);
   if (p->out_dtype != MLA_DTYPE_BF16 && p->out_dtype != MLA_DTYPE_FP32)
     return fail(MLA_ERR_INVALID_ARGUMENT, "out_dtype must be MLA_DTYPE_BF16 or MLA_DTYPE_FP32");
+  if (p->causal != 0 && p->causal != 1)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", p->causal);
   if (p->head_dim_qk != mla::kDqk || p->head_dim_v != mla::kDv)
     return fail(MLA_ERR_UNSUPPORTED, "head dims must be 576/512 (got %d/%d)", p->head_dim_qk, p->head_dim_v);
   if (p->page_size % mla::kBlock != 0)
@@ -224,6 +226,9 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
   a.bt_stride = p.prob.max_pages_per_seq;
   a.num_workers = p.num_workers;
   a.row_groups = p.row_groups;
+  a.q_len = p.prob.q_len;
+  a.num_heads = p.prob.num_heads;
+  a.causal = p.prob.causal;
   const bool f32 = p.prob.out_dtype == MLA_DTYPE_FP32;
   if ((stages & MLA_STAGE_SPLIT) && p.grid > 0) {
     int e = mla::launch_decode(a, p.rows_per_group, f32, p.grid, stream);

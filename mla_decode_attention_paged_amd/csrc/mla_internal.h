@@ -78,6 +78,9 @@ struct DecodeArgs {
   int32_t bt_stride;
   int32_t num_workers;
   int32_t row_groups;
+  int32_t q_len;
+  int32_t num_heads;
+  int32_t causal;                // row r = i * num_heads + h sees t < L - (q_len - 1 - i)
 };
 
 struct MergeArgs {

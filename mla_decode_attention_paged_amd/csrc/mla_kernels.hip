@@ -204,6 +204,14 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     const int te = min(pieces[4 * pi + 2], seqlens[b]);
     const int slot = pieces[4 * pi + 3];
     const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
+    // end of the tokens this lane's query row sees: te, or for a causal problem the
+    // first L - (q_len - 1 - i) tokens of the sequence (row = i * num_heads + h)
+    int lim[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int qi = (row0 + 16 * nb + n) / a.num_heads;
+      lim[nb] = a.causal ? min(te, seqlens[b] - (a.q_len - 1 - qi)) : te;
+    }
 #if MLA_CONTIG_BLOCKS
     const int blk_first = (wave * nblk) / kWaves;
     const int my_n = ((wave + 1) * nblk) / kWaves - blk_first;
@@ -373,12 +381,13 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           if (nsrc) issue(nsrc, st, 0, kLoadsPerBlock);
           continue;
         }
-        const int nvalid = te - (tb + kBlock * blk_of(k));   // >= 1
+        const int tok0 = tb + kBlock * blk_of(k);
         f32x4_t sacc[NB];
         scores(st, sacc, nsrc);
         bool grow = false;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+          const int nvalid = lim[nb] - tok0;   // tokens of the block this row sees (may be <= 0)
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[nb][i] = (4 * g + i < nvalid) ? sacc[nb][i] * a.scale_log2 : -INFINITY;
           mx[nb] = wave_max_over_groups(fmaxf(fmaxf(s[nb][0], s[nb][1]), fmaxf(s[nb][2], s[nb][3])));
@@ -532,6 +541,8 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
     const int slot = pieces[4 * pi + 3];
     const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
     const int steps = (nblk + SB - 1) / SB;
+    // end of the tokens this lane's query row sees (causal: the first L - (q_len - 1 - i))
+    const int lim = a.causal ? min(te, seqlens[b] - (a.q_len - 1 - (row0 + n) / a.num_heads)) : te;
 
     bf16x8_t qf[kKSteps];
     {
@@ -678,8 +689,8 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         }
         if (!use0 && !use1) continue;
         st = lds + (k % SLOTS) * (SB * kBlockBytes);
-        scores(st, use0 ? te - tok0 : 0, s);
-        scores(st + kBlockBytes, use1 ? te - tok1 : 0, s + 4);
+        scores(st, use0 ? lim - tok0 : 0, s);
+        scores(st + kBlockBytes, use1 ? lim - tok1 : 0, s + 4);
         float m8 = s[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, s[i]);

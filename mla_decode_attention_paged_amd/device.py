@@ -16,19 +16,20 @@ def to_device(prob, device="cuda"):
     return {"q": q, "kv_cache": kv, "block_table": bt, "cache_seqlens": sl}
 
 
-def problem_struct(prob):
+def problem_struct(prob, causal=False):
     return B.make_problem(prob.batch, prob.q_len, prob.num_heads, prob.page_size, prob.num_pages,
-                          prob.max_pages_per_seq, out_fp32=prob.out_fp32)
+                          prob.max_pages_per_seq, out_fp32=prob.out_fp32, causal=causal)
 
 
 class Runner:
     """Plan + workspace + outputs for one problem on one device; call() launches the decode."""
 
-    def __init__(self, prob, dev=None, num_cus=0, force_splits=0, device="cuda"):
+    def __init__(self, prob, dev=None, num_cus=0, force_splits=0, device="cuda", causal=False):
         import torch
         self.prob = prob
         self.dev = dev if dev is not None else to_device(prob, device)
-        self.plan = B.Plan(problem_struct(prob), prob.cache_seqlens, num_cus=num_cus, force_splits=force_splits)
+        self.plan = B.Plan(problem_struct(prob, causal), prob.cache_seqlens, num_cus=num_cus,
+                           force_splits=force_splits)
         self.ws = B.alloc_workspace(self.plan, device)
         self.plan.upload(self.ws)
         odt = torch.float32 if prob.out_fp32 else torch.bfloat16

@@ -23,7 +23,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) >= 12
     for n in names:
         assert hasattr(lib, n), f"libmla.so does not export {n}"
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
 
 
 def test_status_strings():
@@ -61,6 +61,8 @@ def _plan(batch=2, q_len=1, heads=16, page=64, lens=(100, 200), num_pages=None, 
     (dict(lens=(100, 200), maxp=2), B.MLA_ERR_INVALID_ARGUMENT),  # 200 > 2*64
     (dict(num_cus=-1), B.MLA_ERR_INVALID_ARGUMENT),
     (dict(force=-2), B.MLA_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), B.MLA_ERR_INVALID_ARGUMENT),
+    (dict(causal=-1), B.MLA_ERR_INVALID_ARGUMENT),
 ])
 def test_plan_rejects_bad_problems(kw, status):
     with pytest.raises(B.MlaError) as ei:
