@@ -4,7 +4,10 @@
 // Split-decode kernel, one work-group (4 waves) per piece list from the planner.
 // Each wave streams its own 16-token KV blocks (blocks w, w+4, w+8, ... of a
 // piece) through a private two-stage LDS ring filled by 16-byte
-// global->LDS DMA loads, and keeps its own online-softmax state.  Per block it
+// global->LDS DMA loads (each instruction moves 128 contiguous bytes of 8 cache
+// rows), and keeps its own online-softmax state.  A block's K and V^T operands
+// are read out of LDS first, so its stage is refilled while the block is still
+// being computed.  Per block it
 // evaluates the transposed flow of the FlashMLA-ETAP summary ("Core
 // mechanism"): S^T = K Q^T on bf16 MFMA with the 16 tokens on the M side and
 // the query rows on N, then P^T = exp2(S^T - m), then O^T += V^T P^T, again
@@ -48,16 +51,9 @@ constexpr float kRescaleSlack = 8.0f;              // lazy rescale threshold (lo
 constexpr float kNegBig = -1.0e30f;                // running-max start value (finite)
 constexpr int kMergeStride = kDv + 4;              // floats per row in the merge buffer
 
-#ifndef MLA_PROGRESSIVE_REFILL
-#define MLA_PROGRESSIVE_REFILL 1   // refill a stage part by part as its bytes are consumed
-#endif
-#ifndef MLA_LDS_SWIZZLE
-#define MLA_LDS_SWIZZLE 8          // token xor applied to odd 16-B column chunks in LDS
-#endif
-#ifndef MLA_CONTIG_BLOCKS
-#define MLA_CONTIG_BLOCKS 0        // 0: wave w takes blocks w, w+4, ...; 1: a contiguous quarter
-#endif
-constexpr int kSwz = MLA_LDS_SWIZZLE;
+// Chunk-major block layout of the grouped kernel (16-B units): chunk c of token t sits at
+// 16 * c + (t ^ ((c & 1) * kSwz)).
+constexpr int kSwz = 8;
 
 // Physical row of logical token t of sequence b (the page walk).  Returns -1
 // when the block-table entry is outside [0, num_pages).
@@ -98,7 +94,8 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_
 
 
 // Batched LDS reads in inline asm, each block waiting for its own reads before it
-// ends.  Issuing a batch back to back (instead of one read, one wait) keeps many
+// ends.  Outputs are early-clobber: a read can return while later reads of the same
+// block still need their address registers, so no output may share one.  Issuing a batch back to back (instead of one read, one wait) keeps many
 // LDS requests in flight; doing it in asm also keeps the compiler from adding a
 // wait for the in-flight global->LDS prefetch of the other stage before every read.
 #define MLA_O4(b, s) "i"(b), "i"(b + s), "i"(b + 2 * s), "i"(b + 3 * s)
@@ -110,19 +107,8 @@ __device__ __forceinline__ void lds_read_b128x6(u32x4_t (&r)[6], LDS_AS const ui
       "ds_read_b128 %0, %6 offset:%7\n\tds_read_b128 %1, %6 offset:%8\n\tds_read_b128 %2, %6 offset:%9\n\t"
       "ds_read_b128 %3, %6 offset:%10\n\tds_read_b128 %4, %6 offset:%11\n\tds_read_b128 %5, %6 offset:%12\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5])
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
       : "v"(p), MLA_O4(OFF, 1024), "i"(OFF + 4096), "i"(OFF + 5120)
-      : "memory");
-}
-template <int OFF>
-__device__ __forceinline__ void lds_read_b128x9(u32x4_t (&r)[9], LDS_AS const uint8_t* p) {
-  asm volatile(
-      "ds_read_b128 %0, %9 offset:%10\n\tds_read_b128 %1, %9 offset:%11\n\tds_read_b128 %2, %9 offset:%12\n\t"
-      "ds_read_b128 %3, %9 offset:%13\n\tds_read_b128 %4, %9 offset:%14\n\tds_read_b128 %5, %9 offset:%15\n\t"
-      "ds_read_b128 %6, %9 offset:%16\n\tds_read_b128 %7, %9 offset:%17\n\tds_read_b128 %8, %9 offset:%18\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]), "=v"(r[8])
-      : "v"(p), MLA_O4(OFF, 1024), MLA_O4(OFF + 4096, 1024), "i"(OFF + 8192)
       : "memory");
 }
 // transpose reads (4 tokens x 16 columns per 16 lanes) at p + OFF + 512*i
@@ -134,30 +120,64 @@ __device__ __forceinline__ void lds_read_tr8(u32x2_t (&r)[8], LDS_AS const uint8
       "ds_read_b64_tr_b16 %4, %8 offset:%13\n\tds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
       "ds_read_b64_tr_b16 %6, %8 offset:%15\n\tds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7])
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
       : "v"(p), MLA_O4(OFF, 512), MLA_O4(OFF + 2048, 512)
       : "memory");
 }
-template <int OFF>
-__device__ __forceinline__ void lds_read_tr16(u32x2_t (&r)[16], LDS_AS const uint8_t* p) {
+// Row-major block layout of the split kernel (16-B units): chunk c of token t sits at
+// 128 * (c / 8) + 8 * t + ((c % 8) ^ row_swz(t)).  One DMA instruction fills 8 tokens x
+// 8 chunks (128 contiguous bytes of each row); the xor spreads the K reads (16 tokens x
+// one chunk) and the V^T transpose reads over all LDS banks.
+__device__ __forceinline__ int row_swz(int t) { return ((t & 2) << 1) | ((t & 4) >> 1); }
+
+// K operand reads of the row-major layout: k-steps K0..K0+8, even ones at pe + 2048*(kk/2),
+// odd ones at po + 2048*(kk/2)
+template <int K0>
+__device__ __forceinline__ void lds_read_k9(u32x4_t (&r)[9], LDS_AS const uint8_t* pe, LDS_AS const uint8_t* po) {
+  if constexpr (K0 == 0) {
+    asm volatile(
+        "ds_read_b128 %0, %9 offset:0\n\tds_read_b128 %1, %10 offset:0\n\tds_read_b128 %2, %9 offset:2048\n\t"
+        "ds_read_b128 %3, %10 offset:2048\n\tds_read_b128 %4, %9 offset:4096\n\tds_read_b128 %5, %10 offset:4096\n\t"
+        "ds_read_b128 %6, %9 offset:6144\n\tds_read_b128 %7, %10 offset:6144\n\tds_read_b128 %8, %9 offset:8192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8])
+        : "v"(pe), "v"(po)
+        : "memory");
+  } else {
+    static_assert(K0 == 9, "two halves");
+    asm volatile(
+        "ds_read_b128 %0, %10 offset:8192\n\tds_read_b128 %1, %9 offset:10240\n\tds_read_b128 %2, %10 offset:10240\n\t"
+        "ds_read_b128 %3, %9 offset:12288\n\tds_read_b128 %4, %10 offset:12288\n\tds_read_b128 %5, %9 offset:14336\n\t"
+        "ds_read_b128 %6, %10 offset:14336\n\tds_read_b128 %7, %9 offset:16384\n\tds_read_b128 %8, %10 offset:16384\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8])
+        : "v"(pe), "v"(po)
+        : "memory");
+  }
+}
+// V^T transpose reads of the row-major layout: column blocks mb = 16*H .. 16*H+15, block mb at
+// p[mb % 4] + 2048 * (mb / 4)
+template <int H>
+__device__ __forceinline__ void lds_read_v16(u32x2_t (&r)[16], LDS_AS const uint8_t* const (&p)[4]) {
+  constexpr int B = 8192 * H;
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:%17\n\tds_read_b64_tr_b16 %1, %16 offset:%18\n\t"
-      "ds_read_b64_tr_b16 %2, %16 offset:%19\n\tds_read_b64_tr_b16 %3, %16 offset:%20\n\t"
-      "ds_read_b64_tr_b16 %4, %16 offset:%21\n\tds_read_b64_tr_b16 %5, %16 offset:%22\n\t"
-      "ds_read_b64_tr_b16 %6, %16 offset:%23\n\tds_read_b64_tr_b16 %7, %16 offset:%24\n\t"
-      "ds_read_b64_tr_b16 %8, %16 offset:%25\n\tds_read_b64_tr_b16 %9, %16 offset:%26\n\t"
-      "ds_read_b64_tr_b16 %10, %16 offset:%27\n\tds_read_b64_tr_b16 %11, %16 offset:%28\n\t"
-      "ds_read_b64_tr_b16 %12, %16 offset:%29\n\tds_read_b64_tr_b16 %13, %16 offset:%30\n\t"
-      "ds_read_b64_tr_b16 %14, %16 offset:%31\n\tds_read_b64_tr_b16 %15, %16 offset:%32\n\t"
+      "ds_read_b64_tr_b16 %0, %16 offset:%20\n\tds_read_b64_tr_b16 %1, %17 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %2, %18 offset:%20\n\tds_read_b64_tr_b16 %3, %19 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:%21\n\tds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:%21\n\tds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%22\n\tds_read_b64_tr_b16 %9, %17 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:%22\n\tds_read_b64_tr_b16 %11, %19 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:%23\n\tds_read_b64_tr_b16 %13, %17 offset:%23\n\t"
+      "ds_read_b64_tr_b16 %14, %18 offset:%23\n\tds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3]), "=v"(r[4]), "=v"(r[5]), "=v"(r[6]), "=v"(r[7]),
-        "=v"(r[8]), "=v"(r[9]), "=v"(r[10]), "=v"(r[11]), "=v"(r[12]), "=v"(r[13]), "=v"(r[14]), "=v"(r[15])
-      : "v"(p), MLA_O4(OFF, 512), MLA_O4(OFF + 2048, 512), MLA_O4(OFF + 4096, 512), MLA_O4(OFF + 6144, 512)
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), MLA_O4(B, 2048)
       : "memory");
 }
 
-// NB = 16-row groups of query rows each wave carries (R = 16 * NB * row groups).
-template <int NB, bool OUT_F32>
+// Split-decode kernel: 16 query rows per work-group (R = 16 * row groups).
+template <bool OUT_F32>
 __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
@@ -178,16 +198,20 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     worker = (y / a.row_groups) * 8 + x;
   }
   if (worker >= a.num_workers) return;
-  const int row0 = rgroup * 16 * NB;
+  const int row0 = rgroup * 16;
   const int R = a.rows;
 
-  // LDS block layout (16-B units): position = chunk*16 + (token ^ ((chunk & 1) << 2)),
-  // chunk = 16-B column chunk 0..71, token 0..15.  K-operand reads are then 1 KB
-  // contiguous and the V^T transpose reads touch all banks once per 16 lanes.
-  const int k_lane = (g * 16 + (n ^ ((g & 1) * kSwz))) * 16;
+  // Row-major block layout (see row_swz).  K reads: token n, chunk 4*kk + g; V^T reads:
+  // token 4g + e, 8-byte piece qq of a 16-column block; DMA instruction j: token
+  // 8*(j & 1) + (lane >> 3), chunk 8*(j >> 1) + ((lane & 7) ^ row_swz(token)).
+  const int k_even = 128 * n + 16 * (g ^ row_swz(n));
+  const int k_odd = k_even ^ 64;                               // chunk 4 + g: unit index bit 2 flips
   const int e = n >> 2, qq = n & 3;
-  const int v_lane = ((qq >> 1) * 16 + ((4 * g + e) ^ ((qq >> 1) * kSwz))) * 16 + (qq & 1) * 8;
-  const int ld_token = n ^ ((g & 1) * kSwz);  // token this lane fetches for chunk 4*j + g
+  int v_base[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v_base[i] = 128 * (4 * g + e) + 16 * ((2 * i + (qq >> 1)) ^ row_swz(4 * g + e)) + 8 * (qq & 1);
+  const int ld_tok0 = lane >> 3, ld_tok1 = 8 + (lane >> 3);
+  const int ld_col0 = 8 * ((lane & 7) ^ row_swz(ld_tok0)), ld_col1 = 8 * ((lane & 7) ^ row_swz(ld_tok1));
 
   LDS_AS uint8_t* stage0 = lds + (wave * kStages + 0) * kBlockBytes;
   LDS_AS uint8_t* stage1 = lds + (wave * kStages + 1) * kBlockBytes;
@@ -206,169 +230,117 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
     // end of the tokens this lane's query row sees: te, or for a causal problem the
     // first L - (q_len - 1 - i) tokens of the sequence (row = i * num_heads + h)
-    int lim[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int qi = (row0 + 16 * nb + n) / a.num_heads;
-      lim[nb] = a.causal ? min(te, seqlens[b] - (a.q_len - 1 - qi)) : te;
-    }
-#if MLA_CONTIG_BLOCKS
-    const int blk_first = (wave * nblk) / kWaves;
-    const int my_n = ((wave + 1) * nblk) / kWaves - blk_first;
-    auto blk_of = [&](int k) { return blk_first + k; };
-#else
+    const int lim = a.causal ? min(te, seqlens[b] - (a.q_len - 1 - (row0 + n) / a.num_heads)) : te;
+    // wave w takes blocks w, w + 4, w + 8, ... of the piece
     const int my_n = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
     auto blk_of = [&](int k) { return wave + kWaves * k; };
-#endif
 
-    // query rows as MFMA B operands (Q^T): lane (n, g) holds row 16*nb + n, columns 32*kk + 8*g .. +8
-    bf16x8_t qf[NB][kKSteps];
+    // query rows as MFMA B operands (Q^T): lane (n, g) holds row n, columns 32*kk + 8*g .. +8
+    bf16x8_t qf[kKSteps];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)b * R + row0 + n) * kDqk + 8 * g;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint16_t* qrow = a.q + ((int64_t)b * R + row0 + 16 * nb + n) * kDqk + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) qf[nb][kk] = *(const bf16x8_t*)(qrow + 32 * kk);
+      for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
     }
 
-    float m_ref[NB];         // reference max (log2 units) the p values are taken against
-    float lsum[NB];          // this lane's share of sum_t p_t (tokens 4g..4g+3 of each block)
-    f32x4_t o[NB][kVBlocks]; // O^T: lane (n, g) holds dims 16*mb + 4*g + i of row 16*nb + n
+    float m_ref = kNegBig;   // reference max (log2 units) the p values are taken against
+    float lsum = 0.f;        // this lane's share of sum_t p_t (tokens 4g..4g+3 of each block)
+    f32x4_t o[kVBlocks];     // O^T: lane (n, g) holds dims 16*mb + 4*g + i of row n
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      m_ref[nb] = kNegBig;
-      lsum[nb] = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < kVBlocks; ++mb) o[nb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int mb = 0; mb < kVBlocks; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Source row of this lane for the DMA of the wave's k-th block; `ok` is false for an
-    // out-of-range table entry (then page 0 is read, in bounds, and the block is skipped).
-    auto source = [&](int k, bool& ok) -> const uint16_t* {
+    // This lane's DMA sources for the wave's k-th block (even / odd instructions); `ok` is
+    // false for an out-of-range table entry (then page 0 is read, in bounds, and the block
+    // is skipped).  Rows past the end of the piece re-read its last valid row.
+    struct Src {
+      const uint16_t* p[2];
+    };
+    auto source = [&](int k, bool& ok) -> Src {
       const int tok0 = tb + kBlock * blk_of(k);
       int64_t base = kv_row_of(block_table, a.bt_stride, a.page_size, a.num_pages, b, tok0);
       ok = base >= 0;
       if (!ok) base = 0;
-      const int t = min(ld_token, te - 1 - tok0);   // rows past the end re-read the last valid row
-      return a.kv + (base + t) * kDqk + 8 * g;
+      const int last = te - 1 - tok0;
+      Src r;
+      r.p[0] = a.kv + (base + min(ld_tok0, last)) * kDqk + ld_col0;
+      r.p[1] = a.kv + (base + min(ld_tok1, last)) * kDqk + ld_col1;
+      return r;
     };
-    // DMA loads j0..j1-1 (1 KB each: 16-B column chunks 4j..4j+3 of the 16 rows) into a stage
-    auto issue = [&](const uint16_t* src, LDS_AS uint8_t* stage, int j0, int j1) {
+    // the 18 DMA loads of a block (1 KB each: 128 B of 8 rows, chunk block j/2) into a stage
+    auto issue = [&](const Src& src, LDS_AS uint8_t* stage) {
 #pragma unroll
-      for (int j = j0; j < j1; ++j)
-        __builtin_amdgcn_global_load_lds((GLB_AS void*)(src + 32 * j), (LDS_AS void*)(stage + 1024 * j), 16, 0, 0);
+      for (int j = 0; j < kLoadsPerBlock; ++j)
+        __builtin_amdgcn_global_load_lds((GLB_AS void*)(src.p[j & 1] + 64 * (j >> 1)),
+                                         (LDS_AS void*)(stage + 1024 * j), 16, 0, 0);
     };
-    // O^T += V^T P^T for the 32-column slab starting at column 16*MB0 (VB transpose reads)
-    auto pv_part = [&](const u32x2_t* vf, int mb0, int cnt, const i16x4_t (&ph)[NB], const i16x4_t (&pl)[NB]) {
+    // Every LDS read of a block first (K for S^T, then all of V^T into registers); then the
+    // stage is refilled with the block after next (`ns`, if `nx`) while S^T, the softmax
+    // and O^T += V^T P^T are still being computed.
+    auto scores = [&](LDS_AS uint8_t* st, f32x4_t& sacc, u32x2_t (&vf0)[16], u32x2_t (&vf1)[16], const Src& ns,
+                      bool nx) {
+      f32x4_t acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      auto mma = [&](const u32x4_t* kf, int kk0) {
 #pragma unroll
-      for (int i = 0; i < cnt; ++i) {
-        const i16x4_t v = __builtin_bit_cast(i16x4_t, vf[i]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          o[nb][mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, ph[nb], o[nb][mb0 + i], 0, 0, 0);
-          o[nb][mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pl[nb], o[nb][mb0 + i], 0, 0, 0);
+        for (int i = 0; i < 9; ++i) {
+          f32x4_t& acc = ((kk0 + i) & 1) ? acc2 : sacc;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[i]), qf[kk0 + i], acc, 0, 0, 0);
         }
-      }
+      };
+      u32x4_t kf[9];
+      lds_read_k9<0>(kf, st + k_even, st + k_odd);
+      mma(kf, 0);
+      lds_read_k9<9>(kf, st + k_even, st + k_odd);
+      LDS_AS const uint8_t* const vp[4] = {st + v_base[0], st + v_base[1], st + v_base[2], st + v_base[3]};
+      lds_read_v16<0>(vf0, vp);                // columns 0..255
+      lds_read_v16<1>(vf1, vp);                // columns 256..511
+      if (nx) issue(ns, st);
+      mma(kf, 9);
+      sacc += acc2;
     };
     // O^T += V^T P^T for one block, p = exp2(s - m_ref).  p is split into two bf16
     // terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)), and both go through the
     // MFMA, so the weights carry ~16 mantissa bits instead of bf16's 8; the running
-    // sum l takes p in fp32.  As each part of V^T has been read, the matching part of
-    // the stage is refilled with the block after next (`nsrc`, if any).
-    auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[NB][4], const uint16_t* nsrc) {
-      i16x4_t ph[NB], pl[NB];
+    // sum l takes p in fp32.
+    auto accumulate = [&](const float (&s)[4], const u32x2_t (&vf0)[16], const u32x2_t (&vf1)[16]) {
+      uint32_t hb[4], lb[4];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        uint32_t hb[4], lb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[nb][i] - m_ref[nb]);
-          hb[i] = bf16_rne(p);
-          lb[i] = bf16_rne(p - bf16_bits_to_float(hb[i]));
-          lsum[nb] += p;
-        }
-        ph[nb] = i16x4_t{(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
-        pl[nb] = i16x4_t{(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[i] - m_ref);
+        hb[i] = bf16_rne(p);
+        lb[i] = bf16_rne(p - bf16_bits_to_float(hb[i]));
+        lsum += p;
       }
-      LDS_AS const uint8_t* vp = st + v_lane;
-      if constexpr (NB == 1) {
-        u32x2_t vf[16];
-        lds_read_tr16<0>(vf, vp);                // columns 0..255 = stage bytes [0, 8 KB)
-        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 0, 8);
-        pv_part(vf, 0, 16, ph, pl);
-        lds_read_tr16<8192>(vf, vp);             // columns 256..511 = stage bytes [8 KB, 16 KB)
-        if (nsrc) issue(nsrc, st, MLA_PROGRESSIVE_REFILL ? 8 : 0, MLA_PROGRESSIVE_REFILL ? 16 : kLoadsPerBlock);
-        pv_part(vf, 16, 16, ph, pl);
-      } else {
-        u32x2_t vf[8];
-        lds_read_tr8<0>(vf, vp);                 // columns 128*i .. +127 = stage bytes [4i KB, 4i+4 KB)
-        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 0, 4);
-        pv_part(vf, 0, 8, ph, pl);
-        lds_read_tr8<4096>(vf, vp);
-        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 4, 8);
-        pv_part(vf, 8, 8, ph, pl);
-        lds_read_tr8<8192>(vf, vp);
-        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 8, 12);
-        pv_part(vf, 16, 8, ph, pl);
-        lds_read_tr8<12288>(vf, vp);
-        if (nsrc) issue(nsrc, st, MLA_PROGRESSIVE_REFILL ? 12 : 0, MLA_PROGRESSIVE_REFILL ? 16 : kLoadsPerBlock);
-        pv_part(vf, 24, 8, ph, pl);
-      }
-    };
-    // S^T = K Q^T for one block: 16 tokens x 16*NB rows; lane holds tokens 4g..4g+3 of each row
-    auto scores = [&](LDS_AS uint8_t* st, f32x4_t (&sacc)[NB], const uint16_t* nsrc) {
-      LDS_AS const uint8_t* kp = st + k_lane;
-      f32x4_t acc2[NB];
+      const i16x4_t ph = i16x4_t{(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
+      const i16x4_t pl = i16x4_t{(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
+      auto pv = [&](const u32x2_t (&vf)[16], int mb0) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        sacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        acc2[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-      auto mma = [&](const u32x4_t* kf, int kk0, int cnt) {
-#pragma unroll
-        for (int i = 0; i < cnt; ++i) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            f32x4_t& acc = ((kk0 + i) & 1) ? acc2[nb] : sacc[nb];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[i]), qf[nb][kk0 + i], acc,
-                                                          0, 0, 0);
-          }
+        for (int i = 0; i < 16; ++i) {
+          const i16x4_t v = __builtin_bit_cast(i16x4_t, vf[i]);
+          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, ph, o[mb0 + i], 0, 0, 0);
+          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pl, o[mb0 + i], 0, 0, 0);
         }
       };
-      if constexpr (NB == 1) {
-        u32x4_t kf[9];
-        lds_read_b128x9<0>(kf, kp);
-        mma(kf, 0, 9);
-        lds_read_b128x9<9216>(kf, kp);
-        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 16, kLoadsPerBlock);   // rope: bytes [16 KB, 18 KB)
-        mma(kf, 9, 9);
-      } else {
-        u32x4_t kf[6];
-        lds_read_b128x6<0>(kf, kp);
-        mma(kf, 0, 6);
-        lds_read_b128x6<6144>(kf, kp);
-        mma(kf, 6, 6);
-        lds_read_b128x6<12288>(kf, kp);
-        if (MLA_PROGRESSIVE_REFILL && nsrc) issue(nsrc, st, 16, kLoadsPerBlock);
-        mma(kf, 12, 6);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sacc[nb] += acc2[nb];
+      pv(vf0, 0);
+      pv(vf1, 16);
     };
 
     bool ok0 = true, ok1 = true;   // table entry of the block now in each stage was in range
-    if (my_n > 0) issue(source(0, ok0), stage0, 0, kLoadsPerBlock);
-    if (my_n > 1) issue(source(1, ok1), stage1, 0, kLoadsPerBlock);
+    if (my_n > 0) issue(source(0, ok0), stage0);
+    if (my_n > 1) issue(source(1, ok1), stage1);
 
     int k = 0;
     while (k < my_n) {
-      float s[NB][4], mx[NB];
+      float s[4], mx = 0.f;
       bool rescale = false;
-      const uint16_t* nsrc = nullptr;
+      u32x2_t vf0[16], vf1[16];
       // hot loop: o is only touched by MFMA here
       for (; k < my_n; ++k) {
         LDS_AS uint8_t* st = (k & 1) ? stage1 : stage0;
         bool nok = true;
-        nsrc = (k + 2 < my_n) ? source(k + 2, nok) : nullptr;
+        const bool nx = k + 2 < my_n;
+        Src nsrc{};
+        if (nx) nsrc = source(k + 2, nok);
         if (k + 1 < my_n) {
           asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
         } else {
@@ -378,61 +350,51 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         if (k & 1) ok1 = nok; else ok0 = nok;   // the stage's next occupant
         if (!ok) {
           if (lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (nsrc) issue(nsrc, st, 0, kLoadsPerBlock);
+          if (nx) issue(nsrc, st);
           continue;
         }
         const int tok0 = tb + kBlock * blk_of(k);
-        f32x4_t sacc[NB];
-        scores(st, sacc, nsrc);
-        bool grow = false;
+        f32x4_t sacc;
+        scores(st, sacc, vf0, vf1, nsrc, nx);
+        const int nvalid = lim - tok0;   // tokens of the block this row sees (may be <= 0)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int nvalid = lim[nb] - tok0;   // tokens of the block this row sees (may be <= 0)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s[nb][i] = (4 * g + i < nvalid) ? sacc[nb][i] * a.scale_log2 : -INFINITY;
-          mx[nb] = wave_max_over_groups(fmaxf(fmaxf(s[nb][0], s[nb][1]), fmaxf(s[nb][2], s[nb][3])));
-          grow |= mx[nb] > m_ref[nb] + kRescaleSlack;
-        }
-        if (__any(grow)) {
+        for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
+        mx = wave_max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+        if (__any(mx > m_ref + kRescaleSlack)) {
           rescale = true;
           break;
         }
-        accumulate(st, s, nsrc);
+        accumulate(s, vf0, vf1);
       }
       if (!rescale) break;
       // rare path: a running max grew past the slack; move the reference and rescale
       {
-        LDS_AS uint8_t* st = (k & 1) ? stage1 : stage0;
+        const bool need = mx > m_ref + kRescaleSlack;
+        const float f = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
+        m_ref = need ? mx : m_ref;
+        lsum *= f;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const bool need = mx[nb] > m_ref[nb] + kRescaleSlack;
-          const float f = need ? __builtin_amdgcn_exp2f(m_ref[nb] - mx[nb]) : 1.0f;
-          m_ref[nb] = need ? mx[nb] : m_ref[nb];
-          lsum[nb] *= f;
-#pragma unroll
-          for (int mb = 0; mb < kVBlocks; ++mb) o[nb][mb] *= f;
-        }
-        accumulate(st, s, nsrc);
+        for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
+        accumulate(s, vf0, vf1);
         ++k;
       }
     }
 
-    // ---- merge the four waves' states and write, 16 rows at a time
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const float lrow = wave_sum_over_groups(lsum[nb]);
-      __syncthreads();   // stages (or the previous round's buffer) no longer read
+    // ---- merge the four waves' states and write
+    {
+      const float lrow = wave_sum_over_groups(lsum);
+      __syncthreads();   // stages no longer read
       LDS_AS float* buf = (LDS_AS float*)smem;                     // [4 waves][16 rows][516]
       LDS_AS float* sm_m = buf + kWaves * 16 * kMergeStride;       // [4][16]
       LDS_AS float* sm_l = sm_m + kWaves * 16;                     // [4][16]
       if (g == 0) {
-        sm_m[wave * 16 + n] = m_ref[nb];
+        sm_m[wave * 16 + n] = m_ref;
         sm_l[wave * 16 + n] = lrow;
       }
       {
         LDS_AS float* my = buf + (wave * 16 + n) * kMergeStride + 4 * g;
 #pragma unroll
-        for (int mb = 0; mb < kVBlocks; ++mb) *(LDS_AS f32x4_t*)(my + 16 * mb) = o[nb][mb];
+        for (int mb = 0; mb < kVBlocks; ++mb) *(LDS_AS f32x4_t*)(my + 16 * mb) = o[mb];
       }
       __syncthreads();
       const int r = threadIdx.x >> 4, dseg = threadIdx.x & 15;
@@ -449,7 +411,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         L += fw[w] * sm_l[w * 16 + r];
       }
       const float inv = L > 0.f ? 1.0f / L : 0.f;
-      const int grow = row0 + 16 * nb + r;
+      const int grow = row0 + r;
 #pragma unroll
       for (int j = 0; j < kDv / 64; ++j) {
         const int d = 4 * dseg + 64 * j;
@@ -838,9 +800,9 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
   hipStream_t s = (hipStream_t)stream;
   if (rows_per_group == 16) {
     if (out_fp32)
-      hipLaunchKernelGGL((split_decode_kernel<1, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split_decode_kernel<true>), dim3(grid), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((split_decode_kernel<1, false>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split_decode_kernel<false>), dim3(grid), dim3(kThreads), 0, s, a);
   } else if (rows_per_group == 32) {
     if (out_fp32)
       hipLaunchKernelGGL((group_decode_kernel<2, true>), dim3(grid), dim3(kThreads), 0, s, a);
