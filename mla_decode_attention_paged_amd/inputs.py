@@ -16,6 +16,18 @@ Draw order for one problem (fixed so that a seed names one input set):
   2. the page permutation,
   3. the cache values (page by page, in physical order),
   4. the query values.
+
+FP8 cache rows (``kv_format="fp8"``), 656 bytes per token:
+  bytes [0, 512)    latent columns 0..511 as OCP FP8 E4M3 codes,
+  bytes [512, 640)  rope columns 512..575 as bf16,
+  bytes [640, 656)  four float32 group scales, one per 128 latent columns; only
+                    the exponent counts (a column's value is its code's value times
+                    2^(biased exponent - 127) of its group's scale).
+The generator draws N(0,1) float32 latent values, picks per (row, group) the
+power of two 2^ceil(log2(max|x| / 448)) as the scale and lets torch round x /
+scale to E4M3 (an input encoding; the decode never encodes).  Rope columns are
+N(0,1) rounded to bf16.  Step 3 then draws all latent values (row chunks), then
+all rope values.
 """
 from __future__ import annotations
 
@@ -48,13 +60,17 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 BF16_NAN = np.uint16(0x7FC0)
+FP8_ROW_BYTES = 656         # 512 E4M3 latent + 64 bf16 rope + 4 float32 group scales
+FP8_NAN = np.uint8(0x7F)
+FP8_GROUP = 128             # latent columns per scale
+_ROW_CHUNK = 32768          # fp8 rows generated per RNG call
 
 
 @dataclass
 class Problem:
     """One decode call's inputs, host side."""
     q: np.ndarray              # [B, S_q, H, 576] uint16 (bf16 bits)
-    kv_cache: np.ndarray       # [num_pages, P, 576] uint16 (bf16 bits)
+    kv_cache: np.ndarray       # [num_pages, P, 576] uint16 (bf16 bits) or [num_pages, P, 656] uint8 (fp8 rows)
     block_table: np.ndarray    # [B, max_pages_per_seq] int32, -1 where unused
     cache_seqlens: np.ndarray  # [B] int32
     softmax_scale: float
@@ -84,6 +100,10 @@ class Problem:
     def max_pages_per_seq(self) -> int:
         return int(self.block_table.shape[1])
 
+    @property
+    def kv_format(self) -> str:
+        return "fp8" if self.kv_cache.dtype == np.uint8 else "bf16"
+
 
 def _normal_bf16(rng: np.random.Generator, n: int) -> np.ndarray:
     out = np.empty(n, dtype=np.uint16)
@@ -93,11 +113,30 @@ def _normal_bf16(rng: np.random.Generator, n: int) -> np.ndarray:
     return out
 
 
+def _fp8_rows(rng: np.random.Generator, n: int) -> np.ndarray:
+    """n cache rows in the fp8 layout (see the module docstring)."""
+    import torch
+    rows = np.empty((n, FP8_ROW_BYTES), dtype=np.uint8)
+    for s in range(0, n, _ROW_CHUNK):
+        e = min(n, s + _ROW_CHUNK)
+        x = rng.standard_normal((e - s, D_V), dtype=np.float32).reshape(e - s, D_V // FP8_GROUP, FP8_GROUP)
+        amax = np.maximum(np.abs(x).max(axis=2), np.float32(2.0 ** -100))
+        scale = np.exp2(np.ceil(np.log2(amax.astype(np.float64) / 448.0))).astype(np.float32)
+        codes = torch.from_numpy(np.ascontiguousarray(x / scale[:, :, None])).to(torch.float8_e4m3fn)
+        rows[s:e, :D_V] = codes.view(torch.uint8).numpy().reshape(e - s, D_V)
+        rows[s:e, 640:656] = scale.view(np.uint8).reshape(e - s, 16)
+    for s in range(0, n, _ROW_CHUNK):
+        e = min(n, s + _ROW_CHUNK)
+        rope = f32_to_bf16_bits(rng.standard_normal((e - s, D_QK - D_V), dtype=np.float32))
+        rows[s:e, D_V:640] = rope.view(np.uint8).reshape(e - s, 128)
+    return rows
+
+
 def make_problem(batch: int, q_len: int, num_heads: int, page_size: int,
                  lengths=None, *, seed: int = 0, ragged_range=None,
                  out_fp32: bool = False, tail: str = "normal",
                  extra_pages: int = 0, softmax_scale: float = SOFTMAX_SCALE,
-                 identity_pages: bool = False, name: str = "") -> Problem:
+                 identity_pages: bool = False, name: str = "", kv_format: str = "bf16") -> Problem:
     """Draw one paged decode problem.
 
     lengths        -- per-sequence context lengths (int or sequence); if None,
@@ -122,7 +161,12 @@ def make_problem(batch: int, q_len: int, num_heads: int, page_size: int,
     for b, n in enumerate(pages_per):
         block_table[b, :n] = perm[off:off + n]
         off += n
-    kv = _normal_bf16(rng, num_pages * page_size * D_QK).reshape(num_pages, page_size, D_QK)
+    if kv_format == "bf16":
+        kv = _normal_bf16(rng, num_pages * page_size * D_QK).reshape(num_pages, page_size, D_QK)
+    elif kv_format == "fp8":
+        kv = _fp8_rows(rng, num_pages * page_size).reshape(num_pages, page_size, FP8_ROW_BYTES)
+    else:
+        raise ValueError(f"unknown kv_format {kv_format!r}")
     q = _normal_bf16(rng, batch * q_len * num_heads * D_QK).reshape(batch, q_len, num_heads, D_QK)
     if tail == "nan":
         poison_unused(kv, block_table, lengths, page_size)
@@ -144,7 +188,12 @@ def poison_unused(kv: np.ndarray, block_table: np.ndarray, lengths: np.ndarray, 
         phys = block_table[b, t // page_size].astype(np.int64)
         mapped[phys * page_size + t % page_size] = True
     flat = kv.reshape(-1, kv.shape[-1])
-    flat[~mapped] = BF16_NAN
+    if kv.dtype == np.uint8:                      # fp8 rows: NaN codes and NaN rope
+        flat[~mapped, :D_V] = FP8_NAN
+        nan_rope = np.full(D_QK - D_V, BF16_NAN, dtype=np.uint16).view(np.uint8)
+        flat[~mapped, D_V:640] = nan_rope
+    else:
+        flat[~mapped] = BF16_NAN
 
 
 # The five measured workloads.  Index 0 is the small one the oracle finishes in

@@ -26,6 +26,14 @@ What is computed (plain definitions, written out; every float op in float64):
   equals the LSE-weighted sum of the per-range results; ``combine`` states that
   identity directly.
 
+* FP8 latent cache (a cache format the pages name for FlashMLA without fixing
+  it; the layout is this library's): each token row is 656 bytes -- 512 OCP
+  FP8 E4M3 codes for the latent columns, 64 bf16 rope columns, and four float32
+  group scales of which only the exponent counts.  ``widen_fp8_rows`` decodes a
+  row from the E4M3 definition (sign, 4-bit exponent with bias 7, 3-bit mantissa,
+  subnormals at exponent 0, S.1111.111 is NaN, no infinities) and multiplies
+  latent column c by 2^(E - 127), E the biased exponent of scale c // 128.
+
 Readings where the pages are silent (each is listed in the design notes):
   - lse is the natural log of sum_t exp(s_t) with s_t = scale * q . k_t;
   - an empty context (L = 0) gives out = 0 and lse = -inf;
@@ -47,6 +55,39 @@ def widen_bf16(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of float32)."""
     b = np.asarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+FP8_ROW_BYTES = 656
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64, exactly."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def widen_fp8_rows(rows: np.ndarray) -> np.ndarray:
+    """fp8 cache rows [L, 656] uint8 -> float64 [L, 576] (latent decoded and scaled, rope widened)."""
+    r = np.asarray(rows, dtype=np.uint8)
+    L = r.shape[0]
+    latent = decode_e4m3(r[:, :D_V])
+    scale_bits = np.ascontiguousarray(r[:, 640:656]).view(np.uint32).reshape(L, 4)
+    factor = np.exp2(((scale_bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.float64) - 127.0)
+    latent = latent * np.repeat(factor, D_V // 4, axis=1)
+    rope = widen_bf16(np.ascontiguousarray(r[:, D_V:640]).view(np.uint16).reshape(L, D_QK - D_V))
+    return np.concatenate([latent, rope], axis=1)
+
+
+def widen_rows(rows: np.ndarray) -> np.ndarray:
+    """Cache rows as stored (bf16 [L, 576] uint16 or fp8 [L, 656] uint8) -> float64 [L, 576]."""
+    if np.asarray(rows).dtype == np.uint8:
+        return widen_fp8_rows(rows)
+    return widen_bf16(rows)
 
 
 def gather_sequence(kv_cache: np.ndarray, block_table_row: np.ndarray, length: int,
@@ -86,7 +127,7 @@ def decode_sequence(q_b: np.ndarray, kv_cache: np.ndarray, block_table_row: np.n
     """One sequence: q_b [S_q, H, 576] bits -> (out [S_q, H, 512], lse [S_q, H]) float64."""
     s_q, h = q_b.shape[0], q_b.shape[1]
     rows = gather_sequence(kv_cache, block_table_row, length, page_size)
-    k = widen_bf16(rows)
+    k = widen_rows(rows)
     if not causal:
         q = widen_bf16(q_b).reshape(s_q * h, D_QK)
         out, lse = attend(q, k, k[:, :D_V], softmax_scale)
@@ -104,7 +145,8 @@ def decode(q: np.ndarray, kv_cache: np.ndarray, block_table: np.ndarray,
            batch_indices=None, causal: bool = False):
     """Paged MLA decode for every (or the listed) sequence.
 
-    q [B, S_q, H, 576] bf16 bits; kv_cache [num_pages, page_size, 576] bf16 bits;
+    q [B, S_q, H, 576] bf16 bits; kv_cache [num_pages, page_size, 576] bf16 bits or
+    [num_pages, page_size, 656] uint8 fp8 rows;
     block_table [B, max_pages] int32; cache_seqlens [B] int32.
     Returns out [B, S_q, H, 512] and lse [B, S_q, H] in float64 (rows of
     sequences not listed in ``batch_indices`` are left NaN).

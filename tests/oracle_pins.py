@@ -21,6 +21,12 @@ Pins:
   sdpa_special_case     -- one contiguous page == torch SDPA in float64 on CPU.
   split_combine         -- results over disjoint token ranges merged by the
                            log-sum-exp rule equal the unsplit result.
+  causal_*              -- the causal mask between query tokens (see below).
+  fp8_*                 -- the FP8 cache rows: the E4M3 decoder against the
+                           format's definition and torch's float8_e4m3fn, the
+                           exponent-only group scales, a decimal brute force on
+                           fp8 rows, and fp8 rows against a bf16 cache holding
+                           the same values.
 """
 from __future__ import annotations
 
@@ -53,6 +59,38 @@ def _bf16_to_decimal(bits: int) -> Decimal:
         return sign * v
 
 
+def _e4m3_to_decimal(code: int) -> Decimal:
+    """Decode an OCP E4M3 byte by its fields (sign, 4-bit exponent bias 7, 3-bit mantissa)."""
+    code = int(code)
+    if code & 0x7F == 0x7F:
+        raise ValueError("NaN E4M3 code in decimal brute force")
+    sign = -1 if code >> 7 else 1
+    exp = (code >> 3) & 0xF
+    man = code & 7
+    with localcontext() as ctx:
+        ctx.prec = 60
+        if exp == 0:
+            v = Decimal(man) * (Decimal(2) ** -9)
+        else:
+            v = (Decimal(8 + man) / Decimal(8)) * (Decimal(2) ** (exp - 7))
+        return sign * v
+
+
+def _decimal_row(row) -> list:
+    """One cache row as 576 Decimals: bf16 [576] uint16, or an fp8 row [656] uint8."""
+    row = np.asarray(row)
+    if row.dtype != np.uint8:
+        return [_bf16_to_decimal(x) for x in row.tolist()]
+    b = [int(x) for x in row.tolist()]
+    factors = []
+    for g in range(4):
+        word = b[640 + 4 * g] | (b[641 + 4 * g] << 8) | (b[642 + 4 * g] << 16) | (b[643 + 4 * g] << 24)
+        factors.append(Decimal(2) ** (((word >> 23) & 0xFF) - 127))
+    latent = [_e4m3_to_decimal(b[c]) * factors[c // 128] for c in range(512)]
+    rope = [_bf16_to_decimal(b[512 + 2 * j] | (b[513 + 2 * j] << 8)) for j in range(64)]
+    return latent + rope
+
+
 def decimal_decode(q, kv, block_table, seqlens, scale, page_size, rows=None, causal=False):
     """Brute-force paged MLA decode at 40 significant digits. Returns nested lists.
     causal: query token i of S_q sees tokens t <= L - S_q + i."""
@@ -66,7 +104,7 @@ def decimal_decode(q, kv, block_table, seqlens, scale, page_size, rows=None, cau
             keys = []
             for t in range(L):
                 page = int(block_table[b][t // page_size])
-                keys.append([_bf16_to_decimal(x) for x in kv[page][t % page_size].tolist()])
+                keys.append(_decimal_row(kv[page][t % page_size]))
             for i in range(S):
                 for h in range(H):
                     if rows is not None and (b, i, h) not in rows:
@@ -297,3 +335,79 @@ def causal_decomposition(decode_fn):
 
 ALL_DECODE_PINS = [decimal_brute_force, single_token, equal_scores, shift_invariance, page_permutation,
                    decomposition, sdpa_special_case, causal_decimal, causal_decomposition]
+
+
+# ----------------------------------------------------------------------------- fp8 cache rows
+def fp8_decoder_spec_values(decode_e4m3):
+    """E4M3 values fixed by the format: zero, signed zero, the smallest subnormal, the
+    largest subnormal, the smallest normal, one, the largest finite value, NaN."""
+    codes = np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0xB8, 0x7E, 0xFE, 0x7F, 0xFF, 0x3F], dtype=np.uint8)
+    want = [0.0, -0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, -1.0, 448.0, -448.0, np.nan, np.nan, 1.875]
+    got = decode_e4m3(codes)
+    for c, g, w in zip(codes, got, want):
+        if np.isnan(w):
+            assert np.isnan(g), f"code {c:#x}: {g} is not NaN"
+        else:
+            assert g == w and np.signbit(g) == np.signbit(w), f"code {c:#x}: {g} != {w}"
+
+
+def fp8_decoder_matches_torch(decode_e4m3):
+    """All 256 codes against torch's float8_e4m3fn (a library that implements the same format)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    got = decode_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(ref)], ref[~np.isnan(ref)])
+
+
+def _fp8_row(latent_codes, rope_bits, scales):
+    row = np.zeros(656, dtype=np.uint8)
+    row[:512] = latent_codes
+    row[512:640] = np.asarray(rope_bits, dtype=np.uint16).view(np.uint8)
+    row[640:656] = np.asarray(scales, dtype=np.float32).view(np.uint8)
+    return row
+
+
+def fp8_scale_exponent_only(widen_fp8_rows):
+    """A group scale counts only through its exponent: 1.5 acts as 1, 0.3 as 0.25, 96 as 64.
+    Group g covers latent columns [128g, 128g + 128); rope columns are never scaled."""
+    codes = np.full(512, 0x38, dtype=np.uint8)           # every latent value 1.0
+    rope = gen.f32_to_bf16_bits(np.linspace(-2, 2, 64).astype(np.float32))
+    w = widen_fp8_rows(_fp8_row(codes, rope, [1.5, 0.3, 96.0, 2.0 ** -20])[None])[0]
+    for g, f in enumerate([1.0, 0.25, 64.0, 2.0 ** -20]):
+        assert np.all(w[128 * g:128 * (g + 1)] == f), f"group {g}"
+    assert np.array_equal(w[512:], gen.bf16_bits_to_f32(rope).astype(np.float64))
+
+
+def fp8_decimal_brute_force(decode_fn):
+    cases = [dict(batch=2, q_len=1, num_heads=2, page_size=16, lengths=[1, 19], seed=41, kv_format="fp8"),
+             dict(batch=1, q_len=2, num_heads=2, page_size=16, lengths=[6], seed=42, kv_format="fp8")]
+    for c in cases:
+        p = gen.make_problem(**c)
+        out, lse = decode_fn(p.q, p.kv_cache, p.block_table, p.cache_seqlens, p.softmax_scale, p.page_size)
+        ref = decimal_decode(p.q, p.kv_cache, p.block_table, p.cache_seqlens, p.softmax_scale, p.page_size)
+        for (b, i, h), (o_ref, l_ref) in ref.items():
+            eo = float(np.max(np.abs(np.asarray(out[b, i, h]) - np.asarray(o_ref))))
+            el = abs(float(lse[b, i, h]) - l_ref)
+            assert eo <= TOL and el <= TOL, f"fp8 decimal brute force: {c} row {(b, i, h)}: {eo} {el}"
+
+
+def fp8_matches_bf16_cache(decode_fn):
+    """fp8 rows whose values are exact in bf16 (they all are: 4 significant bits times a power
+    of two) give the same result as a bf16 cache that stores those values."""
+    p = gen.make_problem(batch=3, q_len=2, num_heads=16, page_size=16, lengths=[33, 1, 70], seed=43,
+                         kv_format="fp8")
+    rows = p.kv_cache.reshape(-1, 656)
+    bf = np.empty((rows.shape[0], D_QK), dtype=np.uint16)
+    for r in range(rows.shape[0]):
+        bf[r] = [int(x) for x in (np.array([float(v) for v in _decimal_row(rows[r])], dtype=np.float32)
+                                  .view(np.uint32) >> 16)]
+    kv_bf = bf.reshape(p.kv_cache.shape[0], p.kv_cache.shape[1], D_QK)
+    o8, l8 = decode_fn(p.q, p.kv_cache, p.block_table, p.cache_seqlens, p.softmax_scale, p.page_size)
+    ob, lb = decode_fn(p.q, kv_bf, p.block_table, p.cache_seqlens, p.softmax_scale, p.page_size)
+    assert np.max(np.abs(o8 - ob)) <= TOL and np.max(np.abs(l8 - lb)) <= TOL
+
+
+FP8_DECODE_PINS = [fp8_decimal_brute_force, fp8_matches_bf16_cache]
+ALL_DECODE_PINS = ALL_DECODE_PINS + FP8_DECODE_PINS

@@ -158,3 +158,35 @@ def test_pin_causal_decimal():
 
 def test_pin_causal_decomposition():
     pins.causal_decomposition(orc.decode)
+
+
+def test_pin_fp8_decoder_spec_values():
+    pins.fp8_decoder_spec_values(orc.decode_e4m3)
+
+
+def test_pin_fp8_decoder_matches_torch():
+    pins.fp8_decoder_matches_torch(orc.decode_e4m3)
+
+
+def test_pin_fp8_scale_exponent_only():
+    pins.fp8_scale_exponent_only(orc.widen_fp8_rows)
+
+
+def test_pin_fp8_decimal_brute_force():
+    pins.fp8_decimal_brute_force(orc.decode)
+
+
+def test_pin_fp8_matches_bf16_cache():
+    pins.fp8_matches_bf16_cache(orc.decode)
+
+
+def test_fp8_generator_rows_are_valid():
+    """The generated fp8 rows: finite codes, power-of-two scales, N(0,1)-like latent values."""
+    p = gen.make_problem(batch=2, q_len=1, num_heads=16, page_size=64, lengths=[100, 64], seed=44,
+                         kv_format="fp8")
+    rows = p.kv_cache.reshape(-1, 656)
+    assert not np.any((rows[:, :512] & 0x7F) == 0x7F)
+    sc = np.ascontiguousarray(rows[:, 640:656]).view(np.float32)
+    assert np.all(sc == np.exp2(np.round(np.log2(sc))))
+    w = orc.widen_fp8_rows(rows)
+    assert 0.8 < np.std(w[:, :512]) < 1.2 and 0.8 < np.std(w[:, 512:]) < 1.2

@@ -97,6 +97,45 @@ def _combine_variant(kind):
     return combine
 
 
+def _e4m3_variant(kind):
+    def decode_e4m3(codes):
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        sign = np.where(c >> 7, -1.0, 1.0)
+        e = (c >> 3) & 15
+        m = (c & 7).astype(np.float64)
+        bias = 8 if kind == "bias8" else 7
+        normal = (1.0 + m / 8.0) * np.exp2((e - bias).astype(np.float64))
+        sub = normal if kind == "no_subnormals" else m * 2.0 ** -9
+        out = sign * np.where(e == 0, sub, normal)
+        if kind == "no_nan":
+            return out
+        return np.where((c & 0x7F) == 0x7F, np.nan, out)
+    return decode_e4m3
+
+
+def _widen_fp8_variant(kind):
+    def widen_fp8_rows(rows):
+        r = np.asarray(rows, dtype=np.uint8)
+        L = r.shape[0]
+        latent = orc.decode_e4m3(r[:, :512])
+        sc = np.ascontiguousarray(r[:, 640:656]).view(np.float32).reshape(L, 4).astype(np.float64)
+        if kind == "full_scale":
+            factor = sc
+        else:
+            factor = np.exp2(np.floor(np.log2(sc)))
+        if kind == "no_scale":
+            factor = np.ones_like(factor)
+        if kind == "interleaved_groups":
+            latent = latent * np.tile(factor, (1, 128))
+        else:
+            latent = latent * np.repeat(factor, 128, axis=1)
+        start = 514 if kind == "rope_offset" else 512
+        rope_bytes = np.ascontiguousarray(r[:, start:start + 128])
+        rope = orc.widen_bf16(rope_bytes.view(np.uint16).reshape(L, 64))
+        return np.concatenate([latent, rope], axis=1)
+    return widen_fp8_rows
+
+
 MUTANTS = {
     "no_scale": ("attend", _attend_variant("no_scale")),
     "scale_twice": ("attend", _attend_variant("scale_twice")),
@@ -112,6 +151,13 @@ MUTANTS = {
     "causal_off_by_one": ("decode_sequence", _decode_sequence_variant("causal_off_by_one")),
     "causal_reversed": ("decode_sequence", _decode_sequence_variant("causal_reversed")),
     "causal_ignored": ("decode_sequence", _decode_sequence_variant("causal_ignored")),
+    "e4m3_bias8": ("decode_e4m3", _e4m3_variant("bias8")),
+    "e4m3_no_subnormals": ("decode_e4m3", _e4m3_variant("no_subnormals")),
+    "e4m3_no_nan": ("decode_e4m3", _e4m3_variant("no_nan")),
+    "fp8_full_scale": ("widen_fp8_rows", _widen_fp8_variant("full_scale")),
+    "fp8_no_scale": ("widen_fp8_rows", _widen_fp8_variant("no_scale")),
+    "fp8_interleaved_groups": ("widen_fp8_rows", _widen_fp8_variant("interleaved_groups")),
+    "fp8_rope_offset": ("widen_fp8_rows", _widen_fp8_variant("rope_offset")),
     "combine_sign": ("combine", _combine_variant("sign")),
     "combine_unnormalised": ("combine", _combine_variant("unnormalised")),
 }
@@ -135,8 +181,15 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
             if _caught(lambda: pins.split_combine(orc.attend, orc.combine)):
                 caught.append("split_combine")
         else:
+            if attr == "decode_e4m3":
+                for pin in (pins.fp8_decoder_spec_values, pins.fp8_decoder_matches_torch):
+                    if _caught(lambda: pin(orc.decode_e4m3)):
+                        caught.append(pin.__name__)
+            if attr == "widen_fp8_rows" and _caught(lambda: pins.fp8_scale_exponent_only(orc.widen_fp8_rows)):
+                caught.append("fp8_scale_exponent_only")
             for pin in pins.ALL_DECODE_PINS:
+                if caught:
+                    break
                 if _caught(lambda: pin(orc.decode)):
                     caught.append(pin.__name__)
-                    break
     assert caught, f"planted mistake {name!r} passed every pin"
