@@ -45,8 +45,9 @@ def algorithmic_bytes(prob) -> int:
     L = prob.cache_seqlens.astype(np.int64)
     R = prob.q_len * prob.num_heads
     out_elem = 4 if prob.out_fp32 else 2
+    row_bytes = 656 if prob.kv_format == "fp8" else 576 * 2
     pages = ((L + prob.page_size - 1) // prob.page_size).sum()
-    return int(L.sum() * 576 * 2 + prob.batch * R * 576 * 2 + prob.batch * R * 512 * out_elem
+    return int(L.sum() * row_bytes + prob.batch * R * 576 * 2 + prob.batch * R * 512 * out_elem
                + prob.batch * R * 4 + pages * 4)
 
 
@@ -106,6 +107,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="cache row storage: bf16 (1,152 B per token) or fp8 E4M3 rows (656 B per token)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -121,8 +124,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()  # fail loudly if the HIP library is missing
     print(f"[bench] generating {args.config} inputs", file=sys.stderr, flush=True)
-    prob = gen.make_config(args.config, seed=args.seed)
+    prob = gen.make_config(args.config, seed=args.seed, kv_format=args.kv)
     algo = algorithmic_bytes(prob)
+    counters_key = args.config if args.kv == "bf16" else f"{args.config}_{args.kv}"
 
     t0 = time.perf_counter()
     plan_probe = B.Plan(__import__("mla_decode_attention_paged_amd.device", fromlist=["x"]).problem_struct(prob),
@@ -179,7 +183,7 @@ def main():
     status = B.mla_read_status(r.ws)
     value = algo / wall / 1e9
     achieved = algo / (split_us * 1e-6) / 1e9
-    traffic = measured_traffic(args.config)
+    traffic = measured_traffic(counters_key)
     result = {
         "metric": "µs/call and achieved HBM GB/s (% of peak), MLA decode bs=16 H=16 ctx=64K",
         "value": round(value, 2),
@@ -195,7 +199,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "batch": prob.batch,
+        "config": {"workload": WORKLOAD_TEXT[args.config] + ("" if args.kv == "bf16" else
+                                                             ", FP8 E4M3 cache rows (656 B per token)"),
+                   "name": args.config, "kv": args.kv, "batch": prob.batch,
                    "q_len": prob.q_len, "heads": prob.num_heads, "page_size": prob.page_size,
                    "ctx_tokens_total": int(prob.cache_seqlens.sum()), "seed": prob.seed,
                    "parallelism": "single GPU, split-KV over 256 CUs"},

@@ -5,13 +5,13 @@
  * h < num_heads, with L = cache_seqlens[b] and R = q_len * num_heads rows
  * (row r = i * num_heads + h):
  *
- *     k_t      = kv_cache[block_table[b][t / page_size]][t % page_size][0:576]
+ *     k_t      = row(kv_cache[block_table[b][t / page_size]][t % page_size])[0:576]
  *     v_t      = k_t[0:512]
  *     s_t      = softmax_scale * sum_d q[b][i][h][d] * k_t[d]        (d < 576)
  *     lse      = log sum_{t<E} exp(s_t)                               (natural log)
  *     out[:]   = sum_{t<E} exp(s_t - lse) * v_t
  *
- * where E = L, or, for a causal problem, E = max(0, L - (q_len - 1 - i)): query
+ * where row() widens a stored cache row (see mla_kv_dtype_t) and E = L, or, for a causal problem, E = max(0, L - (q_len - 1 - i)): query
  * token i then sits at position L - q_len + i of a context whose last q_len
  * rows are the query tokens' own (multi-token / speculative decode), and sees
  * only the tokens up to and including itself.  A row with E = 0 gets out = 0
@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum {
   MLA_OK = 0,
@@ -69,6 +69,19 @@ typedef enum {
 } mla_status_t;
 
 typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype_t;
+
+/* Storage of one cached token row.
+ *   MLA_KV_BF16      576 bf16 values (1,152 bytes): 512 latent columns, then 64 rope columns.
+ *   MLA_KV_FP8_E4M3  656 bytes: bytes [0, 512) the latent columns as OCP FP8 E4M3 codes
+ *                    (bias 7, no infinities, S.1111.111 = NaN); bytes [512, 640) the rope
+ *                    columns as bf16; bytes [640, 656) four float32 group scales.  Latent
+ *                    column c widens to e4m3(code) * 2^(E - 127), E the biased exponent of
+ *                    scale c / 128: only the exponent of a scale is used, so power-of-two
+ *                    scales are the natural choice (every widened value is then exact in
+ *                    bf16); scales must be normal, finite numbers.  An FP8 cache is an
+ *                    FP8 latent cache in the sense of the FlashMLA pages; this layout is
+ *                    this library's.  */
+typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_dtype_t;
 
 /* Shapes of one decode call. */
 typedef struct {
@@ -83,6 +96,7 @@ typedef struct {
   mla_dtype_t out_dtype;      /* dtype of `out`: BF16 (round to nearest even) or FP32 */
   int32_t causal;             /* 0: every query token sees all L tokens; 1: token i sees the
                                  first L - (q_len - 1 - i) (see the definition above) */
+  mla_kv_dtype_t kv_dtype;    /* storage of the cache rows (MLA_KV_BF16 or MLA_KV_FP8_E4M3) */
 } mla_problem_t;
 
 /* Planner options.  Zero-initialise for defaults. */
@@ -140,7 +154,8 @@ mla_status_t mla_plan_upload(mla_plan_t plan, void* workspace, size_t workspace_
 /* Paged MLA decode (two launches on `stream`: split decode, then the merge of
  * split sequences).
  *   q             [B, q_len, H, 576] bf16, contiguous, 16-B aligned
- *   kv_cache      [num_pages, page_size, 576] bf16, contiguous, 16-B aligned
+ *   kv_cache      [num_pages, page_size, row] rows of problem->kv_dtype (1,152 or 656 bytes),
+ *                 contiguous, 16-B aligned
  *   block_table   [B, max_pages_per_seq] int32; entries < ceil(L_b/page_size) must lie in
  *                 [0, num_pages).  An entry outside that range is not dereferenced: its
  *                 tokens are dropped and the workspace status word gets bit 0 set.
@@ -172,8 +187,8 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
                                uint32_t stages);
 
 /* Test aid: write every sequence's logical rows, in token order, to rows_out
- * [sum_b L_b, 576] bf16 (sequence b starts at row sum_{b'<b} L_b'), using the
- * same page walk as mla_decode.  Bit-exact copy; async on `stream`. */
+ * [sum_b L_b, row bytes] (sequence b starts at row sum_{b'<b} L_b'), using the
+ * same page walk as mla_decode.  Bit-exact copy of the stored rows; async on `stream`. */
 mla_status_t mla_debug_gather(mla_plan_t plan, const void* kv_cache, const int32_t* block_table,
                               void* rows_out, void* stream);
 

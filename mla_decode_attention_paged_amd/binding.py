@@ -20,6 +20,8 @@ MLA_ERR_HIP = 4
 MLA_ERR_PLAN_MISMATCH = 5
 MLA_DTYPE_BF16 = 0
 MLA_DTYPE_FP32 = 1
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3 = 1
 MLA_STAGE_SPLIT = 1
 MLA_STAGE_MERGE = 2
 MLA_STAGE_ALL = 3
@@ -35,7 +37,7 @@ class mla_problem_t(C.Structure):
     _fields_ = [("batch", C.c_int32), ("q_len", C.c_int32), ("num_heads", C.c_int32),
                 ("head_dim_qk", C.c_int32), ("head_dim_v", C.c_int32), ("page_size", C.c_int32),
                 ("num_pages", C.c_int32), ("max_pages_per_seq", C.c_int32), ("out_dtype", C.c_int32),
-                ("causal", C.c_int32)]
+                ("causal", C.c_int32), ("kv_dtype", C.c_int32)]
 
 
 class mla_plan_options_t(C.Structure):
@@ -106,9 +108,10 @@ def abi_version() -> int:
 
 
 def make_problem(batch, q_len, num_heads, page_size, num_pages, max_pages_per_seq, out_fp32=False,
-                 head_dim_qk=576, head_dim_v=512, causal=False) -> mla_problem_t:
+                 head_dim_qk=576, head_dim_v=512, causal=False, kv_fp8=False) -> mla_problem_t:
     return mla_problem_t(batch, q_len, num_heads, head_dim_qk, head_dim_v, page_size, num_pages,
-                         max_pages_per_seq, MLA_DTYPE_FP32 if out_fp32 else MLA_DTYPE_BF16, int(causal))
+                         max_pages_per_seq, MLA_DTYPE_FP32 if out_fp32 else MLA_DTYPE_BF16, int(causal),
+                         MLA_KV_FP8_E4M3 if kv_fp8 else MLA_KV_BF16)
 
 
 class Plan:
@@ -210,7 +213,7 @@ def mla_decode(plan: Plan, q, kv_cache, block_table, cache_seqlens, softmax_scal
     p = plan.problem
     R = p.q_len * p.num_heads
     _require(q, "q", (torch.bfloat16,), (p.batch, p.q_len, p.num_heads, 576))
-    _require(kv_cache, "kv_cache", (torch.bfloat16,), (p.num_pages, p.page_size, 576))
+    _require(kv_cache, "kv_cache", *_kv_spec(p))
     _require(block_table, "block_table", (torch.int32,), (p.batch, p.max_pages_per_seq))
     _require(cache_seqlens, "cache_seqlens", (torch.int32,), (p.batch,))
     odt = torch.float32 if p.out_dtype == MLA_DTYPE_FP32 else torch.bfloat16
@@ -224,12 +227,49 @@ def mla_decode(plan: Plan, q, kv_cache, block_table, cache_seqlens, softmax_scal
                                    _stream(stream), stages), "mla_decode")
 
 
+class BoundDecode:
+    """mla_decode_stages with every argument but the stream and the stage mask checked and
+    marshalled once (the tensors must stay alive and in place while it is used)."""
+
+    def __init__(self, plan: Plan, q, kv_cache, block_table, cache_seqlens, softmax_scale, out, lse, workspace):
+        import torch
+        p = plan.problem
+        _require(q, "q", (torch.bfloat16,), (p.batch, p.q_len, p.num_heads, 576))
+        _require(kv_cache, "kv_cache", *_kv_spec(p))
+        _require(block_table, "block_table", (torch.int32,), (p.batch, p.max_pages_per_seq))
+        _require(cache_seqlens, "cache_seqlens", (torch.int32,), (p.batch,))
+        odt = torch.float32 if p.out_dtype == MLA_DTYPE_FP32 else torch.bfloat16
+        _require(out, "out", (odt,), (p.batch, p.q_len, p.num_heads, 512))
+        if lse is not None:
+            _require(lse, "lse", (torch.float32,), (p.batch, p.q_len, p.num_heads))
+        _require(workspace, "workspace", (torch.uint8,))
+        self._keep = (plan, q, kv_cache, block_table, cache_seqlens, out, lse, workspace)
+        self._fn = lib().mla_decode_stages
+        self._args = (plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens),
+                      C.c_float(float(softmax_scale)), _ptr(out), _ptr(lse), _ptr(workspace),
+                      C.c_size_t(_nbytes(workspace)))
+
+    def __call__(self, stream_handle: int, stages: int = MLA_STAGE_ALL):
+        st = self._fn(*self._args, stream_handle, stages)
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode", last_error())
+
+
+def _kv_spec(p):
+    """(accepted torch dtypes, shape) of the cache for a problem struct."""
+    import torch
+    if p.kv_dtype == MLA_KV_FP8_E4M3:
+        return (torch.uint8,), (p.num_pages, p.page_size, 656)
+    return (torch.bfloat16, torch.int16), (p.num_pages, p.page_size, 576)
+
+
 def mla_debug_gather(plan: Plan, kv_cache, block_table, rows_out, stream=None):
     import torch
     p = plan.problem
-    _require(kv_cache, "kv_cache", (torch.bfloat16, torch.int16), (p.num_pages, p.page_size, 576))
+    dts, shape = _kv_spec(p)
+    _require(kv_cache, "kv_cache", dts, shape)
     _require(block_table, "block_table", (torch.int32,), (p.batch, p.max_pages_per_seq))
-    _require(rows_out, "rows_out", (torch.bfloat16, torch.int16), (int(plan.seqlens.sum()), 576))
+    _require(rows_out, "rows_out", dts, (int(plan.seqlens.sum()), shape[-1]))
     _check(lib().mla_debug_gather(plan.handle, _ptr(kv_cache), _ptr(block_table), _ptr(rows_out),
                                   _stream(stream)), "mla_debug_gather")
 

@@ -41,6 +41,8 @@ mla_status_t check_problem(const mla_problem_t* p) {
     return fail(MLA_ERR_INVALID_ARGUMENT, "out_dtype must be MLA_DTYPE_BF16 or MLA_DTYPE_FP32");
   if (p->causal != 0 && p->causal != 1)
     return fail(MLA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", p->causal);
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "kv_dtype must be MLA_KV_BF16 or MLA_KV_FP8_E4M3");
   if (p->head_dim_qk != mla::kDqk || p->head_dim_v != mla::kDv)
     return fail(MLA_ERR_UNSUPPORTED, "head dims must be 576/512 (got %d/%d)", p->head_dim_qk, p->head_dim_v);
   if (p->page_size % mla::kBlock != 0)
@@ -229,6 +231,7 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
   a.q_len = p.prob.q_len;
   a.num_heads = p.prob.num_heads;
   a.causal = p.prob.causal;
+  a.kv_fp8 = p.prob.kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
   const bool f32 = p.prob.out_dtype == MLA_DTYPE_FP32;
   if ((stages & MLA_STAGE_SPLIT) && p.grid > 0) {
     int e = mla::launch_decode(a, p.rows_per_group, f32, p.grid, stream);
@@ -258,9 +261,9 @@ mla_status_t mla_debug_gather(mla_plan_t plan, const void* kv_cache, const int32
   const mla::PlanImpl& p = plan->impl;
   for (int b = 0; b < p.prob.batch; ++b) {
     if (p.seqlens[b] == 0) continue;
-    int e = mla::launch_gather((const uint16_t*)kv_cache, block_table, (uint16_t*)rows_out, b, p.seqlens[b],
-                               p.row_offsets[b], p.prob.page_size, p.prob.max_pages_per_seq,
-                               p.prob.num_pages, stream);
+    const int32_t row_bytes = p.prob.kv_dtype == MLA_KV_FP8_E4M3 ? mla::kRowBytesFp8 : mla::kRowBytesBf16;
+    int e = mla::launch_gather(kv_cache, block_table, rows_out, b, p.seqlens[b], p.row_offsets[b],
+                               p.prob.page_size, p.prob.max_pages_per_seq, p.prob.num_pages, row_bytes, stream);
     if (e) return fail(MLA_ERR_HIP, "gather launch: %s", mla::hip_error_string(e));
   }
   return MLA_OK;

@@ -16,6 +16,8 @@ constexpr int kBlock = 16;         // tokens per KV block (one MFMA M tile)
 constexpr int kWaves = 4;          // waves per work-group in the split-decode kernel
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxRows = 128;
+constexpr int kRowBytesBf16 = kDqk * 2;   // 1,152
+constexpr int kRowBytesFp8 = 656;         // 512 E4M3 + 64 bf16 rope + 4 float32 scales
 
 // Workspace layout (byte offsets from the workspace base).
 //   [0, 256)              status word (int32) + padding
@@ -81,6 +83,7 @@ struct DecodeArgs {
   int32_t q_len;
   int32_t num_heads;
   int32_t causal;                // row r = i * num_heads + h sees t < L - (q_len - 1 - i)
+  int32_t kv_fp8;                // cache rows are 656-byte fp8 rows
 };
 
 struct MergeArgs {
@@ -96,9 +99,9 @@ struct MergeArgs {
 // Kernel launchers (mla_kernels.hip).  Return a HIP error code (0 = success).
 int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream);
 int launch_merge(const MergeArgs& a, bool out_fp32, void* stream);
-int launch_gather(const uint16_t* kv, const int32_t* block_table, uint16_t* rows_out, int32_t seq,
-                  int32_t length, int64_t row_offset, int32_t page_size, int32_t bt_stride,
-                  int32_t num_pages, void* stream);
+int launch_gather(const void* kv, const int32_t* block_table, void* rows_out, int32_t seq, int32_t length,
+                  int64_t row_offset, int32_t page_size, int32_t bt_stride, int32_t num_pages, int32_t row_bytes,
+                  void* stream);
 const char* hip_error_string(int code);
 
 }  // namespace mla

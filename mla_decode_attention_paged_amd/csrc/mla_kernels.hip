@@ -46,6 +46,13 @@ constexpr int kVBlocks = kDv / 16;                 // 32 output column blocks
 constexpr int kBlockBytes = kBlock * kDqk * 2;     // 18,432 bytes per 16-token block
 constexpr int kStages = 2;
 constexpr int kSmemBytes = kWaves * kStages * kBlockBytes;   // 147,456
+// FP8 cache rows: 512 E4M3 latent bytes, 64 bf16 rope values, 4 float32 group scales
+constexpr int kF8Row = 656;
+constexpr int kF8Units = kBlock * kF8Row / 16;                 // 656 16-B units per block
+constexpr int kF8Stage = kBlock * kF8Row;                      // 10,496 bytes
+constexpr int kF8Loads = (kF8Units + 63) / 64;                 // 11 DMA instructions per block
+constexpr int kF8WaveBytes = 2 * kF8Stage + kBlockBytes;       // two fp8 stages + one bf16 stage
+constexpr int kSmemFp8 = kWaves * kF8WaveBytes;                // 157,696
 constexpr int kLoadsPerBlock = kBlockBytes / (64 * 16);      // 18 DMA loads per wave per block
 constexpr float kRescaleSlack = 8.0f;              // lazy rescale threshold (log2 units)
 constexpr float kNegBig = -1.0e30f;                // running-max start value (finite)
@@ -176,10 +183,49 @@ __device__ __forceinline__ void lds_read_v16(u32x2_t (&r)[16], LDS_AS const uint
       : "memory");
 }
 
-// Split-decode kernel: 16 query rows per work-group (R = 16 * row groups).
-template <bool OUT_F32>
+// Reads of one lane's share of an fp8 stage: 128 latent bytes at pl, 32 rope bytes at pr
+// and a 4-byte group scale at ps.
+__device__ __forceinline__ void lds_read_f8(u32x4_t (&lat)[8], u32x4_t (&rope)[2], uint32_t& scale,
+                                            LDS_AS const uint8_t* pl, LDS_AS const uint8_t* pr,
+                                            LDS_AS const uint8_t* ps) {
+  asm volatile(
+      "ds_read_b128 %0, %11 offset:0\n\tds_read_b128 %1, %11 offset:16\n\tds_read_b128 %2, %11 offset:32\n\t"
+      "ds_read_b128 %3, %11 offset:48\n\tds_read_b128 %4, %11 offset:64\n\tds_read_b128 %5, %11 offset:80\n\t"
+      "ds_read_b128 %6, %11 offset:96\n\tds_read_b128 %7, %11 offset:112\n\t"
+      "ds_read_b128 %8, %12 offset:0\n\tds_read_b128 %9, %12 offset:16\n\tds_read_b32 %10, %13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lat[0]), "=&v"(lat[1]), "=&v"(lat[2]), "=&v"(lat[3]), "=&v"(lat[4]), "=&v"(lat[5]),
+        "=&v"(lat[6]), "=&v"(lat[7]), "=&v"(rope[0]), "=&v"(rope[1]), "=&v"(scale)
+      : "v"(pl), "v"(pr), "v"(ps)
+      : "memory");
+}
+// Writes of one lane's converted share into the bf16 stage: chunk m of the first 8 at
+// w[m], of the second 8 at w[m] + 2048, the two rope chunks at r0 and r1.
+__device__ __forceinline__ void lds_write_bf16(LDS_AS uint8_t* const (&w)[8], LDS_AS uint8_t* r0, LDS_AS uint8_t* r1,
+                                               const u32x4_t (&c)[16], const u32x4_t (&rope)[2]) {
+  asm volatile(
+      "ds_write_b128 %0, %10\n\tds_write_b128 %1, %11\n\tds_write_b128 %2, %12\n\tds_write_b128 %3, %13\n\t"
+      "ds_write_b128 %4, %14\n\tds_write_b128 %5, %15\n\tds_write_b128 %6, %16\n\tds_write_b128 %7, %17\n\t"
+      "ds_write_b128 %0, %18 offset:2048\n\tds_write_b128 %1, %19 offset:2048\n\t"
+      "ds_write_b128 %2, %20 offset:2048\n\tds_write_b128 %3, %21 offset:2048\n\t"
+      "ds_write_b128 %4, %22 offset:2048\n\tds_write_b128 %5, %23 offset:2048\n\t"
+      "ds_write_b128 %6, %24 offset:2048\n\tds_write_b128 %7, %25 offset:2048\n\t"
+      "ds_write_b128 %8, %26\n\tds_write_b128 %9, %27\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]), "v"(r0), "v"(r1),
+        "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(c[4]), "v"(c[5]), "v"(c[6]), "v"(c[7]),
+        "v"(c[8]), "v"(c[9]), "v"(c[10]), "v"(c[11]), "v"(c[12]), "v"(c[13]), "v"(c[14]), "v"(c[15]),
+        "v"(rope[0]), "v"(rope[1])
+      : "memory");
+}
+
+// Split-decode kernel: 16 query rows per work-group (R = 16 * row groups).  FP8: the cache
+// rows are 656-byte fp8 rows (see kF8Row); each block goes through a small fp8 stage and
+// is widened into one bf16 stage in the row-major layout, where the bf16 path reads it.
+template <bool OUT_F32, bool FP8>
 __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FP8 ? kSmemFp8 : kSmemBytes];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
 
   const int lane = threadIdx.x & 63;
@@ -213,8 +259,11 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   const int ld_tok0 = lane >> 3, ld_tok1 = 8 + (lane >> 3);
   const int ld_col0 = 8 * ((lane & 7) ^ row_swz(ld_tok0)), ld_col1 = 8 * ((lane & 7) ^ row_swz(ld_tok1));
 
-  LDS_AS uint8_t* stage0 = lds + (wave * kStages + 0) * kBlockBytes;
-  LDS_AS uint8_t* stage1 = lds + (wave * kStages + 1) * kBlockBytes;
+  // bf16: two DMA stages; FP8: two fp8 DMA stages and one bf16 stage the blocks are widened into
+  LDS_AS uint8_t* stage0 = FP8 ? lds + wave * kF8WaveBytes : lds + (wave * kStages + 0) * kBlockBytes;
+  LDS_AS uint8_t* stage1 = FP8 ? stage0 + kF8Stage : lds + (wave * kStages + 1) * kBlockBytes;
+  LDS_AS uint8_t* const cstage = FP8 ? stage0 + 2 * kF8Stage : nullptr;
+  const uint8_t* const kv8 = (const uint8_t*)a.kv;
 
   const CST_AS int32_t* worker_off = as_const(a.worker_off);
   const CST_AS int32_t* pieces = as_const(a.pieces);
@@ -253,7 +302,9 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     // false for an out-of-range table entry (then page 0 is read, in bounds, and the block
     // is skipped).  Rows past the end of the piece re-read its last valid row.
     struct Src {
-      const uint16_t* p[2];
+      const uint16_t* p[2];   // bf16: this lane's source for even / odd instructions
+      const uint8_t* row0;    // FP8: the block's first row
+      int last;               // FP8: index of the block's last valid row
     };
     auto source = [&](int k, bool& ok) -> Src {
       const int tok0 = tb + kBlock * blk_of(k);
@@ -261,17 +312,69 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       ok = base >= 0;
       if (!ok) base = 0;
       const int last = te - 1 - tok0;
-      Src r;
-      r.p[0] = a.kv + (base + min(ld_tok0, last)) * kDqk + ld_col0;
-      r.p[1] = a.kv + (base + min(ld_tok1, last)) * kDqk + ld_col1;
+      Src r{};
+      if constexpr (FP8) {
+        r.row0 = kv8 + base * kF8Row;
+        r.last = last;
+      } else {
+        r.p[0] = a.kv + (base + min(ld_tok0, last)) * kDqk + ld_col0;
+        r.p[1] = a.kv + (base + min(ld_tok1, last)) * kDqk + ld_col1;
+      }
       return r;
     };
-    // the 18 DMA loads of a block (1 KB each: 128 B of 8 rows, chunk block j/2) into a stage
+    // The DMA loads of a block into a stage.  bf16: 18 instructions of 1 KB, each 128 B of 8
+    // rows (chunk block j/2).  FP8: the 656 16-B units of the 16 rows in row order, 64 per
+    // instruction (the 11th moves the last 16).
     auto issue = [&](const Src& src, LDS_AS uint8_t* stage) {
+      if constexpr (FP8) {
 #pragma unroll
-      for (int j = 0; j < kLoadsPerBlock; ++j)
-        __builtin_amdgcn_global_load_lds((GLB_AS void*)(src.p[j & 1] + 64 * (j >> 1)),
-                                         (LDS_AS void*)(stage + 1024 * j), 16, 0, 0);
+        for (int j = 0; j < kF8Loads; ++j) {
+          const int u = 64 * j + lane;
+          if (j + 1 < kF8Loads || u < kF8Units) {
+            const int t = u / (kF8Row / 16), c = u - t * (kF8Row / 16);
+            __builtin_amdgcn_global_load_lds((GLB_AS void*)(src.row0 + min(t, src.last) * kF8Row + 16 * c),
+                                             (LDS_AS void*)(stage + 1024 * j), 16, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kLoadsPerBlock; ++j)
+          __builtin_amdgcn_global_load_lds((GLB_AS void*)(src.p[j & 1] + 64 * (j >> 1)),
+                                           (LDS_AS void*)(stage + 1024 * j), 16, 0, 0);
+      }
+    };
+    // FP8: widen an fp8 stage into the bf16 stage.  Lane (t = lane % 16, q = lane / 16)
+    // converts latent columns [128q, 128q + 128) of token t (one group scale, which the
+    // conversion applies through its exponent) and copies rope chunks 2q, 2q + 1.
+    auto widen = [&](LDS_AS const uint8_t* f8, LDS_AS uint8_t* dst) {
+      const int t = lane & 15, q = lane >> 4;
+      u32x4_t lat[8], rope[2];
+      uint32_t scale_bits;
+      lds_read_f8(lat, rope, scale_bits, f8 + t * kF8Row + 128 * q, f8 + t * kF8Row + 512 + 32 * q,
+                  f8 + t * kF8Row + 640 + 4 * q);
+      const float scale = __uint_as_float(scale_bits);
+      u32x4_t c[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t x = lat[i][2 * h + w];
+            c[2 * i + h][2 * w + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, scale, false));
+            c[2 * i + h][2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, scale, true));
+          }
+        }
+      }
+      // chunk m of this lane's 16 is column chunk 16q + m of token t: unit
+      // 128 * (2q + m / 8) + 8t + ((m % 8) ^ row_swz(t)); rope chunk 64 + 2q + i likewise
+      const int sw = row_swz(t);
+      LDS_AS uint8_t* w[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) w[m] = dst + 16 * (256 * q + 8 * t + (m ^ sw));
+      LDS_AS uint8_t* r0 = dst + 16 * (1024 + 8 * t + ((2 * q) ^ sw));
+      LDS_AS uint8_t* r1 = dst + 16 * (1024 + 8 * t + ((2 * q + 1) ^ sw));
+      lds_write_bf16(w, r0, r1, c, rope);
     };
     // Every LDS read of a block first (K for S^T, then all of V^T into registers); then the
     // stage is refilled with the block after next (`ns`, if `nx`) while S^T, the softmax
@@ -294,7 +397,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       LDS_AS const uint8_t* const vp[4] = {st + v_base[0], st + v_base[1], st + v_base[2], st + v_base[3]};
       lds_read_v16<0>(vf0, vp);                // columns 0..255
       lds_read_v16<1>(vf1, vp);                // columns 256..511
-      if (nx) issue(ns, st);
+      if (!FP8 && nx) issue(ns, st);
       mma(kf, 9);
       sacc += acc2;
     };
@@ -342,7 +445,10 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         Src nsrc{};
         if (nx) nsrc = source(k + 2, nok);
         if (k + 1 < my_n) {
-          asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+          if constexpr (FP8)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kF8Loads) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerBlock) : "memory");
         } else {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
@@ -355,7 +461,13 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         }
         const int tok0 = tb + kBlock * blk_of(k);
         f32x4_t sacc;
-        scores(st, sacc, vf0, vf1, nsrc, nx);
+        if constexpr (FP8) {
+          widen(st, cstage);
+          if (nx) issue(nsrc, st);
+          scores(cstage, sacc, vf0, vf1, nsrc, false);
+        } else {
+          scores(st, sacc, vf0, vf1, nsrc, nx);
+        }
         const int nvalid = lim - tok0;   // tokens of the block this row sees (may be <= 0)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
@@ -781,28 +893,36 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   if (cg == 0 && (threadIdx.x & 15) == 0 && a.lse) a.lse[(int64_t)b * R + r] = L > 0.f ? M + __logf(L) : -INFINITY;
 }
 
-// Debug gather: one thread per 16-B chunk of a sequence's logical rows.
-__global__ void __launch_bounds__(256) gather_kernel(const uint16_t* kv, const int32_t* block_table, uint16_t* rows_out,
+// Debug gather: one thread per 16-B chunk of a sequence's logical rows (row_bytes per row).
+__global__ void __launch_bounds__(256) gather_kernel(const uint8_t* kv, const int32_t* block_table, uint8_t* rows_out,
                                                      int32_t seq, int32_t length, int64_t row_offset,
-                                                     int32_t page_size, int32_t bt_stride, int32_t num_pages) {
+                                                     int32_t page_size, int32_t bt_stride, int32_t num_pages,
+                                                     int32_t row_bytes) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int t = (int)(idx / (kDqk / 8));
-  const int c = (int)(idx % (kDqk / 8));
+  const int chunks = row_bytes / 16;
+  const int t = (int)(idx / chunks);
+  const int c = (int)(idx % chunks);
   if (t >= length) return;
   const int64_t row = kv_row_of(block_table, bt_stride, page_size, num_pages, seq, t);
   if (row < 0) return;
-  *(u32x4_t*)(rows_out + (row_offset + t) * kDqk + 8 * c) = *(const u32x4_t*)(kv + row * kDqk + 8 * c);
+  *(u32x4_t*)(rows_out + (row_offset + t) * row_bytes + 16 * c) = *(const u32x4_t*)(kv + row * row_bytes + 16 * c);
 }
 
 }  // namespace
 
 int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (rows_per_group == 16) {
+  if (a.kv_fp8) {
+    if (rows_per_group != 16) return (int)hipErrorInvalidValue;
     if (out_fp32)
-      hipLaunchKernelGGL((split_decode_kernel<true>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split_decode_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((split_decode_kernel<false>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split_decode_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else if (rows_per_group == 16) {
+    if (out_fp32)
+      hipLaunchKernelGGL((split_decode_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((split_decode_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, a);
   } else if (rows_per_group == 32) {
     if (out_fp32)
       hipLaunchKernelGGL((group_decode_kernel<2, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -829,12 +949,13 @@ int launch_merge(const MergeArgs& a, bool out_fp32, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_gather(const uint16_t* kv, const int32_t* block_table, uint16_t* rows_out, int32_t seq, int32_t length,
-                  int64_t row_offset, int32_t page_size, int32_t bt_stride, int32_t num_pages, void* stream) {
-  const int64_t chunks = (int64_t)length * (kDqk / 8);
+int launch_gather(const void* kv, const int32_t* block_table, void* rows_out, int32_t seq, int32_t length,
+                  int64_t row_offset, int32_t page_size, int32_t bt_stride, int32_t num_pages, int32_t row_bytes,
+                  void* stream) {
+  const int64_t chunks = (int64_t)length * (row_bytes / 16);
   const int grid = (int)((chunks + 255) / 256);
-  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, kv, block_table, rows_out, seq,
-                     length, row_offset, page_size, bt_stride, num_pages);
+  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)kv, block_table,
+                     (uint8_t*)rows_out, seq, length, row_offset, page_size, bt_stride, num_pages, row_bytes);
   return (int)hipGetLastError();
 }
 

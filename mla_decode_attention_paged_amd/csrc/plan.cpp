@@ -36,7 +36,9 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
   pl.rows = (int32_t)R;
   // query rows per work-group: 16 (one wave each), 32 or 64 (grouped waves sharing KV);
   // more rows run as several row groups over the same token ranges
-  if (R % 64 == 0) {
+  if (p.kv_dtype == MLA_KV_FP8_E4M3) {
+    pl.rows_per_group = 16;            // the fp8 rows are widened by the 16-row kernel
+  } else if (R % 64 == 0) {
     pl.rows_per_group = 64;
   } else if (R == 32) {
     pl.rows_per_group = 32;

@@ -10,7 +10,10 @@ def to_device(prob, device="cuda"):
     """Host Problem -> dict of contiguous device tensors (bf16 bit patterns reinterpreted)."""
     import torch
     q = torch.from_numpy(prob.q.view(np.int16)).to(device).view(torch.bfloat16)
-    kv = torch.from_numpy(prob.kv_cache.view(np.int16)).to(device).view(torch.bfloat16)
+    if prob.kv_cache.dtype == np.uint8:           # fp8 rows (656 bytes each)
+        kv = torch.from_numpy(prob.kv_cache).to(device)
+    else:
+        kv = torch.from_numpy(prob.kv_cache.view(np.int16)).to(device).view(torch.bfloat16)
     bt = torch.from_numpy(prob.block_table).to(device)
     sl = torch.from_numpy(prob.cache_seqlens.astype(np.int32)).to(device)
     return {"q": q, "kv_cache": kv, "block_table": bt, "cache_seqlens": sl}
@@ -18,7 +21,8 @@ def to_device(prob, device="cuda"):
 
 def problem_struct(prob, causal=False):
     return B.make_problem(prob.batch, prob.q_len, prob.num_heads, prob.page_size, prob.num_pages,
-                          prob.max_pages_per_seq, out_fp32=prob.out_fp32, causal=causal)
+                          prob.max_pages_per_seq, out_fp32=prob.out_fp32, causal=causal,
+                          kv_fp8=prob.kv_format == "fp8")
 
 
 class Runner:
@@ -36,10 +40,14 @@ class Runner:
         self.out = torch.empty((prob.batch, prob.q_len, prob.num_heads, 512), dtype=odt, device=device)
         self.lse = torch.empty((prob.batch, prob.q_len, prob.num_heads), dtype=torch.float32, device=device)
 
-    def __call__(self, stream=None, stages=B.MLA_STAGE_ALL):
         d = self.dev
-        B.mla_decode(self.plan, d["q"], d["kv_cache"], d["block_table"], d["cache_seqlens"],
-                     self.prob.softmax_scale, self.out, self.lse, self.ws, stream=stream, stages=stages)
+        self._bound = B.BoundDecode(self.plan, d["q"], d["kv_cache"], d["block_table"], d["cache_seqlens"],
+                                    self.prob.softmax_scale, self.out, self.lse, self.ws)
+
+    def __call__(self, stream=None, stages=B.MLA_STAGE_ALL):
+        import torch
+        sh = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+        self._bound(sh, stages)
         return self.out, self.lse
 
     def results(self):

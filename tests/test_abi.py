@@ -23,7 +23,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) >= 12
     for n in names:
         assert hasattr(lib, n), f"libmla.so does not export {n}"
-    assert B.abi_version() == 2
+    assert B.abi_version() == 3
 
 
 def test_status_strings():
