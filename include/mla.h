@@ -104,7 +104,10 @@ typedef struct {
   int32_t num_cus;            /* compute units to plan for; 0 = ask the current HIP device */
   int32_t force_splits;       /* 0 = cost model; k > 0 = cut every sequence into min(k, blocks)
                                  near-equal parts, one work-group each (testing the merge) */
-  int32_t reserved[6];        /* must be zero */
+  int32_t rows_per_group;     /* 0 = automatic; 16, 32 or 64 = query rows per work-group (16: the
+                                 16-row kernel in R/16 row groups; 32, 64: the grouped kernel,
+                                 R must be a multiple) -- a tuning and testing knob */
+  int32_t reserved[5];        /* must be zero */
 } mla_plan_options_t;
 
 /* Read-only summary of a plan (for tests and diagnostics). */
@@ -191,6 +194,30 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
  * same page walk as mla_decode.  Bit-exact copy of the stored rows; async on `stream`. */
 mla_status_t mla_debug_gather(mla_plan_t plan, const void* kv_cache, const int32_t* block_table,
                               void* rows_out, void* stream);
+
+/* ---- Device-scheduled decode (no host plan; graph-capturable with changing lengths).
+ *
+ * The work-groups cut the batch's 16-token blocks among themselves at run time from the
+ * device cache_seqlens (with W = min(num_workers, T / 4), at least 1, work-group w < W takes
+ * blocks [floor(wT/W), floor((w+1)T/W)) of the batch's T blocks, in sequence order); each
+ * sequence's first piece records how the sequence was cut, and a second launch combines
+ * the pieces of split sequences by log-sum-exp.  The lengths may change between calls
+ * (and between replays of a captured graph) up to max_pages_per_seq * page_size (larger
+ * device values are clipped to it).  Problems run as 16-row groups.
+ *
+ * num_workers: work-groups per row group; 0 = the current device's compute units divided
+ * by the number of row groups (R / 16), at least 1.
+ *
+ * Workspace: mla_devplan_workspace_bytes bytes, 256-B aligned; mla_devplan_prepare clears
+ * its status word (and need only be called once).  Calls that share a workspace must not
+ * overlap in time. */
+size_t mla_devplan_workspace_bytes(const mla_problem_t* problem, int32_t num_workers);   /* 0 on error */
+mla_status_t mla_devplan_prepare(const mla_problem_t* problem, int32_t num_workers, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_workers, const void* q,
+                                const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+                                float softmax_scale, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Read the workspace status word (synchronises `stream`).  Bit 0: a block_table
  * entry was out of range in some mla_decode since the last mla_plan_upload. */

@@ -41,7 +41,8 @@ class mla_problem_t(C.Structure):
 
 
 class mla_plan_options_t(C.Structure):
-    _fields_ = [("num_cus", C.c_int32), ("force_splits", C.c_int32), ("reserved", C.c_int32 * 6)]
+    _fields_ = [("num_cus", C.c_int32), ("force_splits", C.c_int32), ("rows_per_group", C.c_int32),
+                ("reserved", C.c_int32 * 5)]
 
 
 class mla_plan_info_t(C.Structure):
@@ -71,6 +72,11 @@ _SIGS = {
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_uint32]),
     "mla_debug_gather": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "mla_read_status": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(C.c_int32)]),
+    "mla_devplan_workspace_bytes": (C.c_size_t, [C.POINTER(mla_problem_t), C.c_int32]),
+    "mla_devplan_prepare": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "mla_decode_devplan": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                     C.c_void_p]),
     "mla_plan_destroy": (None, [C.c_void_p]),
     "mla_status_string": (C.c_char_p, [C.c_int]),
     "mla_last_error": (C.c_char_p, []),
@@ -117,14 +123,15 @@ def make_problem(batch, q_len, num_heads, page_size, num_pages, max_pages_per_se
 class Plan:
     """Host-side split-KV schedule (mla_plan)."""
 
-    def __init__(self, problem: mla_problem_t, cache_seqlens_host, num_cus: int = 0, force_splits: int = 0):
+    def __init__(self, problem: mla_problem_t, cache_seqlens_host, num_cus: int = 0, force_splits: int = 0,
+                 rows_per_group: int = 0):
         import numpy as np
         self.problem = problem
         sl = np.ascontiguousarray(np.asarray(cache_seqlens_host, dtype=np.int32))
         if sl.shape != (problem.batch,):
             raise ValueError(f"cache_seqlens_host must have shape ({problem.batch},), got {sl.shape}")
         self.seqlens = sl
-        opt = mla_plan_options_t(num_cus, force_splits)
+        opt = mla_plan_options_t(num_cus, force_splits, rows_per_group)
         h = C.c_void_p()
         _check(lib().mla_plan(C.byref(problem), sl.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(opt),
                               C.byref(h)), "mla_plan")
@@ -272,6 +279,48 @@ def mla_debug_gather(plan: Plan, kv_cache, block_table, rows_out, stream=None):
     _require(rows_out, "rows_out", dts, (int(plan.seqlens.sum()), shape[-1]))
     _check(lib().mla_debug_gather(plan.handle, _ptr(kv_cache), _ptr(block_table), _ptr(rows_out),
                                   _stream(stream)), "mla_debug_gather")
+
+
+def devplan_workspace_bytes(problem: mla_problem_t, num_workers: int = 0) -> int:
+    n = lib().mla_devplan_workspace_bytes(C.byref(problem), num_workers)
+    if n == 0:
+        raise MlaError(MLA_ERR_INVALID_ARGUMENT, "mla_devplan_workspace_bytes", last_error())
+    return n
+
+
+def devplan_prepare(problem: mla_problem_t, num_workers: int, workspace, stream=None):
+    _check(lib().mla_devplan_prepare(C.byref(problem), num_workers, _ptr(workspace), _nbytes(workspace),
+                                     _stream(stream)), "mla_devplan_prepare")
+
+
+class BoundDevplanDecode:
+    """mla_decode_devplan with its arguments checked and marshalled once (the tensors must
+    stay alive and in place; the cache_seqlens tensor's contents may change between calls)."""
+
+    def __init__(self, problem: mla_problem_t, num_workers, q, kv_cache, block_table, cache_seqlens,
+                 softmax_scale, out, lse, workspace):
+        import torch
+        p = problem
+        _require(q, "q", (torch.bfloat16,), (p.batch, p.q_len, p.num_heads, 576))
+        _require(kv_cache, "kv_cache", *_kv_spec(p))
+        _require(block_table, "block_table", (torch.int32,), (p.batch, p.max_pages_per_seq))
+        _require(cache_seqlens, "cache_seqlens", (torch.int32,), (p.batch,))
+        odt = torch.float32 if p.out_dtype == MLA_DTYPE_FP32 else torch.bfloat16
+        _require(out, "out", (odt,), (p.batch, p.q_len, p.num_heads, 512))
+        if lse is not None:
+            _require(lse, "lse", (torch.float32,), (p.batch, p.q_len, p.num_heads))
+        _require(workspace, "workspace", (torch.uint8,))
+        self._problem = mla_problem_t.from_buffer_copy(p)
+        self._keep = (q, kv_cache, block_table, cache_seqlens, out, lse, workspace)
+        self._fn = lib().mla_decode_devplan
+        self._args = (C.byref(self._problem), num_workers, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                      _ptr(cache_seqlens), C.c_float(float(softmax_scale)), _ptr(out), _ptr(lse), _ptr(workspace),
+                      C.c_size_t(_nbytes(workspace)))
+
+    def __call__(self, stream_handle: int):
+        st = self._fn(*self._args, stream_handle)
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode_devplan", last_error())
 
 
 def mla_read_status(workspace, stream=None) -> int:

@@ -60,6 +60,39 @@ mla_status_t hip_fail(hipError_t e, const char* what) {
   return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Device-scheduled decode: workers per row group and the workspace layout
+// [status | per-sequence cut (4 x batch + 2 int32) | partial lse (2W x R) | partial out (2W x R x 512)].
+struct DevLayout {
+  int32_t workers = 0, row_groups = 0;
+  size_t off_info = 0, off_lse = 0, off_o = 0, bytes = 0;
+};
+
+mla_status_t dev_layout(const mla_problem_t* p, int32_t num_workers, DevLayout& d) {
+  mla_status_t s = check_problem(p);
+  if (s != MLA_OK) return s;
+  if (num_workers < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_workers must be >= 0");
+  const int32_t R = p->q_len * p->num_heads;
+  d.row_groups = R / 16;
+  int32_t w = num_workers;
+  if (w == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice (pass num_workers to size without a device)");
+    hipDeviceProp_t pr;
+    e = hipGetDeviceProperties(&pr, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    w = pr.multiProcessorCount / d.row_groups;
+  }
+  d.workers = w < 1 ? 1 : w;
+  d.off_info = mla::kMetaOffset;
+  d.off_lse = align256(d.off_info + 4 * (4 * (size_t)p->batch + 2));
+  d.off_o = align256(d.off_lse + 4 * 2 * (size_t)d.workers * R);
+  d.bytes = align256(d.off_o + 4 * 2 * (size_t)d.workers * R * mla::kDv);
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,8 +122,15 @@ mla_status_t mla_plan(const mla_problem_t* problem, const int32_t* cache_seqlens
   if (!cache_seqlens_host) return fail(MLA_ERR_INVALID_ARGUMENT, "cache_seqlens_host is NULL");
   mla_plan_options_t opt{};
   if (options) opt = *options;
-  for (int i = 0; i < 6; ++i)
+  for (int i = 0; i < 5; ++i)
     if (opt.reserved[i] != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "options.reserved must be zero");
+  {
+    const int32_t rpg = opt.rows_per_group, R = problem->q_len * problem->num_heads;
+    if (rpg != 0 && rpg != 16 && rpg != 32 && rpg != 64)
+      return fail(MLA_ERR_INVALID_ARGUMENT, "options.rows_per_group must be 0, 16, 32 or 64");
+    if (rpg > 16 && (R % rpg != 0 || problem->kv_dtype == MLA_KV_FP8_E4M3))
+      return fail(MLA_ERR_UNSUPPORTED, "rows_per_group %d needs R a multiple of it and a bf16 cache", rpg);
+  }
   if (opt.num_cus < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "options.num_cus must be >= 0");
   if (opt.force_splits < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "options.force_splits must be >= 0");
   const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
@@ -114,7 +154,7 @@ mla_status_t mla_plan(const mla_problem_t* problem, const int32_t* cache_seqlens
   mla_plan_s* pl = new (std::nothrow) mla_plan_s();
   if (!pl) return fail(MLA_ERR_INVALID_ARGUMENT, "out of host memory");
   std::string err;
-  s = mla::build_plan(*problem, cache_seqlens_host, cus, opt.force_splits, pl->impl, err);
+  s = mla::build_plan(*problem, cache_seqlens_host, cus, opt.force_splits, opt.rows_per_group, pl->impl, err);
   if (s != MLA_OK) {
     delete pl;
     return fail(s, "%s", err.c_str());
@@ -266,6 +306,84 @@ mla_status_t mla_debug_gather(mla_plan_t plan, const void* kv_cache, const int32
                                p.prob.page_size, p.prob.max_pages_per_seq, p.prob.num_pages, row_bytes, stream);
     if (e) return fail(MLA_ERR_HIP, "gather launch: %s", mla::hip_error_string(e));
   }
+  return MLA_OK;
+}
+
+size_t mla_devplan_workspace_bytes(const mla_problem_t* problem, int32_t num_workers) {
+  DevLayout d;
+  return dev_layout(problem, num_workers, d) == MLA_OK ? d.bytes : 0;
+}
+
+mla_status_t mla_devplan_prepare(const mla_problem_t* problem, int32_t num_workers, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  DevLayout d;
+  mla_status_t s = dev_layout(problem, num_workers, d);
+  if (s != MLA_OK) return s;
+  if (!workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if ((uintptr_t)workspace % 256 != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-B aligned");
+  if (workspace_bytes < d.bytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < required %zu B", workspace_bytes, d.bytes);
+  int e = mla::launch_fill_zero(workspace, d.off_lse, stream);
+  if (e) return fail(MLA_ERR_HIP, "workspace clear: %s", mla::hip_error_string(e));
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_workers, const void* q,
+                                const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+                                float softmax_scale, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  DevLayout d;
+  mla_status_t s = dev_layout(problem, num_workers, d);
+  if (s != MLA_OK) return s;
+  if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if ((uintptr_t)q % 16 || (uintptr_t)kv_cache % 16 || (uintptr_t)out % 16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "q, kv_cache and out must be 16-B aligned");
+  if ((uintptr_t)block_table % 4 || (uintptr_t)cache_seqlens % 4 || (uintptr_t)lse % 4)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "block_table, cache_seqlens and lse must be 4-B aligned");
+  if ((uintptr_t)workspace % 256 != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-B aligned");
+  if (workspace_bytes < d.bytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < required %zu B", workspace_bytes, d.bytes);
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  const mla_problem_t& p = *problem;
+  char* ws = (char*)workspace;
+  mla::DecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.kv = (const uint16_t*)kv_cache;
+  a.block_table = block_table;
+  a.seqlens = cache_seqlens;
+  a.out = out;
+  a.lse = lse;
+  a.part_lse = (float*)(ws + d.off_lse);
+  a.part_o = (float*)(ws + d.off_o);
+  a.status = (int32_t*)ws;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  a.rows = p.q_len * p.num_heads;
+  a.page_size = p.page_size;
+  a.num_pages = p.num_pages;
+  a.bt_stride = p.max_pages_per_seq;
+  a.num_workers = d.workers;
+  a.row_groups = d.row_groups;
+  a.q_len = p.q_len;
+  a.num_heads = p.num_heads;
+  a.causal = p.causal;
+  a.kv_fp8 = p.kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
+  a.batch = p.batch;
+  a.seq_info = (int32_t*)(ws + d.off_info);
+  const int32_t grid = d.row_groups > 1 ? (d.workers + 7) / 8 * 8 * d.row_groups : d.workers;
+  const bool f32 = p.out_dtype == MLA_DTYPE_FP32;
+  int e = mla::launch_decode(a, 16, f32, grid, stream, true);
+  if (e) return fail(MLA_ERR_HIP, "device-scheduled decode launch: %s", mla::hip_error_string(e));
+  mla::MergeArgs m{};
+  m.part_lse = a.part_lse;
+  m.part_o = a.part_o;
+  m.out = out;
+  m.lse = lse;
+  m.rows = a.rows;
+  m.seq_info = a.seq_info;
+  m.batch = p.batch;
+  e = mla::launch_merge_dev(m, f32, stream);
+  if (e) return fail(MLA_ERR_HIP, "device-scheduled merge launch: %s", mla::hip_error_string(e));
   return MLA_OK;
 }
 

@@ -58,7 +58,7 @@ struct PlanImpl {
 
 // Planner (pure host code).  Returns MLA_OK or an error with `err` filled.
 mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t num_cus,
-                        int32_t force_splits, PlanImpl& out, std::string& err);
+                        int32_t force_splits, int32_t rows_per_group, PlanImpl& out, std::string& err);
 
 // Parameters of the split-decode kernel.
 struct DecodeArgs {
@@ -84,6 +84,8 @@ struct DecodeArgs {
   int32_t num_heads;
   int32_t causal;                // row r = i * num_heads + h sees t < L - (q_len - 1 - i)
   int32_t kv_fp8;                // cache rows are 656-byte fp8 rows
+  int32_t batch;
+  int32_t* seq_info;             // device schedule: per-sequence cut [batch][4] + {T, W}
 };
 
 struct MergeArgs {
@@ -94,10 +96,15 @@ struct MergeArgs {
   float* lse;
   int32_t rows;
   int32_t num_merges;
+  const int32_t* seq_info;       // device schedule (merge_dev_kernel)
+  int32_t batch;
 };
 
 // Kernel launchers (mla_kernels.hip).  Return a HIP error code (0 = success).
-int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream);
+int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream,
+                  bool device_schedule = false);
+int launch_merge_dev(const MergeArgs& a, bool out_fp32, void* stream);
+int launch_fill_zero(void* p, size_t bytes, void* stream);   // bytes: a multiple of 4
 int launch_merge(const MergeArgs& a, bool out_fp32, void* stream);
 int launch_gather(const void* kv, const int32_t* block_table, void* rows_out, int32_t seq, int32_t length,
                   int64_t row_offset, int32_t page_size, int32_t bt_stride, int32_t num_pages, int32_t row_bytes,

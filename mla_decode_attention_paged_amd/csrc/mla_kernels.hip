@@ -55,6 +55,8 @@ constexpr int kF8WaveBytes = 2 * kF8Stage + kBlockBytes;       // two fp8 stages
 constexpr int kSmemFp8 = kWaves * kF8WaveBytes;                // 157,696
 constexpr int kLoadsPerBlock = kBlockBytes / (64 * 16);      // 18 DMA loads per wave per block
 constexpr float kRescaleSlack = 8.0f;              // lazy rescale threshold (log2 units)
+constexpr int kMinBlocks = kWaves;                 // device schedule: fewest blocks per work-group
+constexpr int kMergeBatch = 8;                     // partial results read at a time when merging
 constexpr float kNegBig = -1.0e30f;                // running-max start value (finite)
 constexpr int kMergeStride = kDv + 4;              // floats per row in the merge buffer
 
@@ -223,7 +225,9 @@ __device__ __forceinline__ void lds_write_bf16(LDS_AS uint8_t* const (&w)[8], LD
 // Split-decode kernel: 16 query rows per work-group (R = 16 * row groups).  FP8: the cache
 // rows are 656-byte fp8 rows (see kF8Row); each block goes through a small fp8 stage and
 // is widened into one bf16 stage in the row-major layout, where the bf16 path reads it.
-template <bool OUT_F32, bool FP8>
+// DEV: no host schedule; the work-groups cut the batch's blocks among themselves from the
+// device cache_seqlens and combine split sequences in the same launch (see below).
+template <bool OUT_F32, bool FP8, bool DEV>
 __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[FP8 ? kSmemFp8 : kSmemBytes];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
@@ -270,12 +274,9 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   const CST_AS int32_t* seqlens = as_const(a.seqlens);
   const CST_AS int32_t* block_table = as_const(a.block_table);
 
-  const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
-  for (int pi = p_begin; pi < p_end; ++pi) {
-    const int b = pieces[4 * pi + 0];
-    const int tb = pieces[4 * pi + 1];
-    const int te = min(pieces[4 * pi + 2], seqlens[b]);
-    const int slot = pieces[4 * pi + 3];
+  // one piece: tokens [tb, min(te_in, L)) of sequence b; slot -1 writes out/lse, else a partial
+  auto run_piece = [&](const int b, const int tb, const int te_in, const int slot) {
+    const int te = min(te_in, seqlens[b]);
     const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
     // end of the tokens this lane's query row sees: te, or for a causal problem the
     // first L - (q_len - 1 - i) tokens of the sequence (row = i * num_heads + h)
@@ -555,6 +556,90 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       }
     }
     __syncthreads();
+  };
+
+  if constexpr (!DEV) {
+    const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
+    for (int pi = p_begin; pi < p_end; ++pi)
+      run_piece(pieces[4 * pi + 0], pieces[4 * pi + 1], pieces[4 * pi + 2], pieces[4 * pi + 3]);
+    return;
+  } else {
+    // ---- device schedule.  The batch's 16-token blocks, sequence after sequence, form
+    // one range [0, T); with W = min(num_workers, T / kMinBlocks) (at least 1), work-group
+    // w < W takes blocks [floor(wT/W), floor((w+1)T/W)) and cuts them at sequence
+    // boundaries.  A sequence met by several work-groups is split: its piece in work-group
+    // w writes partial slot 2w (when the sequence began before w's range) or 2w + 1 (when
+    // it begins inside it, so at most one piece per slot), and merge_dev_kernel combines
+    // them in the next launch from the cut each sequence's first piece records.
+    const int B = a.batch;
+    const int cap = a.bt_stride * a.page_size;            // tokens one block-table row maps
+    auto seq_len = [&](int bb) { return max(0, min(seqlens[bb], cap)); };
+    auto seq_blocks = [&](int bb) { return (seq_len(bb) + kBlock - 1) / kBlock; };
+    // block prefix over the batch: each thread sums a contiguous chunk, then an inclusive
+    // scan of the 256 chunk sums (the LDS stages are not in use yet)
+    LDS_AS int32_t* sums = (LDS_AS int32_t*)smem;         // [2][256]
+    const int per = (B + kThreads - 1) / kThreads;
+    const int c0 = min(B, (int)threadIdx.x * per), c1 = min(B, c0 + per);
+    int mine = 0;
+    for (int bb = c0; bb < c1; ++bb) mine += (max(0, min(a.seqlens[bb], cap)) + kBlock - 1) / kBlock;
+    sums[threadIdx.x] = mine;
+    __syncthreads();
+    int src = 0;
+    for (int d = 1; d < kThreads; d <<= 1) {
+      const int v = sums[src * kThreads + threadIdx.x] +
+                    ((int)threadIdx.x >= d ? sums[src * kThreads + threadIdx.x - d] : 0);
+      sums[(src ^ 1) * kThreads + threadIdx.x] = v;
+      __syncthreads();
+      src ^= 1;
+    }
+    const int64_t T = sums[src * kThreads + kThreads - 1];
+    // at least kMinBlocks blocks per work-group (one per wave): short batches use fewer
+    const int W = (int)max<int64_t>(1, min<int64_t>(a.num_workers, T / kMinBlocks));
+    const int64_t s0 = worker < W ? T * worker / W : T, e0 = worker < W ? T * (worker + 1) / W : T;
+    // the chunk holding block s0, then the sequence in it (uniform: every lane computes it)
+    int ch = 0;
+    for (int lo = 0, hi = kThreads - 1; lo < hi;) {
+      const int mid = (lo + hi) >> 1;
+      if (sums[src * kThreads + mid] > s0) hi = mid; else lo = mid + 1;
+      ch = lo;
+    }
+    int64_t pre = ch > 0 ? sums[src * kThreads + ch - 1] : 0;   // blocks before chunk ch
+    __syncthreads();                                       // the stages may overwrite sums now
+    int bcur = min(B, ch * per);
+    while (bcur < B && pre + seq_blocks(bcur) <= s0) pre += seq_blocks(bcur++);
+    // worker holding block x of the range (the largest w with floor(wT/W) <= x)
+    auto wpos = [&](int64_t x) { return (int)(((x + 1) * W - 1) / T); };
+    auto wstart = [&](int w) { return T * w / W; };
+    for (; bcur < B && pre < e0; pre += seq_blocks(bcur++)) {
+      const int64_t p0 = pre, p1 = pre + seq_blocks(bcur);
+      if (p1 == p0) continue;                              // empty: handled below
+      const int64_t lo = max(p0, s0), hi = min(p1, e0);
+      const bool split = p0 < s0 || p1 > e0;
+      const int slot = split ? 2 * worker + (p0 > s0 ? 1 : 0) : -1;
+      if (lo == p0 && rgroup == 0 && threadIdx.x == 0) {
+        // the sequence's first piece records how it was cut, for the merge launch
+        const int wf = wpos(p0), wl = wpos(p1 - 1);
+        int4 info = {split ? wf : -1, wl, p0 > wstart(wf) ? 1 : 0, 0};
+        *(int4*)(a.seq_info + 4 * bcur) = info;
+      }
+      run_piece(bcur, (int)(lo - p0) * kBlock, (int)(hi - p0) * kBlock, slot);
+    }
+    if (worker == 0 && rgroup == 0 && threadIdx.x == 0) {
+      a.seq_info[4 * B + 0] = (int32_t)T;                 // schedule header: T and W
+      a.seq_info[4 * B + 1] = W;
+    }
+    // empty sequences: work-group w < W writes those with index = w (mod W)
+    for (int bb = worker; worker < W && bb < B; bb += W) {
+      if (seq_blocks(bb) != 0) continue;
+      if (rgroup == 0 && threadIdx.x == 0) *(int4*)(a.seq_info + 4 * bb) = int4{-1, -1, 0, 0};
+      const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+      const int64_t off = ((int64_t)bb * R + row0 + r) * kDv + 32 * c;
+      for (int i = 0; i < 32; ++i) {
+        if (OUT_F32) ((float*)a.out)[off + i] = 0.f;
+        else ((uint16_t*)a.out)[off + i] = 0;
+      }
+      if (c == 0 && a.lse) a.lse[(int64_t)bb * R + row0 + r] = -INFINITY;
+    }
   }
 }
 
@@ -834,7 +919,6 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
 // all of the sequence's partial results, so every partial byte is read once and
 // all loads of a thread are independent.
 constexpr int kMergeCols = 64;
-constexpr int kMergeBatch = 8;
 template <bool OUT_F32>
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   const int R = a.rows;
@@ -893,6 +977,73 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   if (cg == 0 && (threadIdx.x & 15) == 0 && a.lse) a.lse[(int64_t)b * R + r] = L > 0.f ? M + __logf(L) : -INFINITY;
 }
 
+// Merge for the device schedule: one work-group per (sequence, 16 rows, 64 columns), as
+// merge_kernel, with the sequence's pieces taken from the cut its first piece recorded
+// (seq_info[b] = {first work-group or -1 if not split, last work-group, 1 if the first
+// piece starts inside its work-group's range}; seq_info[4B..4B+1] = T, W).
+template <bool OUT_F32>
+__global__ void __launch_bounds__(256) merge_dev_kernel(MergeArgs a) {
+  const int R = a.rows;
+  const int col_groups = kDv / kMergeCols;
+  const int per_seq = (R / 16) * col_groups;
+  const int b = blockIdx.x / per_seq;
+  const int rem = blockIdx.x % per_seq;
+  const int rg = rem / col_groups, cg = rem % col_groups;
+  const CST_AS int32_t* info = as_const(a.seq_info);
+  const int wf = info[4 * b + 0], wl = info[4 * b + 1], first_inside = info[4 * b + 2];
+  if (wf < 0) return;
+  const int64_t T = info[4 * a.batch + 0];
+  const int W = info[4 * a.batch + 1];
+  auto wstart = [&](int w) { return T * w / W; };
+  auto slot_of = [&](int w) -> int {
+    return wstart(w + 1) > wstart(w) ? 2 * w + (w == wf ? first_inside : 0) : -1;
+  };
+  const int r = rg * 16 + (threadIdx.x >> 4);
+  const int d = cg * kMergeCols + 4 * (threadIdx.x & 15);
+  float M = -INFINITY;
+  for (int w0 = wf; w0 <= wl; w0 += kMergeBatch) {
+    float l[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int sl = w0 + u <= wl ? slot_of(w0 + u) : -1;
+      l[u] = sl >= 0 ? a.part_lse[(int64_t)sl * R + r] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) M = fmaxf(M, l[u]);
+  }
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M > -INFINITY) {
+    for (int w0 = wf; w0 <= wl; w0 += kMergeBatch) {
+      float l[kMergeBatch];
+      f32x4_t v[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int sl = w0 + u <= wl ? slot_of(w0 + u) : -1;
+        l[u] = sl >= 0 ? a.part_lse[(int64_t)sl * R + r] : -INFINITY;
+        v[u] = sl >= 0 ? *(const f32x4_t*)(a.part_o + ((int64_t)sl * R + r) * kDv + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float w = (l[u] > -INFINITY) ? __expf(l[u] - M) : 0.f;
+        L += w;
+        acc += w * v[u];
+      }
+    }
+  }
+  const f32x4_t v = acc * (L > 0.f ? 1.0f / L : 0.f);
+  const int64_t off = ((int64_t)b * R + r) * kDv + d;
+  if (OUT_F32) {
+    *(f32x4_t*)((float*)a.out + off) = v;
+  } else {
+    u32x2_t pkd;
+    pkd[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+    pkd[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+    *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
+  }
+  if (cg == 0 && (threadIdx.x & 15) == 0 && a.lse) a.lse[(int64_t)b * R + r] = L > 0.f ? M + __logf(L) : -INFINITY;
+}
+
 // Debug gather: one thread per 16-B chunk of a sequence's logical rows (row_bytes per row).
 __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* kv, const int32_t* block_table, uint8_t* rows_out,
                                                      int32_t seq, int32_t length, int64_t row_offset,
@@ -908,21 +1059,48 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* kv, const in
   *(u32x4_t*)(rows_out + (row_offset + t) * row_bytes + 16 * c) = *(const u32x4_t*)(kv + row * row_bytes + 16 * c);
 }
 
+
+template <bool DEV>
+void launch_split(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
+  if (a.kv_fp8) {
+    if (out_fp32)
+      hipLaunchKernelGGL((split_decode_kernel<true, true, DEV>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((split_decode_kernel<false, true, DEV>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else {
+    if (out_fp32)
+      hipLaunchKernelGGL((split_decode_kernel<true, false, DEV>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((split_decode_kernel<false, false, DEV>), dim3(grid), dim3(kThreads), 0, s, a);
+  }
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 }  // namespace
 
-int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream) {
+int launch_fill_zero(void* p, size_t bytes, void* stream) {
+  const int64_t n = (int64_t)(bytes / 4);
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     (uint32_t*)p, n);
+  return (int)hipGetLastError();
+}
+
+int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream,
+                  bool device_schedule) {
   hipStream_t s = (hipStream_t)stream;
-  if (a.kv_fp8) {
+  if (device_schedule || a.kv_fp8) {
     if (rows_per_group != 16) return (int)hipErrorInvalidValue;
-    if (out_fp32)
-      hipLaunchKernelGGL((split_decode_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, a);
+    if (device_schedule)
+      launch_split<true>(a, out_fp32, grid, s);
     else
-      hipLaunchKernelGGL((split_decode_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      launch_split<false>(a, out_fp32, grid, s);
   } else if (rows_per_group == 16) {
-    if (out_fp32)
-      hipLaunchKernelGGL((split_decode_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((split_decode_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    launch_split<false>(a, out_fp32, grid, s);
   } else if (rows_per_group == 32) {
     if (out_fp32)
       hipLaunchKernelGGL((group_decode_kernel<2, true>), dim3(grid), dim3(kThreads), 0, s, a);
@@ -936,6 +1114,17 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
   } else {
     return (int)hipErrorInvalidValue;
   }
+  return (int)hipGetLastError();
+}
+
+int launch_merge_dev(const MergeArgs& a, bool out_fp32, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int grid = a.batch * (a.rows / 16) * (kDv / kMergeCols);
+  if (grid == 0) return 0;
+  if (out_fp32)
+    hipLaunchKernelGGL((merge_dev_kernel<true>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((merge_dev_kernel<false>), dim3(grid), dim3(256), 0, s, a);
   return (int)hipGetLastError();
 }
 

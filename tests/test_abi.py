@@ -126,3 +126,26 @@ def test_workspace_layout_scales_with_partials():
     R = 16
     assert info["workspace_bytes"] >= info["metadata_bytes"] + info["num_partials"] * R * (512 + 1) * 4
     assert info["workspace_bytes"] % 256 == 0
+
+
+def test_devplan_validation():
+    lib = B.lib()
+    prob = B.make_problem(2, 1, 16, 64, 4, 2)
+    assert lib.mla_devplan_workspace_bytes(C.byref(prob), 256) > 0
+    assert lib.mla_devplan_workspace_bytes(C.byref(prob), -1) == 0
+    bad = B.make_problem(2, 1, 8, 64, 4, 2)                 # R = 8
+    assert lib.mla_devplan_workspace_bytes(C.byref(bad), 256) == 0
+    n = lib.mla_devplan_workspace_bytes(C.byref(prob), 256)
+    fake = 1 << 20
+    # nothing launched for bad arguments (no device here)
+    assert lib.mla_devplan_prepare(C.byref(prob), 256, None, n, None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_devplan_prepare(C.byref(prob), 256, fake, n - 1, None) == B.MLA_ERR_WORKSPACE_TOO_SMALL
+    call = lambda **o: lib.mla_decode_devplan(
+        C.byref(prob), o.get("w", 256), o.get("q", fake), fake, fake, fake, C.c_float(o.get("scale", 0.1)),
+        fake, fake, o.get("ws", fake), o.get("n", n), None)
+    assert call(q=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(q=fake + 8) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(ws=fake + 64) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(n=n - 256) == B.MLA_ERR_WORKSPACE_TOO_SMALL
+    assert call(scale=float("nan")) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(w=-3) == B.MLA_ERR_INVALID_ARGUMENT

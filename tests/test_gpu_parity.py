@@ -200,6 +200,21 @@ def test_more_query_rows(heads, q_len):
     compare(out, lse, ref_o, ref_l, what=f"H={heads} S_q={q_len}")
 
 
+@pytest.mark.parametrize("heads,q_len,rpg", [(16, 2, 32), (32, 1, 32), (64, 1, 64), (128, 1, 64), (16, 4, 64),
+                                          (64, 2, 64)])
+@pytest.mark.parametrize("out_fp32", [True, False])
+def test_grouped_kernel(heads, q_len, rpg, out_fp32):
+    """The grouped kernel (32 or 64 rows per work-group), asked for through the plan option."""
+    prob = gen.make_problem(batch=4, q_len=q_len, num_heads=heads, page_size=64, lengths=[700, 2000, 33, 1],
+                            seed=18, tail="nan", extra_pages=1, out_fp32=out_fp32)
+    r = Runner(prob, rows_per_group=rpg)
+    assert r.plan.info()["rows_per_group"] == rpg
+    r()
+    out, lse = r.results()
+    ref_o, ref_l = oracle(prob)
+    check_short_contexts(out, lse, ref_o, ref_l, out_fp32, f"grouped H={heads} S_q={q_len} rpg={rpg}")
+
+
 def test_two_token_query_equals_two_single_token_calls():
     prob = gen.make_problem(batch=2, q_len=2, num_heads=16, page_size=64, lengths=[1500, 300], seed=12,
                             out_fp32=True)

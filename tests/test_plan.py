@@ -66,7 +66,7 @@ def test_plan_covers_every_token_once(name):
         plan = make_plan(lens, heads=heads, q_len=q_len)
         seg, off, info = check_plan(plan, lens)
         R = heads * q_len
-        assert info["rows_per_group"] == (64 if R % 64 == 0 else 32 if R == 32 else 16)
+        assert info["rows_per_group"] == 16
         assert info["row_groups"] == R // info["rows_per_group"]
         workers = 256 // info["row_groups"]
         assert info["num_workers"] <= max(1, workers)
@@ -118,3 +118,21 @@ def test_grid_padding_for_row_groups():
     assert info["row_groups"] == 3 and info["rows_per_group"] == 16
     assert info["grid_size"] % 8 == 0
     assert info["grid_size"] == ((info["num_workers"] + 7) // 8 * 8) * 3
+
+
+@pytest.mark.parametrize("heads,q_len,rpg", [(32, 1, 32), (64, 1, 64), (16, 4, 64), (128, 1, 32)])
+def test_forced_rows_per_group(heads, q_len, rpg):
+    lens = [5000, 300]
+    maxp = max((l + 63) // 64 for l in lens)
+    prob = B.make_problem(len(lens), q_len, heads, 64, sum((l + 63) // 64 for l in lens), maxp)
+    plan = B.Plan(prob, lens, num_cus=256, rows_per_group=rpg)
+    seg, off, info = check_plan(plan, lens)
+    assert info["rows_per_group"] == rpg and info["row_groups"] == heads * q_len // rpg
+
+
+def test_rows_per_group_rejected():
+    prob = B.make_problem(1, 1, 16, 64, 1, 1)
+    with pytest.raises(B.MlaError):
+        B.Plan(prob, [10], num_cus=256, rows_per_group=32)      # R = 16 is not a multiple of 32
+    with pytest.raises(B.MlaError):
+        B.Plan(prob, [10], num_cus=256, rows_per_group=24)
