@@ -216,3 +216,35 @@ def make_config(name: str, seed=None, **overrides) -> Problem:
     if seed is None:
         seed = CONFIG_ORDER.index(name)
     return make_problem(seed=seed, name=name, **cfg)
+
+
+# ---------------------------------------------------------------------------- the layer around
+D_NOPE = 128            # per-head query/key columns that are not rotary (before absorption)
+D_ROPE = 64
+D_VOUT = 128            # per-head value width after the up-projection
+
+
+@dataclass
+class LayerInputs:
+    """Inputs of the steps on either side of the decode (bf16 bit patterns)."""
+    q_nope: np.ndarray   # [B, S_q, H, 128]
+    q_pe: np.ndarray     # [B, S_q, H, 64]   (before rotary embedding)
+    c_kv: np.ndarray     # [B, S_q, 512]     the new tokens' latent rows
+    k_pe: np.ndarray     # [B, S_q, 64]      their rope columns, before rotary embedding
+    w_uk: np.ndarray     # [H, 512, 128]     key up-projection, row e = latent column e
+    w_uv: np.ndarray     # [H, 128, 512]     value up-projection
+
+
+def make_layer_inputs(batch: int, q_len: int, num_heads: int, *, seed: int = 0) -> LayerInputs:
+    """N(0,1) activations; weights N(0, 1/fan_in) so the projected values are O(1).
+    Draw order: q_nope, q_pe, c_kv, k_pe, w_uk, w_uv."""
+    rng = np.random.default_rng(seed)
+    q_nope = _normal_bf16(rng, batch * q_len * num_heads * D_NOPE).reshape(batch, q_len, num_heads, D_NOPE)
+    q_pe = _normal_bf16(rng, batch * q_len * num_heads * D_ROPE).reshape(batch, q_len, num_heads, D_ROPE)
+    c_kv = _normal_bf16(rng, batch * q_len * D_V).reshape(batch, q_len, D_V)
+    k_pe = _normal_bf16(rng, batch * q_len * D_ROPE).reshape(batch, q_len, D_ROPE)
+    w_uk = f32_to_bf16_bits(rng.standard_normal((num_heads, D_V, D_NOPE), dtype=np.float32)
+                            * np.float32(1.0 / math.sqrt(D_NOPE)))
+    w_uv = f32_to_bf16_bits(rng.standard_normal((num_heads, D_VOUT, D_V), dtype=np.float32)
+                            * np.float32(1.0 / math.sqrt(D_V)))
+    return LayerInputs(q_nope=q_nope, q_pe=q_pe, c_kv=c_kv, k_pe=k_pe, w_uk=w_uk, w_uv=w_uv)
