@@ -26,8 +26,10 @@ encoding):
 * The new token's cache row: [c (512 latent), rope(k_pe, pos) (64)] stored at
   row pos % P of page block_table[b][pos // P]; in the fp8 layout the latent
   group g (columns 128g..128g+127) is stored as E4M3 codes of x / 2^e_g with
-  e_g the smallest integer such that max|x| <= 448 * 2^e_g (e_g = 0 for an
-  all-zero group), rounded to nearest even, and the scale 2^e_g as float32.
+  e_g the smallest integer >= -126 such that max|x| <= 448 * 2^e_g (e_g = 0 for
+  an all-zero group), rounded to nearest even, and the scale 2^e_g as float32.
+  The lower limit keeps every scale a normal float32: a row's reader uses only
+  the exponent field of a scale.
 
 Weight layouts (this library's): W_UK as [H, 512, 128] (row e of head h maps
 the 128 nope columns to latent column e), W_UV as [H, 128, 512].
@@ -77,9 +79,11 @@ def out_absorb(out_latent, w_uv):
 
 
 def fp8_group_exponent(amax: float) -> int:
-    """Smallest integer e with amax <= 448 * 2^e (0 for amax == 0)."""
+    """Smallest integer e >= -126 with amax <= 448 * 2^e (0 for amax == 0)."""
     if amax == 0.0:
         return 0
+    if amax <= 448.0 * 2.0 ** -126:
+        return -126
     e = int(np.ceil(np.log2(amax / 448.0)))
     while 448.0 * 2.0 ** (e - 1) >= amax:        # guard the log against rounding
         e -= 1

@@ -8,7 +8,7 @@
                      values (the low-rank compression of the FlashMLA-on-Ascend post).
   fp8 encoding    -- the E4M3 encoder against torch's float8_e4m3fn, every finite code
                      round-trips, ties go to the even code; the group exponent is the
-                     smallest e with max|x| <= 448 * 2^e.
+                     smallest e >= -126 with max|x| <= 448 * 2^e.
   append          -- the latent part of a bf16 row is the input bits; an fp8 row decodes
                      to the input within half an E4M3 step; the row lands in its page.
 """
@@ -77,7 +77,8 @@ def fp8_encoding_pins(encode, group_exponent):
     assert np.array_equal(encode(vals[fin]), codes[fin])
     # ties: the midpoint of 1.0 (0x38, even) and 1.125 (0x39) rounds to 1.0; of 1.125 and 1.25 to 1.25
     assert encode(np.array([1.0625]))[0] == 0x38 and encode(np.array([1.1875]))[0] == 0x3A
-    for amax, e in ((448.0, 0), (448.0001, 1), (224.0, -1), (224.5, 0), (1.0, -8), (1.75, -8), (1.76, -7), (0.0, 0)):
+    for amax, e in ((448.0, 0), (448.0001, 1), (224.0, -1), (224.5, 0), (1.0, -8), (1.75, -8), (1.76, -7), (0.0, 0),
+                    (2.0 ** -130, -126), (448.0 * 2.0 ** -126, -126), (2.0 ** -117, -125)):
         assert group_exponent(amax) == e, (amax, group_exponent(amax), e)
 
 
