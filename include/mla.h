@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 
 typedef enum {
   MLA_OK = 0,
@@ -218,6 +218,58 @@ mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_worker
                                 const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
                                 float softmax_scale, void* out, float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* ---- The steps on either side of the decode (an absorbed MLA attention layer).
+ *
+ * Low-rank joint KV compression (FlashMLA-on-Ascend post, the compression principle and its
+ * computation flow): with the shared latent rows c_t, head h's keys and values are
+ * K_h = c W_UK[h] and V_h = c W_UV[h].  The decode above runs on the absorbed form
+ * (FlashMLA-ETAP summary, "Implementation details"): W_UK is folded into the query and W_UV
+ * is applied to the decode's 512-wide latent output, which gives the same attention as the
+ * decompressed keys and values.  Per head: 128 query columns before absorption, 64 rotary
+ * columns, 128 output columns.
+ *
+ * Rotary embedding (the pages do not spell out its form; this library's reading): the 64
+ * rope columns x rotate in consecutive pairs, (x[2i], x[2i+1]) by the angle
+ * pos * rope_base^(-2i/64), evaluated in float64 and rounded once to bf16.
+ *
+ * Token n = b * q_len + s; positions [B, q_len] int32 on the device gives each new token's
+ * position in its sequence (for the decode's causal reading, L_b - q_len + s with L_b
+ * counting the new tokens).  `problem` is the decode problem these calls surround, checked
+ * as mla_plan checks it.  Every pointer is a device address; launches are asynchronous on
+ * `stream`; nothing is allocated. */
+
+/* Query preparation: q_out[n][h] = [W_UK[h] q_nope[n][h] (512), rope(q_pe[n][h], positions[n]) (64)].
+ *   q_nope [B, q_len, H, 128] bf16, 16-B aligned     q_pe [B, q_len, H, 64] bf16, 4-B aligned
+ *   w_uk   [H, 512, 128] bf16 (row e of head h maps the 128 query columns to latent column e)
+ *   q_out  [B, q_len, H, 576] bf16, the decode's q; latent columns are fp32 sums rounded to
+ *          nearest even. */
+mla_status_t mla_q_absorb(const mla_problem_t* problem, const void* q_nope, const void* q_pe, const void* w_uk,
+                          const int32_t* positions, float rope_base, void* q_out, void* stream);
+
+/* Cache append: writes new token n's row at row positions[n] % page_size of page
+ * block_table[b][positions[n] / page_size], in problem->kv_dtype's layout:
+ *   bf16: [c_kv[n] (512, copied bit for bit), rope(k_pe[n], positions[n]) (64)];
+ *   fp8:  latent group g (columns 128g .. 128g+127) as E4M3 codes (nearest, ties to even) of
+ *         x / 2^e_g, e_g the smallest integer >= -126 with max|x| <= 448 * 2^e_g (0 for an
+ *         all-zero group), scale 2^e_g stored as float32; rope columns as for bf16.
+ *   c_kv [B, q_len, 512] bf16, 16-B aligned        k_pe [B, q_len, 64] bf16, 4-B aligned
+ *   block_table [B, max_pages_per_seq] int32; kv_cache as for mla_decode.
+ * A token whose position is outside [0, max_pages_per_seq * page_size) or whose page entry is
+ * outside [0, num_pages) is not written, and bit 1 of *status is set (status: a device int32,
+ * or NULL).  Two tokens with the same row race. */
+mla_status_t mla_kv_append(const mla_problem_t* problem, const void* c_kv, const void* k_pe,
+                           const int32_t* positions, const int32_t* block_table, float rope_base, void* kv_cache,
+                           int32_t* status, void* stream);
+
+/* Output projection: o[n][h] = W_UV[h] out_latent[n][h].
+ *   out_latent [B, q_len, H, 512] of problem->out_dtype (mla_decode's out), 16-B aligned
+ *   w_uv       [H, 128, 512] bf16 (row v of head h maps the latent columns to output column v)
+ *   o          [B, q_len, H, 128] of problem->out_dtype, 16-B aligned
+ * Products are summed in float32 on bf16 matrix cores; a float32 out_latent enters as
+ * bf16(x) + bf16(x - bf16(x)), about 16 significant bits. */
+mla_status_t mla_out_absorb(const mla_problem_t* problem, const void* out_latent, const void* w_uv, void* o,
+                            void* stream);
 
 /* Read the workspace status word (synchronises `stream`).  Bit 0: a block_table
  * entry was out of range in some mla_decode since the last mla_plan_upload. */

@@ -77,6 +77,11 @@ _SIGS = {
     "mla_decode_devplan": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                      C.c_void_p]),
+    "mla_q_absorb": (C.c_int, [C.POINTER(mla_problem_t), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                               C.c_float, C.c_void_p, C.c_void_p]),
+    "mla_kv_append": (C.c_int, [C.POINTER(mla_problem_t), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                C.c_float, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "mla_out_absorb": (C.c_int, [C.POINTER(mla_problem_t), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "mla_plan_destroy": (None, [C.c_void_p]),
     "mla_status_string": (C.c_char_p, [C.c_int]),
     "mla_last_error": (C.c_char_p, []),
@@ -327,6 +332,47 @@ def mla_read_status(workspace, stream=None) -> int:
     v = C.c_int32(0)
     _check(lib().mla_read_status(_ptr(workspace), _stream(stream), C.byref(v)), "mla_read_status")
     return v.value
+
+
+def mla_q_absorb(problem: mla_problem_t, q_nope, q_pe, w_uk, positions, rope_base, q_out, stream=None):
+    """Query preparation: q_out = [W_UK q_nope, rope(q_pe)] per token and head."""
+    import torch
+    p = problem
+    _require(q_nope, "q_nope", (torch.bfloat16,), (p.batch, p.q_len, p.num_heads, 128))
+    _require(q_pe, "q_pe", (torch.bfloat16,), (p.batch, p.q_len, p.num_heads, 64))
+    _require(w_uk, "w_uk", (torch.bfloat16,), (p.num_heads, 512, 128))
+    _require(positions, "positions", (torch.int32,), (p.batch, p.q_len))
+    _require(q_out, "q_out", (torch.bfloat16,), (p.batch, p.q_len, p.num_heads, 576))
+    _check(lib().mla_q_absorb(C.byref(p), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(positions),
+                              float(rope_base), _ptr(q_out), _stream(stream)), "mla_q_absorb")
+
+
+def mla_kv_append(problem: mla_problem_t, c_kv, k_pe, positions, block_table, rope_base, kv_cache, status=None,
+                  stream=None):
+    """Write the new tokens' cache rows (bf16 or fp8 layout, as problem.kv_dtype)."""
+    import torch
+    p = problem
+    _require(c_kv, "c_kv", (torch.bfloat16,), (p.batch, p.q_len, 512))
+    _require(k_pe, "k_pe", (torch.bfloat16,), (p.batch, p.q_len, 64))
+    _require(positions, "positions", (torch.int32,), (p.batch, p.q_len))
+    _require(block_table, "block_table", (torch.int32,), (p.batch, p.max_pages_per_seq))
+    _require(kv_cache, "kv_cache", *_kv_spec(p))
+    if status is not None:
+        _require(status, "status", (torch.int32,), (1,))
+    _check(lib().mla_kv_append(C.byref(p), _ptr(c_kv), _ptr(k_pe), _ptr(positions), _ptr(block_table),
+                               float(rope_base), _ptr(kv_cache), _ptr(status), _stream(stream)), "mla_kv_append")
+
+
+def mla_out_absorb(problem: mla_problem_t, out_latent, w_uv, o, stream=None):
+    """Output projection: o = W_UV out_latent per token and head (dtype: problem.out_dtype)."""
+    import torch
+    p = problem
+    odt = torch.float32 if p.out_dtype == MLA_DTYPE_FP32 else torch.bfloat16
+    _require(out_latent, "out_latent", (odt,), (p.batch, p.q_len, p.num_heads, 512))
+    _require(w_uv, "w_uv", (torch.bfloat16,), (p.num_heads, 128, 512))
+    _require(o, "o", (odt,), (p.batch, p.q_len, p.num_heads, 128))
+    _check(lib().mla_out_absorb(C.byref(p), _ptr(out_latent), _ptr(w_uv), _ptr(o), _stream(stream)),
+           "mla_out_absorb")
 
 
 def alloc_workspace(plan: Plan, device="cuda"):

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla.so")
 
-SOURCES = ["mla_api.cpp", "plan.cpp", "mla_kernels.hip"]
+SOURCES = ["mla_api.cpp", "plan.cpp", "mla_kernels.hip", "mla_layer_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -398,6 +398,86 @@ mla_status_t mla_read_status(const void* workspace, void* stream, int32_t* statu
   return MLA_OK;
 }
 
+mla_status_t mla_q_absorb(const mla_problem_t* problem, const void* q_nope, const void* q_pe, const void* w_uk,
+                          const int32_t* positions, float rope_base, void* q_out, void* stream) {
+  mla_status_t s = check_problem(problem);
+  if (s != MLA_OK) return s;
+  if (!q_nope || !q_pe || !w_uk || !positions || !q_out)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if ((uintptr_t)q_nope % 16 || (uintptr_t)w_uk % 16 || (uintptr_t)q_out % 16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "q_nope, w_uk and q_out must be 16-B aligned");
+  if ((uintptr_t)q_pe % 4 || (uintptr_t)positions % 4)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "q_pe and positions must be 4-B aligned");
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "rope_base must be a finite positive number");
+  mla::LayerArgs a{};
+  a.batch = problem->batch;
+  a.q_len = problem->q_len;
+  a.num_heads = problem->num_heads;
+  a.rope_base = rope_base;
+  a.q_nope = q_nope;
+  a.q_pe = q_pe;
+  a.w_uk = w_uk;
+  a.positions = positions;
+  a.q_out = q_out;
+  int e = mla::launch_q_absorb(a, stream);
+  if (e) return fail(MLA_ERR_HIP, "query absorption launch: %s", mla::hip_error_string(e));
+  return MLA_OK;
+}
+
+mla_status_t mla_kv_append(const mla_problem_t* problem, const void* c_kv, const void* k_pe,
+                           const int32_t* positions, const int32_t* block_table, float rope_base, void* kv_cache,
+                           int32_t* status, void* stream) {
+  mla_status_t s = check_problem(problem);
+  if (s != MLA_OK) return s;
+  if (!c_kv || !k_pe || !positions || !block_table || !kv_cache)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if ((uintptr_t)c_kv % 16 || (uintptr_t)kv_cache % 16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "c_kv and kv_cache must be 16-B aligned");
+  if ((uintptr_t)k_pe % 4 || (uintptr_t)positions % 4 || (uintptr_t)block_table % 4 || (uintptr_t)status % 4)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "k_pe, positions, block_table and status must be 4-B aligned");
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "rope_base must be a finite positive number");
+  mla::LayerArgs a{};
+  a.batch = problem->batch;
+  a.q_len = problem->q_len;
+  a.num_heads = problem->num_heads;
+  a.page_size = problem->page_size;
+  a.num_pages = problem->num_pages;
+  a.max_pages_per_seq = problem->max_pages_per_seq;
+  a.kv_fp8 = problem->kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
+  a.rope_base = rope_base;
+  a.c_kv = c_kv;
+  a.k_pe = k_pe;
+  a.positions = positions;
+  a.block_table = block_table;
+  a.kv_cache = kv_cache;
+  a.status = status;
+  int e = mla::launch_kv_append(a, stream);
+  if (e) return fail(MLA_ERR_HIP, "cache append launch: %s", mla::hip_error_string(e));
+  return MLA_OK;
+}
+
+mla_status_t mla_out_absorb(const mla_problem_t* problem, const void* out_latent, const void* w_uv, void* o,
+                            void* stream) {
+  mla_status_t s = check_problem(problem);
+  if (s != MLA_OK) return s;
+  if (!out_latent || !w_uv || !o) return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if ((uintptr_t)out_latent % 16 || (uintptr_t)w_uv % 16 || (uintptr_t)o % 16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "out_latent, w_uv and o must be 16-B aligned");
+  mla::LayerArgs a{};
+  a.batch = problem->batch;
+  a.q_len = problem->q_len;
+  a.num_heads = problem->num_heads;
+  a.out_latent = out_latent;
+  a.w_uv = w_uv;
+  a.o = o;
+  const bool f32 = problem->out_dtype == MLA_DTYPE_FP32;
+  int e = mla::launch_out_absorb(a, f32, f32, stream);
+  if (e) return fail(MLA_ERR_HIP, "output projection launch: %s", mla::hip_error_string(e));
+  return MLA_OK;
+}
+
 void mla_plan_destroy(mla_plan_t plan) { delete plan; }
 
 }  // extern "C"

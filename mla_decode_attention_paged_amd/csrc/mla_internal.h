@@ -100,6 +100,31 @@ struct MergeArgs {
   int32_t batch;
 };
 
+// Parameters of the steps around the decode (mla_layer_kernels.hip).
+struct LayerArgs {
+  int32_t batch, q_len, num_heads;
+  int32_t page_size, num_pages, max_pages_per_seq;   // kv append
+  int32_t kv_fp8;
+  float rope_base;
+  const void* q_nope;            // [B, q_len, H, 128] bf16
+  const void* q_pe;              // [B, q_len, H, 64] bf16
+  const void* w_uk;              // [H, 512, 128] bf16
+  const int32_t* positions;      // [B, q_len]
+  void* q_out;                   // [B, q_len, H, 576] bf16
+  const void* c_kv;              // [B, q_len, 512] bf16
+  const void* k_pe;              // [B, q_len, 64] bf16
+  const int32_t* block_table;
+  void* kv_cache;
+  int32_t* status;               // may be null
+  const void* out_latent;        // [B, q_len, H, 512] bf16 or fp32
+  const void* w_uv;              // [H, 128, 512] bf16
+  void* o;                       // [B, q_len, H, 128] bf16 or fp32
+};
+
+int launch_q_absorb(const LayerArgs& a, void* stream);
+int launch_kv_append(const LayerArgs& a, void* stream);
+int launch_out_absorb(const LayerArgs& a, bool in_f32, bool out_f32, void* stream);
+
 // Kernel launchers (mla_kernels.hip).  Return a HIP error code (0 = success).
 int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream,
                   bool device_schedule = false);

@@ -87,3 +87,12 @@ class DevplanRunner:
         import torch
         torch.cuda.synchronize()
         return self.out.float().cpu().numpy().astype(np.float64), self.lse.cpu().numpy().astype(np.float64)
+
+
+def layer_to_device(li, device="cuda"):
+    """Host LayerInputs (see inputs.py) -> dict of contiguous bf16 device tensors."""
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return {k: bf(getattr(li, k)) for k in ("q_nope", "q_pe", "c_kv", "k_pe", "w_uk", "w_uv")}

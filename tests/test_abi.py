@@ -23,7 +23,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) >= 12
     for n in names:
         assert hasattr(lib, n), f"libmla.so does not export {n}"
-    assert B.abi_version() == 3
+    assert B.abi_version() == 4
 
 
 def test_status_strings():
@@ -149,3 +149,34 @@ def test_devplan_validation():
     assert call(n=n - 256) == B.MLA_ERR_WORKSPACE_TOO_SMALL
     assert call(scale=float("nan")) == B.MLA_ERR_INVALID_ARGUMENT
     assert call(w=-3) == B.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_layer_step_validation():
+    """Query preparation, cache append and output projection reject bad arguments before any launch."""
+    lib = B.lib()
+    prob = B.make_problem(2, 1, 16, 64, 4, 2)
+    fake = 1 << 20
+    qa = lambda **o: lib.mla_q_absorb(
+        C.byref(o.get("p", prob)), o.get("qn", fake), o.get("qp", fake), o.get("w", fake), o.get("pos", fake),
+        C.c_float(o.get("base", 10000.0)), o.get("out", fake), None)
+    assert qa(qn=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert qa(pos=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert qa(qn=fake + 8) == B.MLA_ERR_INVALID_ARGUMENT
+    assert qa(qp=fake + 2) == B.MLA_ERR_INVALID_ARGUMENT
+    assert qa(base=0.0) == B.MLA_ERR_INVALID_ARGUMENT
+    assert qa(base=float("inf")) == B.MLA_ERR_INVALID_ARGUMENT
+    assert qa(p=B.make_problem(2, 1, 8, 64, 4, 2)) == B.MLA_ERR_UNSUPPORTED       # R = 8
+    ap = lambda **o: lib.mla_kv_append(
+        C.byref(o.get("p", prob)), o.get("c", fake), o.get("k", fake), o.get("pos", fake), o.get("bt", fake),
+        C.c_float(o.get("base", 10000.0)), o.get("kv", fake), o.get("st", None), None)
+    assert ap(c=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert ap(bt=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert ap(kv=fake + 4) == B.MLA_ERR_INVALID_ARGUMENT
+    assert ap(st=fake + 2) == B.MLA_ERR_INVALID_ARGUMENT
+    assert ap(base=-1.0) == B.MLA_ERR_INVALID_ARGUMENT
+    assert ap(p=B.make_problem(2, 1, 16, 40, 4, 2)) == B.MLA_ERR_UNSUPPORTED      # page size
+    oa = lambda **o: lib.mla_out_absorb(C.byref(o.get("p", prob)), o.get("lat", fake), o.get("w", fake),
+                                        o.get("o", fake), None)
+    assert oa(lat=None) == B.MLA_ERR_INVALID_ARGUMENT
+    assert oa(o=fake + 8) == B.MLA_ERR_INVALID_ARGUMENT
+    assert oa(w=fake + 2) == B.MLA_ERR_INVALID_ARGUMENT
