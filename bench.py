@@ -98,6 +98,81 @@ def cpu_baseline(prob, budget_s: float = 15.0):
     }
 
 
+ROPE_BASE = 10000.0
+
+
+def layer_bytes(prob) -> dict:
+    """Algorithmic bytes of the steps around the decode (each input and output once)."""
+    n, H = prob.batch * prob.q_len, prob.num_heads
+    out_elem = 4 if prob.out_fp32 else 2
+    row_bytes = 656 if prob.kv_format == "fp8" else 576 * 2
+    return {
+        "q_absorb": H * 512 * 128 * 2 + n * H * (128 + 64) * 2 + n * 4 + n * H * 576 * 2,
+        "kv_append": n * (512 + 64) * 2 + n * 8 + n * row_bytes,
+        "out_absorb": H * 128 * 512 * 2 + n * H * 512 * out_elem + n * H * 128 * out_elem,
+    }
+
+
+def layer_leg(prob, r, reps: int = 20):
+    """Mean device time of each step around the decode, and of one whole layer step
+    (append, query preparation, decode, output projection), from HIP graphs of `reps`
+    back-to-back launches replayed on the current stream (no host time in the figures).
+    Runs after the decode timing: the append rewrites each sequence's last row."""
+    import torch
+    from mla_decode_attention_paged_amd import binding as B
+    from mla_decode_attention_paged_amd import inputs as gen
+    from mla_decode_attention_paged_amd.device import layer_to_device, problem_struct
+    li = gen.make_layer_inputs(prob.batch, prob.q_len, prob.num_heads, seed=prob.seed + 1000)
+    d = layer_to_device(li)
+    p = problem_struct(prob)
+    pos = torch.from_numpy((prob.cache_seqlens[:, None] - prob.q_len
+                            + np.arange(prob.q_len)[None, :]).astype(np.int32)).cuda()
+    odt = torch.float32 if prob.out_fp32 else torch.bfloat16
+    o = torch.empty((prob.batch, prob.q_len, prob.num_heads, 128), dtype=odt, device="cuda")
+    dev = r.dev
+    steps = {
+        "q_absorb": lambda: B.mla_q_absorb(p, d["q_nope"], d["q_pe"], d["w_uk"], pos, ROPE_BASE, dev["q"]),
+        "kv_append": lambda: B.mla_kv_append(p, d["c_kv"], d["k_pe"], pos, dev["block_table"], ROPE_BASE,
+                                             dev["kv_cache"]),
+        "out_absorb": lambda: B.mla_out_absorb(p, r.out, d["w_uv"], o),
+    }
+
+    def whole():
+        steps["kv_append"]()
+        steps["q_absorb"]()
+        r()
+        steps["out_absorb"]()
+    steps["layer_step"] = whole
+    res = {}
+    stream = torch.cuda.current_stream()
+    for name, fn in steps.items():
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e3 / reps)
+        res[name] = float(np.median(times))
+        del g
+    nb = layer_bytes(prob)
+    out = {"us": {k: round(v, 2) for k, v in res.items()},
+           "algorithmic_bytes": nb,
+           "GBps": {k: round(nb[k] / (res[k] * 1e-6) / 1e9, 1) for k in nb},
+           "note": "graph-replayed means over back-to-back launches; the layer step is append + query "
+                   "preparation + decode + output projection"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +182,7 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-layer", action="store_true", help="skip timing the steps around the decode")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="cache row storage: bf16 (1,152 B per token) or fp8 E4M3 rows (656 B per token)")
     args = ap.parse_args()
@@ -181,6 +257,10 @@ def main():
     del flush
 
     status = B.mla_read_status(r.ws)
+    layer = None
+    if not args.no_layer:
+        print("[bench] timing the steps around the decode", file=sys.stderr, flush=True)
+        layer = layer_leg(prob, r)
     value = algo / wall / 1e9
     achieved = algo / (split_us * 1e-6) / 1e9
     traffic = measured_traffic(counters_key)
@@ -218,6 +298,7 @@ def main():
                       "plan_host_us": round(plan_us, 1)},
         "plan": {k: info[k] for k in ("num_workers", "grid_size", "num_segments", "num_partials", "num_combine")},
         "status_word": status,
+        "layer_steps": layer,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
