@@ -51,8 +51,11 @@ constexpr int kF8Row = 656;
 constexpr int kF8Units = kBlock * kF8Row / 16;                 // 656 16-B units per block
 constexpr int kF8Stage = kBlock * kF8Row;                      // 10,496 bytes
 constexpr int kF8Loads = (kF8Units + 63) / 64;                 // 11 DMA instructions per block
-constexpr int kF8WaveBytes = 2 * kF8Stage + kBlockBytes;       // two fp8 stages + one bf16 stage
-constexpr int kSmemFp8 = kWaves * kF8WaveBytes;                // 157,696
+constexpr int kF8Stages = 3;                                   // fp8 stages per wave
+constexpr int kF8WaveBytes = kF8Stages * kF8Stage;             // 31,488
+constexpr int kF8QRow = kDqk * 2 + 16;                         // 1,168: a padded Q row in LDS
+constexpr int kF8QOff = kWaves * kF8WaveBytes;                 // 125,952: Q^T rows after the stages
+constexpr int kSmemFp8 = kF8QOff + kBlock * kF8QRow;           // 144,640
 constexpr int kLoadsPerBlock = kBlockBytes / (64 * 16);      // 18 DMA loads per wave per block
 // Cache policy of the KV-cache DMA loads.  With one row group every KV row is read by one
 // work-group only, and the loads carry the non-temporal bit (`nt`): on MI355X a
@@ -66,6 +69,10 @@ constexpr int kMinBlocks = kWaves;                 // device schedule: fewest bl
 constexpr int kMergeBatch = 8;                     // partial results read at a time when merging
 constexpr float kNegBig = -1.0e30f;                // running-max start value (finite)
 constexpr int kMergeStride = kDv + 4;              // floats per row in the merge buffer
+// the four waves' states when a piece ends: o [4][16][kMergeStride] plus m and l [4][16]
+constexpr int kMergeBytes = kWaves * 16 * (kMergeStride + 2) * 4;   // 132,608
+constexpr int kSplitSmemBf16 = kSmemBytes > kMergeBytes ? kSmemBytes : kMergeBytes;
+constexpr int kSplitSmemFp8 = kSmemFp8 > kMergeBytes ? kSmemFp8 : kMergeBytes;
 
 // Chunk-major block layout of the grouped kernel (16-B units): chunk c of token t sits at
 // 16 * c + (t ^ ((c & 1) * kSwz)).
@@ -192,51 +199,82 @@ __device__ __forceinline__ void lds_read_v16(u32x2_t (&r)[16], LDS_AS const uint
       : "memory");
 }
 
-// Reads of one lane's share of an fp8 stage: 128 latent bytes at pl, 32 rope bytes at pr
-// and a 4-byte group scale at ps.
-__device__ __forceinline__ void lds_read_f8(u32x4_t (&lat)[8], u32x4_t (&rope)[2], uint32_t& scale,
-                                            LDS_AS const uint8_t* pl, LDS_AS const uint8_t* pr,
-                                            LDS_AS const uint8_t* ps) {
+// FP8 stage reads for S^T, lane (t, g): 8 latent codes of token t at pk + 256 * H + 32 * kk
+// (columns 256H + 32kk + 8g .. + 8, kk < 8) and, for H = 0, the token's four group scales at
+// ps; for H = 1, the two rope chunks at pr and pr + 64 (bf16 columns 512 + 32kk' + 8g .. + 8).
+template <int H>
+__device__ __forceinline__ void lds_read_f8k8(u32x2_t (&k)[8], u32x4_t (&x)[2], LDS_AS const uint8_t* pk,
+                                              LDS_AS const uint8_t* pr, LDS_AS const uint8_t* ps) {
+  constexpr int B = 256 * H;
+  if constexpr (H == 0) {
+    asm volatile(
+        "ds_read_b64 %0, %9 offset:%11\n\tds_read_b64 %1, %9 offset:%12\n\tds_read_b64 %2, %9 offset:%13\n\t"
+        "ds_read_b64 %3, %9 offset:%14\n\tds_read_b64 %4, %9 offset:%15\n\tds_read_b64 %5, %9 offset:%16\n\t"
+        "ds_read_b64 %6, %9 offset:%17\n\tds_read_b64 %7, %9 offset:%18\n\tds_read_b128 %8, %10\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
+          "=&v"(x[0])
+        : "v"(pk), "v"(ps), MLA_O4(B, 32), MLA_O4(B + 128, 32)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64 %0, %10 offset:%12\n\tds_read_b64 %1, %10 offset:%13\n\tds_read_b64 %2, %10 offset:%14\n\t"
+        "ds_read_b64 %3, %10 offset:%15\n\tds_read_b64 %4, %10 offset:%16\n\tds_read_b64 %5, %10 offset:%17\n\t"
+        "ds_read_b64 %6, %10 offset:%18\n\tds_read_b64 %7, %10 offset:%19\n\tds_read_b128 %8, %11 offset:0\n\t"
+        "ds_read_b128 %9, %11 offset:64\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
+          "=&v"(x[0]), "=&v"(x[1])
+        : "v"(pk), "v"(pr), MLA_O4(B, 32), MLA_O4(B + 128, 32)
+        : "memory");
+  }
+}
+// FP8: the query operands of 8 k-steps, 16 B at p + OFF + 64 * i.
+template <int OFF>
+__device__ __forceinline__ void lds_read_q8(u32x4_t (&r)[8], LDS_AS const uint8_t* p) {
   asm volatile(
-      "ds_read_b128 %0, %11 offset:0\n\tds_read_b128 %1, %11 offset:16\n\tds_read_b128 %2, %11 offset:32\n\t"
-      "ds_read_b128 %3, %11 offset:48\n\tds_read_b128 %4, %11 offset:64\n\tds_read_b128 %5, %11 offset:80\n\t"
-      "ds_read_b128 %6, %11 offset:96\n\tds_read_b128 %7, %11 offset:112\n\t"
-      "ds_read_b128 %8, %12 offset:0\n\tds_read_b128 %9, %12 offset:16\n\tds_read_b32 %10, %13\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(lat[0]), "=&v"(lat[1]), "=&v"(lat[2]), "=&v"(lat[3]), "=&v"(lat[4]), "=&v"(lat[5]),
-        "=&v"(lat[6]), "=&v"(lat[7]), "=&v"(rope[0]), "=&v"(rope[1]), "=&v"(scale)
-      : "v"(pl), "v"(pr), "v"(ps)
+      "ds_read_b128 %0, %8 offset:%9\n\tds_read_b128 %1, %8 offset:%10\n\tds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\tds_read_b128 %4, %8 offset:%13\n\tds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\tds_read_b128 %7, %8 offset:%16\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(p), MLA_O4(OFF, 64), MLA_O4(OFF + 256, 64)
       : "memory");
 }
-// Writes of one lane's converted share into the bf16 stage: chunk m of the first 8 at
-// w[m], of the second 8 at w[m] + 2048, the two rope chunks at r0 and r1.
-__device__ __forceinline__ void lds_write_bf16(LDS_AS uint8_t* const (&w)[8], LDS_AS uint8_t* r0, LDS_AS uint8_t* r1,
-                                               const u32x4_t (&c)[16], const u32x4_t (&rope)[2]) {
+template <int OFF>
+__device__ __forceinline__ void lds_read_q2(u32x4_t (&r)[2], LDS_AS const uint8_t* p) {
+  asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(r[0]), "=&v"(r[1])
+               : "v"(p), "i"(OFF), "i"(OFF + 64)
+               : "memory");
+}
+// 4 transpose reads of the codes of one group of 128 columns: pv + 128 * G + 32 * c.
+template <int G>
+__device__ __forceinline__ void lds_read_f8v4(u32x2_t (&v)[4], LDS_AS const uint8_t* pv) {
+  constexpr int B = 128 * G;
   asm volatile(
-      "ds_write_b128 %0, %10\n\tds_write_b128 %1, %11\n\tds_write_b128 %2, %12\n\tds_write_b128 %3, %13\n\t"
-      "ds_write_b128 %4, %14\n\tds_write_b128 %5, %15\n\tds_write_b128 %6, %16\n\tds_write_b128 %7, %17\n\t"
-      "ds_write_b128 %0, %18 offset:2048\n\tds_write_b128 %1, %19 offset:2048\n\t"
-      "ds_write_b128 %2, %20 offset:2048\n\tds_write_b128 %3, %21 offset:2048\n\t"
-      "ds_write_b128 %4, %22 offset:2048\n\tds_write_b128 %5, %23 offset:2048\n\t"
-      "ds_write_b128 %6, %24 offset:2048\n\tds_write_b128 %7, %25 offset:2048\n\t"
-      "ds_write_b128 %8, %26\n\tds_write_b128 %9, %27\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      :
-      : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]), "v"(r0), "v"(r1),
-        "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(c[4]), "v"(c[5]), "v"(c[6]), "v"(c[7]),
-        "v"(c[8]), "v"(c[9]), "v"(c[10]), "v"(c[11]), "v"(c[12]), "v"(c[13]), "v"(c[14]), "v"(c[15]),
-        "v"(rope[0]), "v"(rope[1])
+      "ds_read_b64_tr_b8 %0, %4 offset:%5\n\tds_read_b64_tr_b8 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b8 %2, %4 offset:%7\n\tds_read_b64_tr_b8 %3, %4 offset:%8\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(pv), MLA_O4(B, 32)
       : "memory");
 }
-
+// The four group scales of tokens 4g..4g+3 at ps + 656 * i.
+__device__ __forceinline__ void lds_read_f8s4(u32x4_t (&sc)[4], LDS_AS const uint8_t* ps) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:0\n\tds_read_b128 %1, %4 offset:656\n\t"
+      "ds_read_b128 %2, %4 offset:1312\n\tds_read_b128 %3, %4 offset:1968\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3])
+      : "v"(ps)
+      : "memory");
+}
 // Split-decode kernel: 16 query rows per work-group (R = 16 * row groups).  FP8: the cache
-// rows are 656-byte fp8 rows (see kF8Row); each block goes through a small fp8 stage and
-// is widened into one bf16 stage in the row-major layout, where the bf16 path reads it.
+// rows are 656-byte fp8 rows (see kF8Row); each wave streams its blocks through three fp8
+// stages and builds the MFMA operands from the codes in registers (see the FP8 loop).
 // DEV: no host schedule; the work-groups cut the batch's blocks among themselves from the
 // device cache_seqlens and combine split sequences in the same launch (see below).
 template <bool OUT_F32, bool FP8, bool DEV>
 __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[FP8 ? kSmemFp8 : kSmemBytes];
+  // the stages while blocks stream; the four waves' states (kMergeBytes) when a piece ends
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FP8 ? kSplitSmemFp8 : kSplitSmemBf16];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
 
   const int lane = threadIdx.x & 63;
@@ -271,10 +309,19 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   const int ld_tok0 = lane >> 3, ld_tok1 = 8 + (lane >> 3);
   const int ld_col0 = 8 * ((lane & 7) ^ row_swz(ld_tok0)), ld_col1 = 8 * ((lane & 7) ^ row_swz(ld_tok1));
 
-  // bf16: two DMA stages; FP8: two fp8 DMA stages and one bf16 stage the blocks are widened into
+  // bf16: two DMA stages per wave; FP8: kF8Stages fp8 stages per wave
   LDS_AS uint8_t* stage0 = FP8 ? lds + wave * kF8WaveBytes : lds + (wave * kStages + 0) * kBlockBytes;
   LDS_AS uint8_t* stage1 = FP8 ? stage0 + kF8Stage : lds + (wave * kStages + 1) * kBlockBytes;
-  LDS_AS uint8_t* const cstage = FP8 ? stage0 + 2 * kF8Stage : nullptr;
+  // FP8 operand addresses within a stage.  S^T: lane (t = n, g) reads token t's codes at
+  // 656t + 8g (+ 32kk), its rope chunks at 656t + 512 + 16g (+ 64) and its scales at
+  // 656t + 640.  O^T: the transpose read gathers, per 16-lane group g, 8-byte rows from
+  // the addresses of its lanes j = 2k + p: token 4g + (k & 3), columns 16 (k >> 2) + 8p
+  // (+ 32c); lane (m, g) then holds tokens 4g..4g+3 of columns 32c + m and 32c + 16 + m.
+  const int f8_k = kF8Row * n + 8 * g;
+  const int f8_r = kF8Row * n + 512 + 16 * g;
+  const int f8_s = kF8Row * n + 640;
+  const int f8_v = kF8Row * (4 * g + ((n >> 1) & 3)) + 16 * (n >> 3) + 8 * (n & 1);
+  const int f8_p = kF8Row * 4 * g + 640;
   const uint8_t* const kv8 = (const uint8_t*)a.kv;
 
   const CST_AS int32_t* worker_off = as_const(a.worker_off);
@@ -293,9 +340,20 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     const int my_n = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
     auto blk_of = [&](int k) { return wave + kWaves * k; };
 
-    // query rows as MFMA B operands (Q^T): lane (n, g) holds row n, columns 32*kk + 8*g .. +8
-    bf16x8_t qf[kKSteps];
-    {
+    // query rows as MFMA B operands (Q^T): lane (n, g) holds row n, columns 32*kk + 8*g .. +8.
+    // bf16: resident in VGPRs for the piece.  FP8: the piece's 16 rows are put in LDS (row r at
+    // kF8QOff + kF8QRow * r; the padded stride keeps the 16-lane reads conflict-free) and read
+    // per k-step, which leaves the registers to the operand conversions.
+    bf16x8_t qf[FP8 ? 1 : kKSteps];
+    if constexpr (FP8) {
+      LDS_AS uint8_t* qlds = lds + kF8QOff;
+      for (int c = threadIdx.x; c < kBlock * (kDqk / 8); c += kThreads) {
+        const int r = c / (kDqk / 8), ch = c - r * (kDqk / 8);
+        const u32x4_t v = *(const GLB_AS u32x4_t*)(a.q + ((int64_t)b * R + row0 + r) * kDqk + 8 * ch);
+        *(LDS_AS u32x4_t*)(qlds + kF8QRow * r + 16 * ch) = v;
+      }
+      __syncthreads();
+    } else {
       const uint16_t* qrow = a.q + ((int64_t)b * R + row0 + n) * kDqk + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
@@ -313,7 +371,6 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     struct Src {
       const uint16_t* p[2];   // bf16: this lane's source for even / odd instructions
       const uint8_t* row0;    // FP8: the block's first row
-      int last;               // FP8: index of the block's last valid row
     };
     auto source = [&](int k, bool& ok) -> Src {
       const int tok0 = tb + kBlock * blk_of(k);
@@ -324,7 +381,6 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       Src r{};
       if constexpr (FP8) {
         r.row0 = kv8 + base * kF8Row;
-        r.last = last;
       } else {
         r.p[0] = a.kv + (base + min(ld_tok0, last)) * kDqk + ld_col0;
         r.p[1] = a.kv + (base + min(ld_tok1, last)) * kDqk + ld_col1;
@@ -336,17 +392,26 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     // instruction (the 11th moves the last 16).
     auto issue = [&](const Src& src, LDS_AS uint8_t* stage) {
       if constexpr (FP8) {
+        // the block's 16 rows are contiguous (a block never crosses a page); rows past the
+        // end of the piece are loaded too and masked where they are used
+        const uint8_t* gp = src.row0 + 16 * lane;
+        constexpr int kTail = kF8Units - 64 * (kF8Loads - 1);   // lanes of the last load (16)
+        if (stream) {
 #pragma unroll
-        for (int j = 0; j < kF8Loads; ++j) {
-          const int u = 64 * j + lane;
-          if (j + 1 < kF8Loads || u < kF8Units) {
-            const int t = u / (kF8Row / 16), c = u - t * (kF8Row / 16);
-            GLB_AS void* gp = (GLB_AS void*)(src.row0 + min(t, src.last) * kF8Row + 16 * c);
-            if (stream)
-              __builtin_amdgcn_global_load_lds(gp, (LDS_AS void*)(stage + 1024 * j), 16, 0, kKvLoadStream);
-            else
-              __builtin_amdgcn_global_load_lds(gp, (LDS_AS void*)(stage + 1024 * j), 16, 0, kKvLoadReuse);
-          }
+          for (int j = 0; j + 1 < kF8Loads; ++j)
+            __builtin_amdgcn_global_load_lds((GLB_AS void*)(gp + 1024 * j), (LDS_AS void*)(stage + 1024 * j), 16, 0,
+                                             kKvLoadStream);
+          if (lane < kTail)
+            __builtin_amdgcn_global_load_lds((GLB_AS void*)(gp + 1024 * (kF8Loads - 1)),
+                                             (LDS_AS void*)(stage + 1024 * (kF8Loads - 1)), 16, 0, kKvLoadStream);
+        } else {
+#pragma unroll
+          for (int j = 0; j + 1 < kF8Loads; ++j)
+            __builtin_amdgcn_global_load_lds((GLB_AS void*)(gp + 1024 * j), (LDS_AS void*)(stage + 1024 * j), 16, 0,
+                                             kKvLoadReuse);
+          if (lane < kTail)
+            __builtin_amdgcn_global_load_lds((GLB_AS void*)(gp + 1024 * (kF8Loads - 1)),
+                                             (LDS_AS void*)(stage + 1024 * (kF8Loads - 1)), 16, 0, kKvLoadReuse);
         }
       } else if (stream) {
 #pragma unroll
@@ -359,39 +424,6 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           __builtin_amdgcn_global_load_lds((GLB_AS void*)(src.p[j & 1] + 64 * (j >> 1)),
                                            (LDS_AS void*)(stage + 1024 * j), 16, 0, kKvLoadReuse);
       }
-    };
-    // FP8: widen an fp8 stage into the bf16 stage.  Lane (t = lane % 16, q = lane / 16)
-    // converts latent columns [128q, 128q + 128) of token t (one group scale, which the
-    // conversion applies through its exponent) and copies rope chunks 2q, 2q + 1.
-    auto widen = [&](LDS_AS const uint8_t* f8, LDS_AS uint8_t* dst) {
-      const int t = lane & 15, q = lane >> 4;
-      u32x4_t lat[8], rope[2];
-      uint32_t scale_bits;
-      lds_read_f8(lat, rope, scale_bits, f8 + t * kF8Row + 128 * q, f8 + t * kF8Row + 512 + 32 * q,
-                  f8 + t * kF8Row + 640 + 4 * q);
-      const float scale = __uint_as_float(scale_bits);
-      u32x4_t c[16];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const uint32_t x = lat[i][2 * h + w];
-            c[2 * i + h][2 * w + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, scale, false));
-            c[2 * i + h][2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, scale, true));
-          }
-        }
-      }
-      // chunk m of this lane's 16 is column chunk 16q + m of token t: unit
-      // 128 * (2q + m / 8) + 8t + ((m % 8) ^ row_swz(t)); rope chunk 64 + 2q + i likewise
-      const int sw = row_swz(t);
-      LDS_AS uint8_t* w[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) w[m] = dst + 16 * (256 * q + 8 * t + (m ^ sw));
-      LDS_AS uint8_t* r0 = dst + 16 * (1024 + 8 * t + ((2 * q) ^ sw));
-      LDS_AS uint8_t* r1 = dst + 16 * (1024 + 8 * t + ((2 * q + 1) ^ sw));
-      lds_write_bf16(w, r0, r1, c, rope);
     };
     // Every LDS read of a block first (K for S^T, then all of V^T into registers); then the
     // stage is refilled with the block after next (`ns`, if `nx`) while S^T, the softmax
@@ -414,7 +446,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       LDS_AS const uint8_t* const vp[4] = {st + v_base[0], st + v_base[1], st + v_base[2], st + v_base[3]};
       lds_read_v16<0>(vf0, vp);                // columns 0..255
       lds_read_v16<1>(vf1, vp);                // columns 256..511
-      if (!FP8 && nx) issue(ns, st);
+      if (nx) issue(ns, st);
       mma(kf, 9);
       sacc += acc2;
     };
@@ -431,61 +463,168 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         lb[i] = bf16_rne(p - bf16_bits_to_float(hb[i]));
         lsum += p;
       }
-      const i16x4_t ph = i16x4_t{(short)hb[0], (short)hb[1], (short)hb[2], (short)hb[3]};
-      const i16x4_t pl = i16x4_t{(short)lb[0], (short)lb[1], (short)lb[2], (short)lb[3]};
+      // one 16x16x32 MFMA per column block: K index 8g + j is token 4g + (j & 3), taking
+      // p's hi part for j < 4 and its lo part for j >= 4, against V^T repeated twice
+      const u32x4_t pp = u32x4_t{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16),
+                                 lb[2] | (lb[3] << 16)};
       auto pv = [&](const u32x2_t (&vf)[16], int mb0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const i16x4_t v = __builtin_bit_cast(i16x4_t, vf[i]);
-          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, ph, o[mb0 + i], 0, 0, 0);
-          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, pl, o[mb0 + i], 0, 0, 0);
+          const u32x4_t v = u32x4_t{vf[i][0], vf[i][1], vf[i][0], vf[i][1]};
+          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v),
+                                                               __builtin_bit_cast(bf16x8_t, pp), o[mb0 + i], 0, 0, 0);
         }
       };
       pv(vf0, 0);
       pv(vf1, 16);
     };
 
-    bool ok0 = true, ok1 = true;   // table entry of the block now in each stage was in range
-    if (my_n > 0) issue(source(0, ok0), stage0);
-    if (my_n > 1) issue(source(1, ok1), stage1);
+    // FP8: O^T += V^T P^T with V^T the codes (converted exactly to bf16, scale 1) and, for
+    // the columns of group G, P^T scaled by each token's 2^e[t][G], the exponent part of its
+    // group scale; p_t 2^e is split into hi + lo exactly as p is on the bf16 path.  The codes
+    // are read one group at a time; the stage is refilled (`refill`) after the last read.  Tokens 4g + i >= vvalid (past the end of the piece, whose
+    // rows may hold anything) get zero codes and zero weights.
+    auto accumulate_f8 = [&](const float (&s)[4], LDS_AS const uint8_t* st, const int vvalid, auto&& refill) {
+      float p[4];
+      uint32_t vmask = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
+        lsum += p[i];
+        vmask |= (4 * g + i < vvalid ? 0xFFu : 0u) << (8 * i);
+      }
+      u32x4_t psc[4];
+      lds_read_f8s4(psc, st + f8_p);
+      auto group = [&](const u32x2_t (&vraw)[4], int G) {
+        const int c0 = 4 * G;
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pg = 4 * g + i < vvalid ? p[i] * __uint_as_float(psc[i][G] & 0x7F800000u) : 0.f;
+          hb[i] = bf16_rne(pg);
+          lb[i] = bf16_rne(pg - bf16_bits_to_float(hb[i]));
+        }
+        const u32x4_t pp = u32x4_t{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16),
+                                   lb[2] | (lb[3] << 16)};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int c = c0 + cc;                  // 32-column chunk (tiles 2c, 2c + 1)
+          const uint32_t w0 = vraw[cc][0] & vmask, w1 = vraw[cc][1] & vmask;
+          const uint32_t l0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+          const uint32_t l1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+          const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+          const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+          o[2 * c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4_t{l0, l1, l0, l1}),
+                                                             __builtin_bit_cast(bf16x8_t, pp), o[2 * c], 0, 0, 0);
+          o[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4_t{h0, h1, h0, h1}),
+                                                                 __builtin_bit_cast(bf16x8_t, pp), o[2 * c + 1], 0, 0, 0);
+        }
+      };
+      {
+        u32x2_t v[4];
+        lds_read_f8v4<0>(v, st + f8_v);
+        group(v, 0);
+      }
+      {
+        u32x2_t v[4];
+        lds_read_f8v4<1>(v, st + f8_v);
+        group(v, 1);
+      }
+      {
+        u32x2_t v[4];
+        lds_read_f8v4<2>(v, st + f8_v);
+        group(v, 2);
+      }
+      {
+        u32x2_t v[4];
+        lds_read_f8v4<3>(v, st + f8_v);
+        refill();
+        group(v, 3);
+      }
+    };
 
-    int k = 0;
-    while (k < my_n) {
-      float s[4], mx = 0.f;
-      bool rescale = false;
-      u32x2_t vf0[16], vf1[16];
-      // hot loop: o is only touched by MFMA here
-      for (; k < my_n; ++k) {
-        LDS_AS uint8_t* st = (k & 1) ? stage1 : stage0;
-        bool nok = true;
-        const bool nx = k + 2 < my_n;
-        Src nsrc{};
-        if (nx) nsrc = source(k + 2, nok);
-        if (k + 1 < my_n) {
-          if constexpr (FP8)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kF8Loads) : "memory");
-          else
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerBlock) : "memory");
-        } else {
+    if constexpr (FP8) {
+      // ---- FP8 rows: three stages per wave; block k is in stage k % 3 while blocks k + 1
+      // and k + 2 are in flight; its codes are read into registers, then the stage is
+      // refilled with block k + 3.  S^T takes K = code * scale from the conversion (which
+      // applies the scale's exponent); O^T takes V^T = code and folds each token's group
+      // scale 2^e into P (exact for powers of two): O^T[d] += sum_t code[t][d] (p_t 2^e[t][d/128]).
+      uint32_t okq = 0;   // bit i: the table entry of the block now in stage i was in range
+#pragma unroll
+      for (int i = 0; i < kF8Stages; ++i) {
+        bool ok = true;
+        if (i < my_n) issue(source(i, ok), stage0 + i * kF8Stage);
+        okq |= (ok ? 1u : 0u) << i;
+      }
+      int k = 0;
+      while (k < my_n) {
+       float s[4], mx = 0.f;
+       bool rescale = false;
+       for (; k < my_n; ++k) {
+        const int slot = k % kF8Stages;
+        LDS_AS uint8_t* const st = stage0 + slot * kF8Stage;
+        const int after = min(kF8Stages - 1, my_n - 1 - k);   // blocks issued after block k
+        if (after >= 2)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kF8Loads) : "memory");
+        else if (after == 1)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kF8Loads) : "memory");
+        else
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const bool ok = (okq >> slot) & 1u;
+        // refill the stage with block k + 3 once block k's codes are in registers
+        auto refill = [&] {
+          bool nok = true;
+          if (k + kF8Stages < my_n) issue(source(k + kF8Stages, nok), st);
+          okq = (okq & ~(1u << slot)) | ((nok ? 1u : 0u) << slot);
+        };
+        // a block whose table entry was out of range (its DMA read page 0) takes the same
+        // path with every token masked, so it adds nothing; one branch-free loop body keeps
+        // the accumulators in place across iterations
+        if (!ok && lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // S^T = K Q^T from the codes (two batches of 8 k-steps, then the rope columns)
+        f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        u32x4_t ksc;
+        auto kstep = [&](const u32x2_t (&kraw)[8], const u32x4_t (&qv)[8], int kk0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int kk = kk0 + i;
+            const float sc = __uint_as_float(ksc[kk >> 2]);
+            u32x4_t kf;
+            kf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kraw[i][0], sc, false));
+            kf[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kraw[i][0], sc, true));
+            kf[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kraw[i][1], sc, false));
+            kf[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kraw[i][1], sc, true));
+            f32x4_t& acc = (kk & 1) ? acc2 : sacc;
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf),
+                                                          __builtin_bit_cast(bf16x8_t, qv[i]), acc, 0, 0, 0);
+          }
+        };
+        LDS_AS const uint8_t* const qp = lds + kF8QOff + kF8QRow * n + 16 * g;
+        {
+          u32x2_t kraw[8];
+          u32x4_t x[2], qv[8];
+          lds_read_f8k8<0>(kraw, x, st + f8_k, nullptr, st + f8_s);
+          lds_read_q8<0>(qv, qp);
+          ksc = x[0];
+          kstep(kraw, qv, 0);
         }
-        const bool ok = (k & 1) ? ok1 : ok0;
-        if (k & 1) ok1 = nok; else ok0 = nok;   // the stage's next occupant
-        if (!ok) {
-          if (lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (nx) issue(nsrc, st);
-          continue;
+        {
+          u32x2_t kraw[8];
+          u32x4_t rope[2], qv[8];
+          lds_read_f8k8<1>(kraw, rope, st + f8_k, st + f8_r, nullptr);
+          lds_read_q8<512>(qv, qp);
+          kstep(kraw, qv, 8);
+          u32x4_t qr[2];
+          lds_read_q2<1024>(qr, qp);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rope[0]),
+                                                         __builtin_bit_cast(bf16x8_t, qr[0]), sacc, 0, 0, 0);
+          acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rope[1]),
+                                                         __builtin_bit_cast(bf16x8_t, qr[1]), acc2, 0, 0, 0);
         }
+        sacc += acc2;
         const int tok0 = tb + kBlock * blk_of(k);
-        f32x4_t sacc;
-        if constexpr (FP8) {
-          widen(st, cstage);
-          if (nx) issue(nsrc, st);
-          scores(cstage, sacc, vf0, vf1, nsrc, false);
-        } else {
-          scores(st, sacc, vf0, vf1, nsrc, nx);
-        }
-        const int nvalid = lim - tok0;   // tokens of the block this row sees (may be <= 0)
+        const int nvalid = ok ? lim - tok0 : 0;   // tokens of the block this row sees (may be <= 0)
+        const int vvalid = ok ? te - tok0 : 0;    // tokens of the block inside the piece
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
         mx = wave_max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
@@ -493,20 +632,86 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           rescale = true;
           break;
         }
-        accumulate(s, vf0, vf1);
-      }
-      if (!rescale) break;
-      // rare path: a running max grew past the slack; move the reference and rescale
-      {
+        accumulate_f8(s, st, vvalid, refill);
+       }
+       if (!rescale) break;
+       {
+        // rare path: a running max grew past the slack; move the reference and rescale
+        // (block k is still in its stage: the stage is refilled by accumulate_f8)
+        const int slot = k % kF8Stages;
+        LDS_AS uint8_t* const st = stage0 + slot * kF8Stage;
+        const bool okb = (okq >> slot) & 1u;   // (a masked block never gets here: its max is -inf)
+        auto refill = [&] {
+          bool nok = true;
+          if (k + kF8Stages < my_n) issue(source(k + kF8Stages, nok), st);
+          okq = (okq & ~(1u << slot)) | ((nok ? 1u : 0u) << slot);
+        };
         const bool need = mx > m_ref + kRescaleSlack;
         const float f = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
         m_ref = need ? mx : m_ref;
         lsum *= f;
 #pragma unroll
         for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
-        accumulate(s, vf0, vf1);
+        accumulate_f8(s, st, okb ? te - (tb + kBlock * blk_of(k)) : 0, refill);
         ++k;
+       }
       }
+    } else {
+    bool ok0 = true, ok1 = true;   // table entry of the block now in each stage was in range
+      if (my_n > 0) issue(source(0, ok0), stage0);
+      if (my_n > 1) issue(source(1, ok1), stage1);
+
+      int k = 0;
+      while (k < my_n) {
+        float s[4], mx = 0.f;
+        bool rescale = false;
+        u32x2_t vf0[16], vf1[16];
+        // hot loop: o is only touched by MFMA here
+        for (; k < my_n; ++k) {
+          LDS_AS uint8_t* st = (k & 1) ? stage1 : stage0;
+          bool nok = true;
+          const bool nx = k + 2 < my_n;
+          Src nsrc{};
+          if (nx) nsrc = source(k + 2, nok);
+          if (k + 1 < my_n) {
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerBlock) : "memory");
+          } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          }
+          const bool ok = (k & 1) ? ok1 : ok0;
+          if (k & 1) ok1 = nok; else ok0 = nok;   // the stage's next occupant
+          if (!ok) {
+            if (lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (nx) issue(nsrc, st);
+            continue;
+          }
+          const int tok0 = tb + kBlock * blk_of(k);
+          f32x4_t sacc;
+          scores(st, sacc, vf0, vf1, nsrc, nx);
+          const int nvalid = lim - tok0;   // tokens of the block this row sees (may be <= 0)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
+          mx = wave_max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+          if (__any(mx > m_ref + kRescaleSlack)) {
+            rescale = true;
+            break;
+          }
+          accumulate(s, vf0, vf1);
+        }
+        if (!rescale) break;
+        // rare path: a running max grew past the slack; move the reference and rescale
+        {
+          const bool need = mx > m_ref + kRescaleSlack;
+          const float f = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
+          m_ref = need ? mx : m_ref;
+          lsum *= f;
+#pragma unroll
+          for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
+          accumulate(s, vf0, vf1);
+          ++k;
+        }
+      }
+
     }
 
     // ---- merge the four waves' states and write
