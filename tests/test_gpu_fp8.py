@@ -1,9 +1,9 @@
 """FP8 (E4M3) latent cache rows on the HIP path (through the C-ABI) against the fp64 oracle.
 
-The kernel widens each fp8 block into the bf16 layout with the exponent-only group
-scales, which is exact, and then runs the bf16 arithmetic; so an fp8 cache and a bf16
-cache holding the same values give bit-identical results, and the fp32-output bounds
-of the bf16 path apply.
+The kernel converts the codes to bf16 in registers (K with the exponent of its group scale,
+V^T unscaled with each token's power-of-two scale folded into its softmax weight), which is
+exact and forms the same products as the bf16 path; so an fp8 cache and a bf16 cache holding
+the same values give bit-identical results, and the fp32-output bounds of the bf16 path apply.
 """
 import numpy as np
 import pytest
@@ -12,7 +12,8 @@ from mla_decode_attention_paged_amd import binding as B
 from mla_decode_attention_paged_amd import inputs as gen
 from mla_decode_attention_paged_amd.device import Runner, to_device
 from oracle import mla_oracle as orc
-from tests.test_gpu_parity import (F32_LSE_TOL, F32_MAX_TOL, F32_RMSE_TOL, _say, bf16_half_ulp, compare)
+from tests.test_gpu_parity import (F32_LSE_TOL, F32_MAX_TOL, F32_RMSE_TOL, _say, bf16_half_ulp, check_dropped_page,
+                                   compare)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,3 +122,21 @@ def test_fp8_full_size_sampled(name, sample):
     ref_o, ref_l = oracle(prob, sample)
     compare(out, lse, ref_o, ref_l, batch_idx=sample, what=f"{name} fp8")
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+def test_fp8_out_of_range_block_table_entry_drops_its_tokens():
+    """A used table entry outside [0, num_pages): its 16-token blocks are masked out (their DMA
+    reads page 0), bit 0 of the status word is set, and the rest is exact."""
+    prob = gen.make_problem(batch=2, q_len=1, num_heads=16, page_size=64, lengths=[640, 600], seed=31,
+                            kv_format="fp8", out_fp32=True)
+    bt = prob.block_table.copy()
+    bt[1, 3] = prob.num_pages + 5
+    bad = gen.Problem(q=prob.q, kv_cache=prob.kv_cache, block_table=bt, cache_seqlens=prob.cache_seqlens,
+                      softmax_scale=prob.softmax_scale, page_size=64, out_fp32=True)
+    r = Runner(bad)
+    r()
+    out, lse = r.results()
+    assert B.mla_read_status(r.ws) & 1
+    ref_o, ref_l = oracle(prob, [0])
+    compare(out, lse, ref_o, ref_l, batch_idx=[0], what="fp8 unaffected sequence", tol=TIGHT)
+    check_dropped_page(prob, out, lse, seq=1, page_idx=3, tol=TIGHT)

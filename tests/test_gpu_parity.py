@@ -245,7 +245,23 @@ def test_out_of_range_block_table_entry_is_flagged():
     assert B.mla_read_status(r.ws) & 1
     ref_o, ref_l = oracle(prob, [0])
     compare(out, lse, ref_o, ref_l, batch_idx=[0], what="unaffected sequence")
-    assert np.all(np.isfinite(out[1]))
+    check_dropped_page(prob, out, lse, seq=1, page_idx=3)
+
+
+def check_dropped_page(prob, out, lse, seq, page_idx, tol=(RMSE_TOL, MAX_TOL, LSE_TOL)):
+    """Sequence `seq` must equal attention over its tokens outside table entry `page_idx`."""
+    P, L = prob.page_size, int(prob.cache_seqlens[seq])
+    keep = [t for t in range(L) if t // P != page_idx]
+    rows = orc.widen_rows(orc.gather_sequence(prob.kv_cache, prob.block_table[seq], L, P)[keep])
+    R = prob.q_len * prob.num_heads
+    q = orc.widen_bf16(prob.q[seq]).reshape(R, -1)
+    ref_o, ref_l = orc.attend(q, rows, rows[:, :512], prob.softmax_scale)
+    ro = ref_o.reshape(out[seq].shape)
+    rl = ref_l.reshape(lse[seq].shape)
+    err = out[seq] - ro
+    rmse, mx, le = float(np.sqrt(np.mean(err ** 2))), float(np.max(np.abs(err))), float(np.max(np.abs(lse[seq] - rl)))
+    _say(f"  dropped page {page_idx} of sequence {seq}: rmse {rmse:.2e} max {mx:.2e} lse {le:.2e}")
+    assert rmse <= tol[0] and mx <= tol[1] and le <= tol[2]
 
 
 def test_repeated_calls_are_deterministic():
