@@ -31,6 +31,8 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLB_AS __attribute__((address_space(1)))
@@ -107,13 +109,21 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Two fp32 -> packed bf16 (a in the low half), round to nearest even: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+// Softmax weights as bf16 hi + lo (hi = bf16(p), lo = bf16(p - hi), ~16 mantissa bits):
+// {hi(p0, p1), hi(p2, p3), lo(p0, p1), lo(p2, p3)}.
+__device__ __forceinline__ u32x4_t split_hi_lo(float p0, float p1, float p2, float p3) {
+  const uint32_t h01 = bf16x2_rne(p0, p1), h23 = bf16x2_rne(p2, p3);
+  const uint32_t l01 = bf16x2_rne(p0 - __uint_as_float(h01 << 16), p1 - __uint_as_float(h01 & 0xFFFF0000u));
+  const uint32_t l23 = bf16x2_rne(p2 - __uint_as_float(h23 << 16), p3 - __uint_as_float(h23 & 0xFFFF0000u));
+  return u32x4_t{h01, h23, l01, l23};
+}
 
 
 // Batched LDS reads in inline asm, each block waiting for its own reads before it
@@ -455,18 +465,15 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     // MFMA, so the weights carry ~16 mantissa bits instead of bf16's 8; the running
     // sum l takes p in fp32.
     auto accumulate = [&](const float (&s)[4], const u32x2_t (&vf0)[16], const u32x2_t (&vf1)[16]) {
-      uint32_t hb[4], lb[4];
+      float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[i] - m_ref);
-        hb[i] = bf16_rne(p);
-        lb[i] = bf16_rne(p - bf16_bits_to_float(hb[i]));
-        lsum += p;
+        p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
+        lsum += p[i];
       }
       // one 16x16x32 MFMA per column block: K index 8g + j is token 4g + (j & 3), taking
       // p's hi part for j < 4 and its lo part for j >= 4, against V^T repeated twice
-      const u32x4_t pp = u32x4_t{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16),
-                                 lb[2] | (lb[3] << 16)};
+      const u32x4_t pp = split_hi_lo(p[0], p[1], p[2], p[3]);
       auto pv = [&](const u32x2_t (&vf)[16], int mb0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -482,34 +489,29 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     // FP8: O^T += V^T P^T with V^T the codes (converted exactly to bf16, scale 1) and, for
     // the columns of group G, P^T scaled by each token's 2^e[t][G], the exponent part of its
     // group scale; p_t 2^e is split into hi + lo exactly as p is on the bf16 path.  The codes
-    // are read one group at a time; the stage is refilled (`refill`) after the last read.  Tokens 4g + i >= vvalid (past the end of the piece, whose
-    // rows may hold anything) get zero codes and zero weights.
-    auto accumulate_f8 = [&](const float (&s)[4], LDS_AS const uint8_t* st, const int vvalid, auto&& refill) {
+    // are read one group at a time; the stage is refilled (`refill`) after the last read.
+    // Rows past the end of the piece were zeroed in the stage (codes and scales), so they
+    // add nothing.
+    auto accumulate_f8 = [&](const float (&s)[4], LDS_AS const uint8_t* st, auto&& refill) {
       float p[4];
-      uint32_t vmask = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
         lsum += p[i];
-        vmask |= (4 * g + i < vvalid ? 0xFFu : 0u) << (8 * i);
       }
       u32x4_t psc[4];
       lds_read_f8s4(psc, st + f8_p);
       auto group = [&](const u32x2_t (&vraw)[4], int G) {
         const int c0 = 4 * G;
-        uint32_t hb[4], lb[4];
+        float pg[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pg = 4 * g + i < vvalid ? p[i] * __uint_as_float(psc[i][G] & 0x7F800000u) : 0.f;
-          hb[i] = bf16_rne(pg);
-          lb[i] = bf16_rne(pg - bf16_bits_to_float(hb[i]));
-        }
-        const u32x4_t pp = u32x4_t{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16),
-                                   lb[2] | (lb[3] << 16)};
+        for (int i = 0; i < 4; ++i)
+          pg[i] = p[i] * __uint_as_float(psc[i][G] & 0x7F800000u);
+        const u32x4_t pp = split_hi_lo(pg[0], pg[1], pg[2], pg[3]);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
           const int c = c0 + cc;                  // 32-column chunk (tiles 2c, 2c + 1)
-          const uint32_t w0 = vraw[cc][0] & vmask, w1 = vraw[cc][1] & vmask;
+          const uint32_t w0 = vraw[cc][0], w1 = vraw[cc][1];
           const uint32_t l0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
           const uint32_t l1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
           const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
@@ -577,10 +579,17 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           if (k + kF8Stages < my_n) issue(source(k + kF8Stages, nok), st);
           okq = (okq & ~(1u << slot)) | ((nok ? 1u : 0u) << slot);
         };
-        // a block whose table entry was out of range (its DMA read page 0) takes the same
-        // path with every token masked, so it adds nothing; one branch-free loop body keeps
-        // the accumulators in place across iterations
+        // A block whose table entry was out of range (its DMA read page 0) takes the same
+        // path with every row zeroed and every score masked, so it adds nothing; one loop
+        // body without a skip keeps the accumulators in place across iterations.
         if (!ok && lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int tok0 = tb + kBlock * blk_of(k);
+        const int vvalid = ok ? te - tok0 : 0;    // rows of the block inside the piece
+        if (vvalid < kBlock) {
+          // rows vvalid..15 may hold anything: zero their codes, rope and scales in the stage
+          for (int u = (kF8Row / 16) * vvalid + lane; u < kF8Units; u += 64)
+            *(LDS_AS u32x4_t*)(st + 16 * u) = u32x4_t{0u, 0u, 0u, 0u};
+        }
         // S^T = K Q^T from the codes (two batches of 8 k-steps, then the rope columns)
         f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
         u32x4_t ksc;
@@ -622,9 +631,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
                                                          __builtin_bit_cast(bf16x8_t, qr[1]), acc2, 0, 0, 0);
         }
         sacc += acc2;
-        const int tok0 = tb + kBlock * blk_of(k);
         const int nvalid = ok ? lim - tok0 : 0;   // tokens of the block this row sees (may be <= 0)
-        const int vvalid = ok ? te - tok0 : 0;    // tokens of the block inside the piece
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
         mx = wave_max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
@@ -632,7 +639,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           rescale = true;
           break;
         }
-        accumulate_f8(s, st, vvalid, refill);
+        accumulate_f8(s, st, refill);
        }
        if (!rescale) break;
        {
@@ -640,7 +647,6 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         // (block k is still in its stage: the stage is refilled by accumulate_f8)
         const int slot = k % kF8Stages;
         LDS_AS uint8_t* const st = stage0 + slot * kF8Stage;
-        const bool okb = (okq >> slot) & 1u;   // (a masked block never gets here: its max is -inf)
         auto refill = [&] {
           bool nok = true;
           if (k + kF8Stages < my_n) issue(source(k + kF8Stages, nok), st);
@@ -652,7 +658,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         lsum *= f;
 #pragma unroll
         for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
-        accumulate_f8(s, st, okb ? te - (tb + kBlock * blk_of(k)) : 0, refill);
+        accumulate_f8(s, st, refill);
         ++k;
        }
       }
@@ -759,8 +765,8 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
             *(f32x4_t*)((float*)a.out + off) = acc;
           } else {
             u32x2_t pkd;
-            pkd[0] = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
-            pkd[1] = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
+            pkd[0] = bf16x2_rne(acc[0], acc[1]);
+            pkd[1] = bf16x2_rne(acc[2], acc[3]);
             *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
           }
         } else {
@@ -991,20 +997,14 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
     // block delivers.  A block that is not used contributes a zero V^T half.
     // p = exp2(s - m_ref) goes in as bf16 hi + lo (about 16 mantissa bits).
     auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[8], bool use0, bool use1) {
-      uint32_t hb[8], lb[8];
+      float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[i] - m_ref);
-        hb[i] = bf16_rne(p);
-        lb[i] = bf16_rne(p - bf16_bits_to_float(hb[i]));
-        lsum += p;
+        p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
+        lsum += p[i];
       }
-      u32x4_t ph, pl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ph[i] = hb[2 * i] | (hb[2 * i + 1] << 16);
-        pl[i] = lb[2 * i] | (lb[2 * i + 1] << 16);
-      }
+      const u32x4_t q0 = split_hi_lo(p[0], p[1], p[2], p[3]), q1 = split_hi_lo(p[4], p[5], p[6], p[7]);
+      const u32x4_t ph = u32x4_t{q0[0], q0[1], q1[0], q1[1]}, pl = u32x4_t{q0[2], q0[3], q1[2], q1[3]};
       const uint32_t keep0 = use0 ? 0xFFFFFFFFu : 0u, keep1 = use1 ? 0xFFFFFFFFu : 0u;
       LDS_AS const uint8_t* vp0 = st + v_lane;
       LDS_AS const uint8_t* vp1 = st + kBlockBytes + v_lane;
@@ -1116,8 +1116,8 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
             *(f32x4_t*)((float*)a.out + off) = v;
           } else {
             u32x2_t pkd;
-            pkd[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-            pkd[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+            pkd[0] = bf16x2_rne(v[0], v[1]);
+            pkd[1] = bf16x2_rne(v[2], v[3]);
             *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
           }
         } else {
@@ -1196,8 +1196,8 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     *(f32x4_t*)((float*)a.out + off) = v;
   } else {
     u32x2_t pkd;
-    pkd[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-    pkd[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+    pkd[0] = bf16x2_rne(v[0], v[1]);
+    pkd[1] = bf16x2_rne(v[2], v[3]);
     *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
   }
   if (cg == 0 && (threadIdx.x & 15) == 0 && a.lse) a.lse[(int64_t)b * R + r] = L > 0.f ? M + __logf(L) : -INFINITY;
@@ -1263,8 +1263,8 @@ __global__ void __launch_bounds__(256) merge_dev_kernel(MergeArgs a) {
     *(f32x4_t*)((float*)a.out + off) = v;
   } else {
     u32x2_t pkd;
-    pkd[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-    pkd[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+    pkd[0] = bf16x2_rne(v[0], v[1]);
+    pkd[1] = bf16x2_rne(v[2], v[3]);
     *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
   }
   if (cg == 0 && (threadIdx.x & 15) == 0 && a.lse) a.lse[(int64_t)b * R + r] = L > 0.f ? M + __logf(L) : -INFINITY;
