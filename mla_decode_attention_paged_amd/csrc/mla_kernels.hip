@@ -33,6 +33,7 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLB_AS __attribute__((address_space(1)))
@@ -55,9 +56,7 @@ constexpr int kF8Stage = kBlock * kF8Row;                      // 10,496 bytes
 constexpr int kF8Loads = (kF8Units + 63) / 64;                 // 11 DMA instructions per block
 constexpr int kF8Stages = 3;                                   // fp8 stages per wave
 constexpr int kF8WaveBytes = kF8Stages * kF8Stage;             // 31,488
-constexpr int kF8QRow = kDqk * 2 + 16;                         // 1,168: a padded Q row in LDS
-constexpr int kF8QOff = kWaves * kF8WaveBytes;                 // 125,952: Q^T rows after the stages
-constexpr int kSmemFp8 = kF8QOff + kBlock * kF8QRow;           // 144,640
+constexpr int kSmemFp8 = kWaves * kF8WaveBytes;               // 125,952
 constexpr int kLoadsPerBlock = kBlockBytes / (64 * 16);      // 18 DMA loads per wave per block
 // Cache policy of the KV-cache DMA loads.  With one row group every KV row is read by one
 // work-group only, and the loads carry the non-temporal bit (`nt`): on MI355X a
@@ -108,8 +107,6 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
   r = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
-
-__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
 // Two fp32 -> packed bf16 (a in the low half), round to nearest even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
@@ -209,73 +206,68 @@ __device__ __forceinline__ void lds_read_v16(u32x2_t (&r)[16], LDS_AS const uint
       : "memory");
 }
 
-// FP8 stage reads for S^T, lane (t, g): 8 latent codes of token t at pk + 256 * H + 32 * kk
-// (columns 256H + 32kk + 8g .. + 8, kk < 8) and, for H = 0, the token's four group scales at
-// ps; for H = 1, the two rope chunks at pr and pr + 64 (bf16 columns 512 + 32kk' + 8g .. + 8).
-template <int H>
-__device__ __forceinline__ void lds_read_f8k8(u32x2_t (&k)[8], u32x4_t (&x)[2], LDS_AS const uint8_t* pk,
-                                              LDS_AS const uint8_t* pr, LDS_AS const uint8_t* ps) {
-  constexpr int B = 256 * H;
-  if constexpr (H == 0) {
-    asm volatile(
-        "ds_read_b64 %0, %9 offset:%11\n\tds_read_b64 %1, %9 offset:%12\n\tds_read_b64 %2, %9 offset:%13\n\t"
-        "ds_read_b64 %3, %9 offset:%14\n\tds_read_b64 %4, %9 offset:%15\n\tds_read_b64 %5, %9 offset:%16\n\t"
-        "ds_read_b64 %6, %9 offset:%17\n\tds_read_b64 %7, %9 offset:%18\n\tds_read_b128 %8, %10\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
-          "=&v"(x[0])
-        : "v"(pk), "v"(ps), MLA_O4(B, 32), MLA_O4(B + 128, 32)
-        : "memory");
+// LDS reads the compiler schedules and counts itself (lgkmcnt), so that reads of a block
+// overlap the MFMAs of the same block.  Its stages are filled by dma_f8_block (asm): the
+// compiler does not see those LDS writes, so it adds no wait for them before a read; the
+// loop waits for them with an explicit s_waitcnt vmcnt.
+__device__ __forceinline__ u32x2_t lds_ld64(LDS_AS const uint8_t* p) { return *(LDS_AS const u32x2_t*)p; }
+__device__ __forceinline__ u32x4_t lds_ld128(LDS_AS const uint8_t* p) { return *(LDS_AS const u32x4_t*)p; }
+// gfx950 LDS transpose read of 8-bit elements (see the FP8 operand layout in the kernel)
+__device__ __forceinline__ u32x2_t lds_tr8(LDS_AS const uint8_t* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2_t*)p));
+}
+
+// One FP8 block (16 rows of 656 B, contiguous) into an LDS stage: 16 B per lane, lane l
+// moving bytes 16l + 1024j for j < 10 and lanes l < 16 also 16l + 10240.  The instruction
+// offset applies to the global and the LDS address alike; it stays below 4096, so the
+// 1024-B steps go from three bases 4096 B apart.  The LDS base is taken from M0, which is
+// saved and restored around the loads.  The block opens with s_waitcnt lgkmcnt(0): every
+// LDS read issued before it (the stage's previous block) has completed before the stage is
+// overwritten.
+template <bool NT>
+__device__ __forceinline__ void dma_f8_block(const uint8_t* row0, uint32_t voff, uint32_t lds, bool tail_lane) {
+  const uint8_t* b1 = row0 + 4096;
+  const uint8_t* b2 = row0 + 8192;
+  uint32_t sv;
+#define MLA_F8_DMA(NTS)                                                                          \
+  asm volatile(                                                                                  \
+      "s_waitcnt lgkmcnt(0)\n\ts_mov_b32 %0, m0\n\t"                                             \
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\t"                                                          \
+      "global_load_lds_dwordx4 %1, %5" NTS "\n\t"                                                \
+      "global_load_lds_dwordx4 %1, %5 offset:1024" NTS "\n\t"                                    \
+      "global_load_lds_dwordx4 %1, %5 offset:2048" NTS "\n\t"                                    \
+      "global_load_lds_dwordx4 %1, %5 offset:3072" NTS "\n\t"                                    \
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\t"                                                          \
+      "global_load_lds_dwordx4 %1, %6" NTS "\n\t"                                                \
+      "global_load_lds_dwordx4 %1, %6 offset:1024" NTS "\n\t"                                    \
+      "global_load_lds_dwordx4 %1, %6 offset:2048" NTS "\n\t"                                    \
+      "global_load_lds_dwordx4 %1, %6 offset:3072" NTS "\n\t"                                    \
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\t"                                                          \
+      "global_load_lds_dwordx4 %1, %7" NTS "\n\t"                                                \
+      "global_load_lds_dwordx4 %1, %7 offset:1024" NTS "\n\t"                                    \
+      "s_mov_b32 m0, %0"                                                                         \
+      : "=&s"(sv)                                                                                \
+      : "v"(voff), "s"(lds), "s"(lds + 4096), "s"(lds + 8192), "s"(row0), "s"(b1), "s"(b2)      \
+      : "memory")
+#define MLA_F8_DMA_TAIL(NTS)                                                                     \
+  asm volatile(                                                                                  \
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"                                      \
+      "global_load_lds_dwordx4 %1, %3 offset:2048" NTS "\n\t"                                    \
+      "s_mov_b32 m0, %0"                                                                         \
+      : "=&s"(sv)                                                                                \
+      : "v"(voff), "s"(lds + 8192), "s"(b2)                                                      \
+      : "memory")
+  if constexpr (NT) {
+    MLA_F8_DMA(" nt");
+    if (tail_lane) MLA_F8_DMA_TAIL(" nt");
   } else {
-    asm volatile(
-        "ds_read_b64 %0, %10 offset:%12\n\tds_read_b64 %1, %10 offset:%13\n\tds_read_b64 %2, %10 offset:%14\n\t"
-        "ds_read_b64 %3, %10 offset:%15\n\tds_read_b64 %4, %10 offset:%16\n\tds_read_b64 %5, %10 offset:%17\n\t"
-        "ds_read_b64 %6, %10 offset:%18\n\tds_read_b64 %7, %10 offset:%19\n\tds_read_b128 %8, %11 offset:0\n\t"
-        "ds_read_b128 %9, %11 offset:64\n\ts_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
-          "=&v"(x[0]), "=&v"(x[1])
-        : "v"(pk), "v"(pr), MLA_O4(B, 32), MLA_O4(B + 128, 32)
-        : "memory");
+    MLA_F8_DMA("");
+    if (tail_lane) MLA_F8_DMA_TAIL("");
   }
+#undef MLA_F8_DMA
+#undef MLA_F8_DMA_TAIL
 }
-// FP8: the query operands of 8 k-steps, 16 B at p + OFF + 64 * i.
-template <int OFF>
-__device__ __forceinline__ void lds_read_q8(u32x4_t (&r)[8], LDS_AS const uint8_t* p) {
-  asm volatile(
-      "ds_read_b128 %0, %8 offset:%9\n\tds_read_b128 %1, %8 offset:%10\n\tds_read_b128 %2, %8 offset:%11\n\t"
-      "ds_read_b128 %3, %8 offset:%12\n\tds_read_b128 %4, %8 offset:%13\n\tds_read_b128 %5, %8 offset:%14\n\t"
-      "ds_read_b128 %6, %8 offset:%15\n\tds_read_b128 %7, %8 offset:%16\n\ts_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(p), MLA_O4(OFF, 64), MLA_O4(OFF + 256, 64)
-      : "memory");
-}
-template <int OFF>
-__device__ __forceinline__ void lds_read_q2(u32x4_t (&r)[2], LDS_AS const uint8_t* p) {
-  asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(r[0]), "=&v"(r[1])
-               : "v"(p), "i"(OFF), "i"(OFF + 64)
-               : "memory");
-}
-// 4 transpose reads of the codes of one group of 128 columns: pv + 128 * G + 32 * c.
-template <int G>
-__device__ __forceinline__ void lds_read_f8v4(u32x2_t (&v)[4], LDS_AS const uint8_t* pv) {
-  constexpr int B = 128 * G;
-  asm volatile(
-      "ds_read_b64_tr_b8 %0, %4 offset:%5\n\tds_read_b64_tr_b8 %1, %4 offset:%6\n\t"
-      "ds_read_b64_tr_b8 %2, %4 offset:%7\n\tds_read_b64_tr_b8 %3, %4 offset:%8\n\ts_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-      : "v"(pv), MLA_O4(B, 32)
-      : "memory");
-}
-// The four group scales of tokens 4g..4g+3 at ps + 656 * i.
-__device__ __forceinline__ void lds_read_f8s4(u32x4_t (&sc)[4], LDS_AS const uint8_t* ps) {
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:0\n\tds_read_b128 %1, %4 offset:656\n\t"
-      "ds_read_b128 %2, %4 offset:1312\n\tds_read_b128 %3, %4 offset:1968\n\ts_waitcnt lgkmcnt(0)"
-      : "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3])
-      : "v"(ps)
-      : "memory");
-}
+
 // Split-decode kernel: 16 query rows per work-group (R = 16 * row groups).  FP8: the cache
 // rows are 656-byte fp8 rows (see kF8Row); each wave streams its blocks through three fp8
 // stages and builds the MFMA operands from the codes in registers (see the FP8 loop).
@@ -350,20 +342,10 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     const int my_n = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
     auto blk_of = [&](int k) { return wave + kWaves * k; };
 
-    // query rows as MFMA B operands (Q^T): lane (n, g) holds row n, columns 32*kk + 8*g .. +8.
-    // bf16: resident in VGPRs for the piece.  FP8: the piece's 16 rows are put in LDS (row r at
-    // kF8QOff + kF8QRow * r; the padded stride keeps the 16-lane reads conflict-free) and read
-    // per k-step, which leaves the registers to the operand conversions.
-    bf16x8_t qf[FP8 ? 1 : kKSteps];
-    if constexpr (FP8) {
-      LDS_AS uint8_t* qlds = lds + kF8QOff;
-      for (int c = threadIdx.x; c < kBlock * (kDqk / 8); c += kThreads) {
-        const int r = c / (kDqk / 8), ch = c - r * (kDqk / 8);
-        const u32x4_t v = *(const GLB_AS u32x4_t*)(a.q + ((int64_t)b * R + row0 + r) * kDqk + 8 * ch);
-        *(LDS_AS u32x4_t*)(qlds + kF8QRow * r + 16 * ch) = v;
-      }
-      __syncthreads();
-    } else {
+    // query rows as MFMA B operands (Q^T), resident in VGPRs for the piece: lane (n, g) holds
+    // row n, columns 32*kk + 8*g .. +8
+    bf16x8_t qf[kKSteps];
+    {
       const uint16_t* qrow = a.q + ((int64_t)b * R + row0 + n) * kDqk + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
@@ -404,25 +386,11 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       if constexpr (FP8) {
         // the block's 16 rows are contiguous (a block never crosses a page); rows past the
         // end of the piece are loaded too and masked where they are used
-        const uint8_t* gp = src.row0 + 16 * lane;
-        constexpr int kTail = kF8Units - 64 * (kF8Loads - 1);   // lanes of the last load (16)
-        if (stream) {
-#pragma unroll
-          for (int j = 0; j + 1 < kF8Loads; ++j)
-            __builtin_amdgcn_global_load_lds((GLB_AS void*)(gp + 1024 * j), (LDS_AS void*)(stage + 1024 * j), 16, 0,
-                                             kKvLoadStream);
-          if (lane < kTail)
-            __builtin_amdgcn_global_load_lds((GLB_AS void*)(gp + 1024 * (kF8Loads - 1)),
-                                             (LDS_AS void*)(stage + 1024 * (kF8Loads - 1)), 16, 0, kKvLoadStream);
-        } else {
-#pragma unroll
-          for (int j = 0; j + 1 < kF8Loads; ++j)
-            __builtin_amdgcn_global_load_lds((GLB_AS void*)(gp + 1024 * j), (LDS_AS void*)(stage + 1024 * j), 16, 0,
-                                             kKvLoadReuse);
-          if (lane < kTail)
-            __builtin_amdgcn_global_load_lds((GLB_AS void*)(gp + 1024 * (kF8Loads - 1)),
-                                             (LDS_AS void*)(stage + 1024 * (kF8Loads - 1)), 16, 0, kKvLoadReuse);
-        }
+        const uint32_t l = (uint32_t)(uintptr_t)stage;
+        if (stream)
+          dma_f8_block<true>(src.row0, 16u * lane, l, lane < 16);
+        else
+          dma_f8_block<false>(src.row0, 16u * lane, l, lane < 16);
       } else if (stream) {
 #pragma unroll
         for (int j = 0; j < kLoadsPerBlock; ++j)
@@ -488,21 +456,19 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
 
     // FP8: O^T += V^T P^T with V^T the codes (converted exactly to bf16, scale 1) and, for
     // the columns of group G, P^T scaled by each token's 2^e[t][G], the exponent part of its
-    // group scale; p_t 2^e is split into hi + lo exactly as p is on the bf16 path.  The codes
-    // are read one group at a time; the stage is refilled (`refill`) after the last read.
-    // Rows past the end of the piece were zeroed in the stage (codes and scales), so they
-    // add nothing.
-    auto accumulate_f8 = [&](const float (&s)[4], LDS_AS const uint8_t* st, auto&& refill) {
+    // group scale; p_t 2^e is split into hi + lo exactly as p is on the bf16 path.  vr holds
+    // the transposed codes (4 reads per group) and psc the scales of tokens 4g..4g+3.  Rows
+    // past the end of the piece were zeroed in the stage (codes and scales), so they add
+    // nothing.
+    auto accumulate_f8 = [&](const float (&s)[4], const u32x2_t (&vr)[16], const u32x4_t (&psc)[4]) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
         lsum += p[i];
       }
-      u32x4_t psc[4];
-      lds_read_f8s4(psc, st + f8_p);
-      auto group = [&](const u32x2_t (&vraw)[4], int G) {
-        const int c0 = 4 * G;
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
         float pg[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -510,8 +476,8 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         const u32x4_t pp = split_hi_lo(pg[0], pg[1], pg[2], pg[3]);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          const int c = c0 + cc;                  // 32-column chunk (tiles 2c, 2c + 1)
-          const uint32_t w0 = vraw[cc][0], w1 = vraw[cc][1];
+          const int c = 4 * G + cc;               // 32-column chunk (tiles 2c, 2c + 1)
+          const uint32_t w0 = vr[c][0], w1 = vr[c][1];
           const uint32_t l0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
           const uint32_t l1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
           const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
@@ -521,36 +487,16 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           o[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4_t{h0, h1, h0, h1}),
                                                                  __builtin_bit_cast(bf16x8_t, pp), o[2 * c + 1], 0, 0, 0);
         }
-      };
-      {
-        u32x2_t v[4];
-        lds_read_f8v4<0>(v, st + f8_v);
-        group(v, 0);
-      }
-      {
-        u32x2_t v[4];
-        lds_read_f8v4<1>(v, st + f8_v);
-        group(v, 1);
-      }
-      {
-        u32x2_t v[4];
-        lds_read_f8v4<2>(v, st + f8_v);
-        group(v, 2);
-      }
-      {
-        u32x2_t v[4];
-        lds_read_f8v4<3>(v, st + f8_v);
-        refill();
-        group(v, 3);
       }
     };
 
     if constexpr (FP8) {
       // ---- FP8 rows: three stages per wave; block k is in stage k % 3 while blocks k + 1
-      // and k + 2 are in flight; its codes are read into registers, then the stage is
-      // refilled with block k + 3.  S^T takes K = code * scale from the conversion (which
-      // applies the scale's exponent); O^T takes V^T = code and folds each token's group
-      // scale 2^e into P (exact for powers of two): O^T[d] += sum_t code[t][d] (p_t 2^e[t][d/128]).
+      // and k + 2 are in flight.  All of block k's operands are read from the stage (the
+      // compiler interleaves the reads with the S^T MFMAs), then the stage is refilled with
+      // block k + 3.  S^T takes K = code * scale from the conversion (which applies the
+      // scale's exponent); O^T takes V^T = code and folds each token's group scale 2^e into
+      // P (exact for powers of two): O^T[d] += sum_t code[t][d] (p_t 2^e[t][d/128]).
       uint32_t okq = 0;   // bit i: the table entry of the block now in stage i was in range
 #pragma unroll
       for (int i = 0; i < kF8Stages; ++i) {
@@ -560,107 +506,87 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       }
       int k = 0;
       while (k < my_n) {
-       float s[4], mx = 0.f;
-       bool rescale = false;
-       for (; k < my_n; ++k) {
-        const int slot = k % kF8Stages;
-        LDS_AS uint8_t* const st = stage0 + slot * kF8Stage;
-        const int after = min(kF8Stages - 1, my_n - 1 - k);   // blocks issued after block k
-        if (after >= 2)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kF8Loads) : "memory");
-        else if (after == 1)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kF8Loads) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        const bool ok = (okq >> slot) & 1u;
-        // refill the stage with block k + 3 once block k's codes are in registers
-        auto refill = [&] {
-          bool nok = true;
-          if (k + kF8Stages < my_n) issue(source(k + kF8Stages, nok), st);
-          okq = (okq & ~(1u << slot)) | ((nok ? 1u : 0u) << slot);
-        };
-        // A block whose table entry was out of range (its DMA read page 0) takes the same
-        // path with every row zeroed and every score masked, so it adds nothing; one loop
-        // body without a skip keeps the accumulators in place across iterations.
-        if (!ok && lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int tok0 = tb + kBlock * blk_of(k);
-        const int vvalid = ok ? te - tok0 : 0;    // rows of the block inside the piece
-        if (vvalid < kBlock) {
-          // rows vvalid..15 may hold anything: zero their codes, rope and scales in the stage
-          for (int u = (kF8Row / 16) * vvalid + lane; u < kF8Units; u += 64)
-            *(LDS_AS u32x4_t*)(st + 16 * u) = u32x4_t{0u, 0u, 0u, 0u};
-        }
-        // S^T = K Q^T from the codes (two batches of 8 k-steps, then the rope columns)
-        f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        u32x4_t ksc;
-        auto kstep = [&](const u32x2_t (&kraw)[8], const u32x4_t (&qv)[8], int kk0) {
+        float s[4], mx = 0.f;
+        bool rescale = false;
+        u32x2_t vr[16];
+        u32x4_t psc[4];
+        for (; k < my_n; ++k) {
+          const int slot = k % kF8Stages;
+          LDS_AS uint8_t* const st = stage0 + slot * kF8Stage;
+          const int after = min(kF8Stages - 1, my_n - 1 - k);   // blocks issued after block k
+          if (after >= 2)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kF8Loads) : "memory");
+          else if (after == 1)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kF8Loads) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          const bool ok = (okq >> slot) & 1u;
+          // A block whose table entry was out of range (its DMA read page 0) takes the same
+          // path with every row zeroed and every score masked, so it adds nothing; one loop
+          // body without a skip keeps the accumulators in place across iterations.
+          if (!ok && lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int tok0 = tb + kBlock * blk_of(k);
+          const int vvalid = ok ? te - tok0 : 0;    // rows of the block inside the piece
+          if (vvalid < kBlock) {
+            // rows vvalid..15 may hold anything: zero their codes, rope and scales in the stage
+            for (int u = (kF8Row / 16) * vvalid + lane; u < kF8Units; u += 64)
+              *(LDS_AS u32x4_t*)(st + 16 * u) = u32x4_t{0u, 0u, 0u, 0u};
+          }
+          // block k's operands
+          const u32x4_t ksc = lds_ld128(st + f8_s);
+          u32x2_t kr[16];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int kk = kk0 + i;
+          for (int i = 0; i < 16; ++i) kr[i] = lds_ld64(st + f8_k + 32 * i);
+          const u32x4_t rope0 = lds_ld128(st + f8_r), rope1 = lds_ld128(st + f8_r + 64);
+#pragma unroll
+          for (int c = 0; c < 16; ++c) vr[c] = lds_tr8(st + f8_v + 32 * c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) psc[i] = lds_ld128(st + f8_p + kF8Row * i);
+          // S^T = K Q^T: 16 k-steps from the codes, then the two rope k-steps
+          f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk) {
             const float sc = __uint_as_float(ksc[kk >> 2]);
             u32x4_t kf;
-            kf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kraw[i][0], sc, false));
-            kf[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kraw[i][0], sc, true));
-            kf[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kraw[i][1], sc, false));
-            kf[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kraw[i][1], sc, true));
+            kf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[kk][0], sc, false));
+            kf[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[kk][0], sc, true));
+            kf[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[kk][1], sc, false));
+            kf[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[kk][1], sc, true));
             f32x4_t& acc = (kk & 1) ? acc2 : sacc;
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf),
-                                                          __builtin_bit_cast(bf16x8_t, qv[i]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[kk], acc, 0, 0, 0);
           }
-        };
-        LDS_AS const uint8_t* const qp = lds + kF8QOff + kF8QRow * n + 16 * g;
-        {
-          u32x2_t kraw[8];
-          u32x4_t x[2], qv[8];
-          lds_read_f8k8<0>(kraw, x, st + f8_k, nullptr, st + f8_s);
-          lds_read_q8<0>(qv, qp);
-          ksc = x[0];
-          kstep(kraw, qv, 0);
-        }
-        {
-          u32x2_t kraw[8];
-          u32x4_t rope[2], qv[8];
-          lds_read_f8k8<1>(kraw, rope, st + f8_k, st + f8_r, nullptr);
-          lds_read_q8<512>(qv, qp);
-          kstep(kraw, qv, 8);
-          u32x4_t qr[2];
-          lds_read_q2<1024>(qr, qp);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rope[0]),
-                                                         __builtin_bit_cast(bf16x8_t, qr[0]), sacc, 0, 0, 0);
-          acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rope[1]),
-                                                         __builtin_bit_cast(bf16x8_t, qr[1]), acc2, 0, 0, 0);
-        }
-        sacc += acc2;
-        const int nvalid = ok ? lim - tok0 : 0;   // tokens of the block this row sees (may be <= 0)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rope0), qf[16], sacc, 0, 0, 0);
+          acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rope1), qf[17], acc2, 0, 0, 0);
+          // refill the stage with block k + 3 (the DMA waits for the reads above first)
+          {
+            bool nok = true;
+            if (k + kF8Stages < my_n) issue(source(k + kF8Stages, nok), st);
+            okq = (okq & ~(1u << slot)) | ((nok ? 1u : 0u) << slot);
+          }
+          sacc += acc2;
+          const int nvalid = ok ? lim - tok0 : 0;   // tokens of the block this row sees (may be <= 0)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
-        mx = wave_max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-        if (__any(mx > m_ref + kRescaleSlack)) {
-          rescale = true;
-          break;
+          for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
+          mx = wave_max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+          if (__any(mx > m_ref + kRescaleSlack)) {
+            rescale = true;
+            break;
+          }
+          accumulate_f8(s, vr, psc);
         }
-        accumulate_f8(s, st, refill);
-       }
-       if (!rescale) break;
-       {
-        // rare path: a running max grew past the slack; move the reference and rescale
-        // (block k is still in its stage: the stage is refilled by accumulate_f8)
-        const int slot = k % kF8Stages;
-        LDS_AS uint8_t* const st = stage0 + slot * kF8Stage;
-        auto refill = [&] {
-          bool nok = true;
-          if (k + kF8Stages < my_n) issue(source(k + kF8Stages, nok), st);
-          okq = (okq & ~(1u << slot)) | ((nok ? 1u : 0u) << slot);
-        };
-        const bool need = mx > m_ref + kRescaleSlack;
-        const float f = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
-        m_ref = need ? mx : m_ref;
-        lsum *= f;
+        if (!rescale) break;
+        {
+          // rare path: a running max grew past the slack; move the reference and rescale
+          // (block k's operands are still in vr and psc)
+          const bool need = mx > m_ref + kRescaleSlack;
+          const float f = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
+          m_ref = need ? mx : m_ref;
+          lsum *= f;
 #pragma unroll
-        for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
-        accumulate_f8(s, st, refill);
-        ++k;
-       }
+          for (int mb = 0; mb < kVBlocks; ++mb) o[mb] *= f;
+          accumulate_f8(s, vr, psc);
+          ++k;
+        }
       }
     } else {
     bool ok0 = true, ok1 = true;   // table entry of the block now in each stage was in range
