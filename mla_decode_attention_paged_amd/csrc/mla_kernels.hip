@@ -160,52 +160,6 @@ __device__ __forceinline__ void lds_read_tr8(u32x2_t (&r)[8], LDS_AS const uint8
 // one chunk) and the V^T transpose reads over all LDS banks.
 __device__ __forceinline__ int row_swz(int t) { return ((t & 2) << 1) | ((t & 4) >> 1); }
 
-// K operand reads of the row-major layout: k-steps K0..K0+8, even ones at pe + 2048*(kk/2),
-// odd ones at po + 2048*(kk/2)
-template <int K0>
-__device__ __forceinline__ void lds_read_k9(u32x4_t (&r)[9], LDS_AS const uint8_t* pe, LDS_AS const uint8_t* po) {
-  if constexpr (K0 == 0) {
-    asm volatile(
-        "ds_read_b128 %0, %9 offset:0\n\tds_read_b128 %1, %10 offset:0\n\tds_read_b128 %2, %9 offset:2048\n\t"
-        "ds_read_b128 %3, %10 offset:2048\n\tds_read_b128 %4, %9 offset:4096\n\tds_read_b128 %5, %10 offset:4096\n\t"
-        "ds_read_b128 %6, %9 offset:6144\n\tds_read_b128 %7, %10 offset:6144\n\tds_read_b128 %8, %9 offset:8192\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8])
-        : "v"(pe), "v"(po)
-        : "memory");
-  } else {
-    static_assert(K0 == 9, "two halves");
-    asm volatile(
-        "ds_read_b128 %0, %10 offset:8192\n\tds_read_b128 %1, %9 offset:10240\n\tds_read_b128 %2, %10 offset:10240\n\t"
-        "ds_read_b128 %3, %9 offset:12288\n\tds_read_b128 %4, %10 offset:12288\n\tds_read_b128 %5, %9 offset:14336\n\t"
-        "ds_read_b128 %6, %10 offset:14336\n\tds_read_b128 %7, %9 offset:16384\n\tds_read_b128 %8, %10 offset:16384\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8])
-        : "v"(pe), "v"(po)
-        : "memory");
-  }
-}
-// V^T transpose reads of the row-major layout: column blocks mb = 16*H .. 16*H+15, block mb at
-// p[mb % 4] + 2048 * (mb / 4)
-template <int H>
-__device__ __forceinline__ void lds_read_v16(u32x2_t (&r)[16], LDS_AS const uint8_t* const (&p)[4]) {
-  constexpr int B = 8192 * H;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16 offset:%20\n\tds_read_b64_tr_b16 %1, %17 offset:%20\n\t"
-      "ds_read_b64_tr_b16 %2, %18 offset:%20\n\tds_read_b64_tr_b16 %3, %19 offset:%20\n\t"
-      "ds_read_b64_tr_b16 %4, %16 offset:%21\n\tds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
-      "ds_read_b64_tr_b16 %6, %18 offset:%21\n\tds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
-      "ds_read_b64_tr_b16 %8, %16 offset:%22\n\tds_read_b64_tr_b16 %9, %17 offset:%22\n\t"
-      "ds_read_b64_tr_b16 %10, %18 offset:%22\n\tds_read_b64_tr_b16 %11, %19 offset:%22\n\t"
-      "ds_read_b64_tr_b16 %12, %16 offset:%23\n\tds_read_b64_tr_b16 %13, %17 offset:%23\n\t"
-      "ds_read_b64_tr_b16 %14, %18 offset:%23\n\tds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
-        "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), MLA_O4(B, 2048)
-      : "memory");
-}
-
 // LDS reads the compiler schedules and counts itself (lgkmcnt), so that reads of a block
 // overlap the MFMAs of the same block.  Its stages are filled by dma_f8_block (asm): the
 // compiler does not see those LDS writes, so it adds no wait for them before a read; the
@@ -266,6 +220,88 @@ __device__ __forceinline__ void dma_f8_block(const uint8_t* row0, uint32_t voff,
   }
 #undef MLA_F8_DMA
 #undef MLA_F8_DMA_TAIL
+}
+
+// One bf16 block into an LDS stage: 18 loads of 16 B per lane, load j reading chunk block
+// j / 2 (bytes 128 (j / 2) ..) of the lane's row for even (p0) or odd (p1) loads and
+// writing 1 KB at stage + 1024 j.  The instruction offset (128 (j / 2)) applies to the
+// global and the LDS address alike, so M0 is stepped to stage + 1024 j - 128 (j / 2)
+// before each load (saved and restored around them).  Like dma_f8_block it first waits
+// for the LDS reads issued before it, and it is hidden from the compiler's counters.
+template <bool NT>
+__device__ __forceinline__ void dma_bf16_block(const uint16_t* p0, const uint16_t* p1, uint32_t lds) {
+  uint32_t sv;
+#define MLA_BF16_DMA(NTS)                                                                         \
+  asm volatile(                                                                                   \
+      "s_waitcnt lgkmcnt(0)\n\t"                                                              \
+      "s_mov_b32 %0, m0\n\t"                                                              \
+      "s_mov_b32 m0, %3\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %1, off" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 1024\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %2, off" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 896\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %1, off offset:128" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 1024\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %2, off offset:128" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 896\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %1, off offset:256" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 1024\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %2, off offset:256" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 896\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %1, off offset:384" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 1024\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %2, off offset:384" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 896\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %1, off offset:512" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 1024\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %2, off offset:512" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 896\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %1, off offset:640" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 1024\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %2, off offset:640" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 896\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %1, off offset:768" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 1024\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %2, off offset:768" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 896\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %1, off offset:896" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 1024\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %2, off offset:896" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 896\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %1, off offset:1024" NTS "\n\t"                                                   \
+      "s_add_u32 m0, m0, 1024\n\t"                                                              \
+      "s_nop 0\n\t"                                                              \
+      "global_load_lds_dwordx4 %2, off offset:1024" NTS "\n\t"                                                   \
+      "s_mov_b32 m0, %0\n\t"                                                              \
+      : "=&s"(sv)                                                                                 \
+      : "v"(p0), "v"(p1), "s"(lds)                                                                \
+      : "memory", "scc")
+  if constexpr (NT)
+    MLA_BF16_DMA(" nt");
+  else
+    MLA_BF16_DMA("");
+#undef MLA_BF16_DMA
+}
+// gfx950 LDS transpose read of 16-bit elements (the V^T operand)
+__device__ __forceinline__ u32x2_t lds_tr16(LDS_AS const uint8_t* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)p));
 }
 
 // Split-decode kernel: 16 query rows per work-group (R = 16 * row groups).  FP8: the cache
@@ -391,41 +427,36 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           dma_f8_block<true>(src.row0, 16u * lane, l, lane < 16);
         else
           dma_f8_block<false>(src.row0, 16u * lane, l, lane < 16);
-      } else if (stream) {
-#pragma unroll
-        for (int j = 0; j < kLoadsPerBlock; ++j)
-          __builtin_amdgcn_global_load_lds((GLB_AS void*)(src.p[j & 1] + 64 * (j >> 1)),
-                                           (LDS_AS void*)(stage + 1024 * j), 16, 0, kKvLoadStream);
       } else {
-#pragma unroll
-        for (int j = 0; j < kLoadsPerBlock; ++j)
-          __builtin_amdgcn_global_load_lds((GLB_AS void*)(src.p[j & 1] + 64 * (j >> 1)),
-                                           (LDS_AS void*)(stage + 1024 * j), 16, 0, kKvLoadReuse);
+        const uint32_t l = (uint32_t)(uintptr_t)stage;
+        if (stream)
+          dma_bf16_block<true>(src.p[0], src.p[1], l);
+        else
+          dma_bf16_block<false>(src.p[0], src.p[1], l);
       }
     };
-    // Every LDS read of a block first (K for S^T, then all of V^T into registers); then the
-    // stage is refilled with the block after next (`ns`, if `nx`) while S^T, the softmax
-    // and O^T += V^T P^T are still being computed.
+    // S^T for one block and its V^T operands: the K and V^T reads are ordinary LDS loads the
+    // compiler interleaves with the S^T MFMAs; then the stage is refilled with the block after
+    // next (`ns`, if `nx`; the DMA first waits for the reads) while the softmax and
+    // O^T += V^T P^T are computed.
     auto scores = [&](LDS_AS uint8_t* st, f32x4_t& sacc, u32x2_t (&vf0)[16], u32x2_t (&vf1)[16], const Src& ns,
                       bool nx) {
+      u32x4_t kf[kKSteps];
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) kf[kk] = lds_ld128(st + ((kk & 1) ? k_odd : k_even) + 2048 * (kk >> 1));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        vf0[i] = lds_tr16(st + v_base[i & 3] + 2048 * (i >> 2));          // columns 0..255
+        vf1[i] = lds_tr16(st + v_base[i & 3] + 8192 + 2048 * (i >> 2));   // columns 256..511
+      }
       f32x4_t acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
       sacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      auto mma = [&](const u32x4_t* kf, int kk0) {
 #pragma unroll
-        for (int i = 0; i < 9; ++i) {
-          f32x4_t& acc = ((kk0 + i) & 1) ? acc2 : sacc;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[i]), qf[kk0 + i], acc, 0, 0, 0);
-        }
-      };
-      u32x4_t kf[9];
-      lds_read_k9<0>(kf, st + k_even, st + k_odd);
-      mma(kf, 0);
-      lds_read_k9<9>(kf, st + k_even, st + k_odd);
-      LDS_AS const uint8_t* const vp[4] = {st + v_base[0], st + v_base[1], st + v_base[2], st + v_base[3]};
-      lds_read_v16<0>(vf0, vp);                // columns 0..255
-      lds_read_v16<1>(vf1, vp);                // columns 256..511
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        f32x4_t& acc = (kk & 1) ? acc2 : sacc;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]), qf[kk], acc, 0, 0, 0);
+      }
       if (nx) issue(ns, st);
-      mma(kf, 9);
       sacc += acc2;
     };
     // O^T += V^T P^T for one block, p = exp2(s - m_ref).  p is split into two bf16
