@@ -67,7 +67,7 @@ constexpr int kKvLoadStream = 2;   // nt
 constexpr int kKvLoadReuse = 0;
 constexpr float kRescaleSlack = 8.0f;              // lazy rescale threshold (log2 units)
 constexpr int kMinBlocks = kWaves;                 // device schedule: fewest blocks per work-group
-constexpr int kMergeBatch = 8;                     // partial results read at a time when merging
+constexpr int kMergeBatch = 16;                    // partial results read at a time when merging
 constexpr float kNegBig = -1.0e30f;                // running-max start value (finite)
 constexpr int kMergeStride = kDv + 4;              // floats per row in the merge buffer
 // the four waves' states when a piece ends: o [4][16][kMergeStride] plus m and l [4][16]
@@ -470,15 +470,26 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
         lsum += p[i];
       }
-      // one 16x16x32 MFMA per column block: K index 8g + j is token 4g + (j & 3), taking
-      // p's hi part for j < 4 and its lo part for j >= 4, against V^T repeated twice
-      const u32x4_t pp = split_hi_lo(p[0], p[1], p[2], p[3]);
       auto pv = [&](const u32x2_t (&vf)[16], int mb0) {
+        if constexpr (OUT_F32) {
+          // fp32 output: one 16x16x32 MFMA per column block, K index 8g + j being token
+          // 4g + (j & 3) with p's hi part for j < 4 and its lo part for j >= 4, against V^T
+          // repeated twice
+          const u32x4_t pp = split_hi_lo(p[0], p[1], p[2], p[3]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const u32x4_t v = u32x4_t{vf[i][0], vf[i][1], vf[i][0], vf[i][1]};
-          o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v),
-                                                               __builtin_bit_cast(bf16x8_t, pp), o[mb0 + i], 0, 0, 0);
+          for (int i = 0; i < 16; ++i) {
+            const u32x4_t v = u32x4_t{vf[i][0], vf[i][1], vf[i][0], vf[i][1]};
+            o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v),
+                                                                 __builtin_bit_cast(bf16x8_t, pp), o[mb0 + i], 0, 0, 0);
+          }
+        } else {
+          // bf16 output: p in bf16, one 16x16x16 MFMA per column block (K index 4g + j is
+          // token 4g + j)
+          const u32x2_t pp = u32x2_t{bf16x2_rne(p[0], p[1]), bf16x2_rne(p[2], p[3])};
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            o[mb0 + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, vf[i]),
+                                                                   __builtin_bit_cast(i16x4_t, pp), o[mb0 + i], 0, 0, 0);
         }
       };
       pv(vf0, 0);
@@ -504,7 +515,10 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           pg[i] = p[i] * __uint_as_float(psc[i][G] & 0x7F800000u);
-        const u32x4_t pp = split_hi_lo(pg[0], pg[1], pg[2], pg[3]);
+        // fp32 output: p 2^e as hi + lo on the K axis of a 16x16x32 MFMA (as on the bf16
+        // path); bf16 output: p 2^e in bf16 on a 16x16x16 MFMA
+        const u32x4_t pp = OUT_F32 ? split_hi_lo(pg[0], pg[1], pg[2], pg[3])
+                                   : u32x4_t{bf16x2_rne(pg[0], pg[1]), bf16x2_rne(pg[2], pg[3]), 0u, 0u};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
           const int c = 4 * G + cc;               // 32-column chunk (tiles 2c, 2c + 1)
@@ -513,10 +527,18 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           const uint32_t l1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
           const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
           const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
-          o[2 * c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4_t{l0, l1, l0, l1}),
-                                                             __builtin_bit_cast(bf16x8_t, pp), o[2 * c], 0, 0, 0);
-          o[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4_t{h0, h1, h0, h1}),
-                                                                 __builtin_bit_cast(bf16x8_t, pp), o[2 * c + 1], 0, 0, 0);
+          if constexpr (OUT_F32) {
+            o[2 * c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4_t{l0, l1, l0, l1}),
+                                                               __builtin_bit_cast(bf16x8_t, pp), o[2 * c], 0, 0, 0);
+            o[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4_t{h0, h1, h0, h1}),
+                                                                   __builtin_bit_cast(bf16x8_t, pp), o[2 * c + 1], 0, 0, 0);
+          } else {
+            const i16x4_t pb = __builtin_bit_cast(i16x4_t, u32x2_t{pp[0], pp[1]});
+            o[2 * c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, u32x2_t{l0, l1}), pb,
+                                                                 o[2 * c], 0, 0, 0);
+            o[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, u32x2_t{h0, h1}), pb,
+                                                                     o[2 * c + 1], 0, 0, 0);
+          }
         }
       }
     };
@@ -1097,6 +1119,28 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
   }
 }
 
+// Log-sum-exp merge of one batch of partial results into a running (M, L, acc): with
+// M' = max(M, l_u), acc and L are scaled by e^(M - M') and each partial u adds
+// w_u = e^(l_u - M') times its o (and w_u to L).  Partials with l = -inf (no tokens) add
+// nothing.
+__device__ __forceinline__ void merge_batch(const float (&l)[kMergeBatch], const f32x4_t (&v)[kMergeBatch],
+                                            float& M, float& L, f32x4_t& acc) {
+  float mb = M;
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, l[u]);
+  if (mb == -INFINITY) return;
+  const float f = M > -INFINITY ? __expf(M - mb) : 0.f;
+  L *= f;
+  acc *= f;
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const float w = (l[u] > -INFINITY) ? __expf(l[u] - mb) : 0.f;
+    L += w;
+    acc += w * v[u];
+  }
+  M = mb;
+}
+
 // Merge of split sequences.  One work-group per (sequence, 16 query rows, 64
 // output columns): thread (r, q) merges row r, columns 4q..4q+3 of the slice over
 // all of the sequence's partial results, so every partial byte is read once and
@@ -1118,34 +1162,20 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   const int d = cg * kMergeCols + 4 * (threadIdx.x & 15);
   const float* lse_col = a.part_lse + (int64_t)s0 * R + r;                 // stride R per slot
   const float* o_col = a.part_o + ((int64_t)s0 * R + r) * kDv + d;         // stride R*512 per slot
-  // loads are issued kMergeBatch at a time so their latencies overlap
-  float M = -INFINITY;
+  // one pass: kMergeBatch partial results (their lse and 4 columns of o) are loaded at once,
+  // so the loads of a batch overlap; the running max moves per batch
+  float M = -INFINITY, L = 0.f;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < ns; s += kMergeBatch) {
     float l[kMergeBatch];
+    f32x4_t v[kMergeBatch];
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) l[u] = (s + u < ns) ? lse_col[(int64_t)(s + u) * R] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) M = fmaxf(M, l[u]);
-  }
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M > -INFINITY) {
-    for (int s = 0; s < ns; s += kMergeBatch) {
-      float l[kMergeBatch];
-      f32x4_t v[kMergeBatch];
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const bool in = s + u < ns;
-        l[u] = in ? lse_col[(int64_t)(s + u) * R] : -INFINITY;
-        v[u] = in ? *(const f32x4_t*)(o_col + (int64_t)(s + u) * R * kDv) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const float w = (l[u] > -INFINITY) ? __expf(l[u] - M) : 0.f;
-        L += w;
-        acc += w * v[u];
-      }
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const bool in = s + u < ns;
+      l[u] = in ? lse_col[(int64_t)(s + u) * R] : -INFINITY;
+      v[u] = in ? *(const f32x4_t*)(o_col + (int64_t)(s + u) * R * kDv) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    merge_batch(l, v, M, L, acc);
   }
   const f32x4_t v = acc * (L > 0.f ? 1.0f / L : 0.f);
   const int64_t off = ((int64_t)b * R + r) * kDv + d;
@@ -1183,36 +1213,18 @@ __global__ void __launch_bounds__(256) merge_dev_kernel(MergeArgs a) {
   };
   const int r = rg * 16 + (threadIdx.x >> 4);
   const int d = cg * kMergeCols + 4 * (threadIdx.x & 15);
-  float M = -INFINITY;
+  float M = -INFINITY, L = 0.f;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int w0 = wf; w0 <= wl; w0 += kMergeBatch) {
     float l[kMergeBatch];
+    f32x4_t v[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       const int sl = w0 + u <= wl ? slot_of(w0 + u) : -1;
       l[u] = sl >= 0 ? a.part_lse[(int64_t)sl * R + r] : -INFINITY;
+      v[u] = sl >= 0 ? *(const f32x4_t*)(a.part_o + ((int64_t)sl * R + r) * kDv + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) M = fmaxf(M, l[u]);
-  }
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M > -INFINITY) {
-    for (int w0 = wf; w0 <= wl; w0 += kMergeBatch) {
-      float l[kMergeBatch];
-      f32x4_t v[kMergeBatch];
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const int sl = w0 + u <= wl ? slot_of(w0 + u) : -1;
-        l[u] = sl >= 0 ? a.part_lse[(int64_t)sl * R + r] : -INFINITY;
-        v[u] = sl >= 0 ? *(const f32x4_t*)(a.part_o + ((int64_t)sl * R + r) * kDv + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const float w = (l[u] > -INFINITY) ? __expf(l[u] - M) : 0.f;
-        L += w;
-        acc += w * v[u];
-      }
-    }
+    merge_batch(l, v, M, L, acc);
   }
   const f32x4_t v = acc * (L > 0.f ? 1.0f / L : 0.f);
   const int64_t off = ((int64_t)b * R + r) * kDv + d;

@@ -11,7 +11,7 @@ from mla_decode_attention_paged_amd import inputs as gen
 from mla_decode_attention_paged_amd.device import Runner
 from oracle import mla_oracle as orc
 from tests.test_gpu_parity import (F32_LSE_TOL, F32_MAX_TOL, F32_RMSE_TOL, LSE_TOL, MAX_TOL, RMSE_TOL, _say,
-                                   bf16_half_ulp, compare)
+                                   bf16_out_excess, compare, softmax_abs_v)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,14 +29,14 @@ def oracle(prob, batch_idx=None):
                       prob.page_size, batch_indices=batch_idx, causal=True)
 
 
-def check(out, lse, ref_o, ref_l, out_fp32, what):
+def check(out, lse, ref_o, ref_l, out_fp32, what, wabs=None):
     assert np.array_equal(np.isfinite(lse), np.isfinite(ref_l)), f"{what}: lse finiteness differs"
     empty = ~np.isfinite(ref_l)
     assert np.all(lse[empty] == -np.inf) and np.all(out[empty] == 0), f"{what}: empty rows"
     if out_fp32:
         compare(out, lse, ref_o, ref_l, what=what + " fp32", tol=(F32_RMSE_TOL, F32_MAX_TOL, F32_LSE_TOL))
     else:
-        excess = float(np.max(np.abs(out - ref_o) - bf16_half_ulp(ref_o)))
+        excess = bf16_out_excess(out, ref_o, wabs)
         lerr = float(np.max(np.abs(lse[~empty] - ref_l[~empty])))
         _say(f"  {what} bf16: max error beyond bf16 rounding {excess:.3e}, lse {lerr:.3e}")
         assert excess <= F32_MAX_TOL and lerr <= F32_LSE_TOL, (what, excess, lerr)
@@ -49,7 +49,8 @@ def test_causal_edge_lengths(heads, q_len, out_fp32):
                             lengths=EDGE_LENGTHS, seed=21, tail="nan", extra_pages=2, out_fp32=out_fp32)
     out, lse = run(prob)
     ref_o, ref_l = oracle(prob)
-    check(out, lse, ref_o, ref_l, out_fp32, f"causal H={heads} S_q={q_len}")
+    check(out, lse, ref_o, ref_l, out_fp32, f"causal H={heads} S_q={q_len}",
+          None if out_fp32 else softmax_abs_v(prob, causal=True))
 
 
 @pytest.mark.parametrize("heads,q_len", [(8, 2), (16, 2), (64, 2)])
