@@ -104,9 +104,10 @@ typedef struct {
   int32_t num_cus;            /* compute units to plan for; 0 = ask the current HIP device */
   int32_t force_splits;       /* 0 = cost model; k > 0 = cut every sequence into min(k, blocks)
                                  near-equal parts, one work-group each (testing the merge) */
-  int32_t rows_per_group;     /* 0 = automatic; 16, 32 or 64 = query rows per work-group (16: the
+  int32_t rows_per_group;     /* 0 = automatic (64 when R is a multiple of 64 and the cache is
+                                 bf16, else 16); 16, 32 or 64 = query rows per work-group (16: the
                                  16-row kernel in R/16 row groups; 32, 64: the grouped kernel,
-                                 R must be a multiple) -- a tuning and testing knob */
+                                 R must be a multiple, bf16 cache only) -- a tuning and testing knob */
   int32_t reserved[5];        /* must be zero */
 } mla_plan_options_t;
 

@@ -58,13 +58,12 @@ constexpr int kF8Stages = 3;                                   // fp8 stages per
 constexpr int kF8WaveBytes = kF8Stages * kF8Stage;             // 31,488
 constexpr int kSmemFp8 = kWaves * kF8WaveBytes;               // 125,952
 constexpr int kLoadsPerBlock = kBlockBytes / (64 * 16);      // 18 DMA loads per wave per block
-// Cache policy of the KV-cache DMA loads.  With one row group every KV row is read by one
-// work-group only, and the loads carry the non-temporal bit (`nt`): on MI355X a
-// global->LDS stream with `nt` runs at ~6.9 TB/s against ~6.1 TB/s without it (read-only
-// stream of 1.2 GB, 256 work-groups).  With several row groups the work-groups of one token
-// range re-read it through their XCD's L2, and default-policy loads keep it there.
-constexpr int kKvLoadStream = 2;   // nt
-constexpr int kKvLoadReuse = 0;
+// Cache policy of the KV-cache DMA loads (the NT template argument of the dma_* helpers).
+// With one row group every KV row is read by one work-group only, and the loads carry the
+// non-temporal bit (`nt`): on MI355X a global->LDS stream with `nt` runs at ~6.9 TB/s
+// against ~6.1 TB/s without it (read-only stream of 1.2 GB, 256 work-groups).  With several
+// row groups the work-groups of one token range re-read it through their XCD's L2, and
+// default-policy loads keep it there.
 constexpr float kRescaleSlack = 8.0f;              // lazy rescale threshold (log2 units)
 constexpr int kMinBlocks = kWaves;                 // device schedule: fewest blocks per work-group
 constexpr int kMergeBatch = 16;                    // partial results read at a time when merging
@@ -123,37 +122,6 @@ __device__ __forceinline__ u32x4_t split_hi_lo(float p0, float p1, float p2, flo
 }
 
 
-// Batched LDS reads in inline asm, each block waiting for its own reads before it
-// ends.  Outputs are early-clobber: a read can return while later reads of the same
-// block still need their address registers, so no output may share one.  Issuing a batch back to back (instead of one read, one wait) keeps many
-// LDS requests in flight; doing it in asm also keeps the compiler from adding a
-// wait for the in-flight global->LDS prefetch of the other stage before every read.
-#define MLA_O4(b, s) "i"(b), "i"(b + s), "i"(b + 2 * s), "i"(b + 3 * s)
-
-// 16-B reads at p + OFF + 1024*i
-template <int OFF>
-__device__ __forceinline__ void lds_read_b128x6(u32x4_t (&r)[6], LDS_AS const uint8_t* p) {
-  asm volatile(
-      "ds_read_b128 %0, %6 offset:%7\n\tds_read_b128 %1, %6 offset:%8\n\tds_read_b128 %2, %6 offset:%9\n\t"
-      "ds_read_b128 %3, %6 offset:%10\n\tds_read_b128 %4, %6 offset:%11\n\tds_read_b128 %5, %6 offset:%12\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
-      : "v"(p), MLA_O4(OFF, 1024), "i"(OFF + 4096), "i"(OFF + 5120)
-      : "memory");
-}
-// transpose reads (4 tokens x 16 columns per 16 lanes) at p + OFF + 512*i
-template <int OFF>
-__device__ __forceinline__ void lds_read_tr8(u32x2_t (&r)[8], LDS_AS const uint8_t* p) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%9\n\tds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
-      "ds_read_b64_tr_b16 %2, %8 offset:%11\n\tds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\tds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
-      "ds_read_b64_tr_b16 %6, %8 offset:%15\n\tds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(p), MLA_O4(OFF, 512), MLA_O4(OFF + 2048, 512)
-      : "memory");
-}
 // Row-major block layout of the split kernel (16-B units): chunk c of token t sits at
 // 128 * (c / 8) + 8 * t + ((c % 8) ^ row_swz(t)).  One DMA instruction fills 8 tokens x
 // 8 chunks (128 contiguous bytes of each row); the xor spreads the K reads (16 tokens x
@@ -849,6 +817,36 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   }
 }
 
+// Nine loads of one wave's share of a grouped-kernel step: load i reads 16 B per lane at
+// src + 64 i and writes 1 KB at lds + 1024 i.  The instruction offset (64 i) applies to
+// both addresses, so M0 steps by 960 between loads.  As dma_bf16_block: opens with
+// s_waitcnt lgkmcnt(0), saves and restores M0, is hidden from the compiler's counters.
+template <bool NT>
+__device__ __forceinline__ void dma_group_share(const uint16_t* src, uint32_t lds) {
+  uint32_t sv;
+#define MLA_GROUP_DMA(NTS)                                                                        \
+  asm volatile(                                                                                   \
+      "s_waitcnt lgkmcnt(0)\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"               \
+      "global_load_lds_dwordx4 %1, off" NTS "\n\t"                                                \
+      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:64" NTS "\n\t"  \
+      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:128" NTS "\n\t" \
+      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:192" NTS "\n\t" \
+      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:256" NTS "\n\t" \
+      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:320" NTS "\n\t" \
+      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:384" NTS "\n\t" \
+      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:448" NTS "\n\t" \
+      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:512" NTS "\n\t" \
+      "s_mov_b32 m0, %0"                                                                          \
+      : "=&s"(sv)                                                                                 \
+      : "v"(src), "s"(lds)                                                                        \
+      : "memory", "scc")
+  if constexpr (NT)
+    MLA_GROUP_DMA(" nt");
+  else
+    MLA_GROUP_DMA("");
+#undef MLA_GROUP_DMA
+}
+
 // Grouped split-decode kernel for 16 * RG query rows per work-group.  The four
 // waves consume the same KV stream: wave (rg, dh) owns query rows 16*rg..16*rg+15
 // and output columns [512*dh/DH, 512*(dh+1)/DH) with DH = 4 / RG.  Each step is
@@ -865,7 +863,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
   constexpr int SLOTS = kWaves * kStages / SB;          // step slots (4)
   constexpr int LOADS = kLoadsPerBlock * SB / kWaves;   // DMA instructions per wave and step (9)
   constexpr int MBW = kVBlocks / DH;                    // 16-column output blocks per wave
-  static_assert(LOADS * kWaves == kLoadsPerBlock * SB && MBW % 8 == 0, "layout");
+  static_assert(LOADS * kWaves == kLoadsPerBlock * SB && LOADS == 9 && SB == 2 && MBW % 8 == 0, "layout");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
 
@@ -931,41 +929,27 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
       const int t = min(ld_token, te - 1 - tok0);
       return a.kv + (base + t) * kDqk + 8 * g;
     };
+    // Wave w moves block w / 2 of the step, 64-B chunk steps 9 (w % 2) .. 9 (w % 2) + 8 (each
+    // load: 16 tokens x 4 chunks of 16 B).
     auto issue_step = [&](int k) {
-      LDS_AS uint8_t* dst = lds + (k % SLOTS) * (SB * kBlockBytes);
-      const uint16_t* src0 = source(k * SB);
-      const uint16_t* src1 = source(k * SB + 1);
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int I = wave + kWaves * i;                // the step's I-th DMA (of 36)
-        const int j = I / kLoadsPerBlock, jj = I % kLoadsPerBlock;
-        const uint16_t* src = j ? src1 : src0;
-        if (stream)
-          __builtin_amdgcn_global_load_lds((GLB_AS void*)(src + 32 * jj),
-                                           (LDS_AS void*)(dst + j * kBlockBytes + 1024 * jj), 16, 0, kKvLoadStream);
-        else
-          __builtin_amdgcn_global_load_lds((GLB_AS void*)(src + 32 * jj),
-                                           (LDS_AS void*)(dst + j * kBlockBytes + 1024 * jj), 16, 0, kKvLoadReuse);
-      }
+      const int j = wave >> 1, jj0 = LOADS * (wave & 1);
+      const uint16_t* src = source(k * SB + j) + 32 * jj0;
+      const uint32_t dst = (uint32_t)(uintptr_t)(lds + (k % SLOTS) * (SB * kBlockBytes) + j * kBlockBytes + 1024 * jj0);
+      if (stream)
+        dma_group_share<true>(src, dst);
+      else
+        dma_group_share<false>(src, dst);
     };
     // S^T = K Q^T for one 16-token block: this lane's 4 scaled scores (log2 units)
     auto scores = [&](LDS_AS uint8_t* st, int nvalid, float* s) {
       f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      u32x4_t kf[6];
       LDS_AS const uint8_t* kp = st + k_lane;
-      auto mma = [&](int kk0) {
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
-          f32x4_t& acc = (i & 1) ? acc2 : sacc;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[i]), qf[kk0 + i], acc, 0, 0, 0);
-        }
-      };
-      lds_read_b128x6<0>(kf, kp);
-      mma(0);
-      lds_read_b128x6<6144>(kf, kp);
-      mma(6);
-      lds_read_b128x6<12288>(kf, kp);
-      mma(12);
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        f32x4_t& acc = (kk & 1) ? acc2 : sacc;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lds_ld128(kp + 1024 * kk)), qf[kk],
+                                                      acc, 0, 0, 0);
+      }
       sacc += acc2;
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
@@ -973,51 +957,33 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
     // O^T += V^T P^T for this wave's columns over the step's 32 tokens.  The contraction
     // index k = 8g + j is token 4g + j of the first block (j < 4) or 4g + j - 4 of the
     // second: what the S^T layout leaves in this lane and what one transpose read per
-    // block delivers.  A block that is not used contributes a zero V^T half.
-    // p = exp2(s - m_ref) goes in as bf16 hi + lo (about 16 mantissa bits).
-    auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[8], bool use0, bool use1) {
+    // block delivers (an unused block's V^T columns were zeroed in the slot).
+    // p = exp2(s - m_ref) goes in as bf16 (bf16 output) or as bf16 hi + lo, two MFMAs
+    // (fp32 output, about 16 mantissa bits).
+    auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[8]) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
         lsum += p[i];
       }
-      const u32x4_t q0 = split_hi_lo(p[0], p[1], p[2], p[3]), q1 = split_hi_lo(p[4], p[5], p[6], p[7]);
-      const u32x4_t ph = u32x4_t{q0[0], q0[1], q1[0], q1[1]}, pl = u32x4_t{q0[2], q0[3], q1[2], q1[3]};
-      const uint32_t keep0 = use0 ? 0xFFFFFFFFu : 0u, keep1 = use1 ? 0xFFFFFFFFu : 0u;
+      u32x4_t ph, pl;
+      if constexpr (OUT_F32) {
+        const u32x4_t q0 = split_hi_lo(p[0], p[1], p[2], p[3]), q1 = split_hi_lo(p[4], p[5], p[6], p[7]);
+        ph = u32x4_t{q0[0], q0[1], q1[0], q1[1]};
+        pl = u32x4_t{q0[2], q0[3], q1[2], q1[3]};
+      } else {
+        ph = u32x4_t{bf16x2_rne(p[0], p[1]), bf16x2_rne(p[2], p[3]), bf16x2_rne(p[4], p[5]), bf16x2_rne(p[6], p[7])};
+      }
       LDS_AS const uint8_t* vp0 = st + v_lane;
       LDS_AS const uint8_t* vp1 = st + kBlockBytes + v_lane;
-      u32x2_t va[8], vb[8];
-      auto pv = [&](int mbl) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          u32x4_t v;
-          v[0] = va[i][0] & keep0;
-          v[1] = va[i][1] & keep0;
-          v[2] = vb[i][0] & keep1;
-          v[3] = vb[i][1] & keep1;
-          const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, v);
-          o[mbl + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, ph), o[mbl + i], 0,
-                                                               0, 0);
-          o[mbl + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, pl), o[mbl + i], 0,
-                                                               0, 0);
-        }
-      };
-      lds_read_tr8<0>(va, vp0);
-      lds_read_tr8<0>(vb, vp1);
-      pv(0);
-      if constexpr (MBW > 8) {
-        lds_read_tr8<4096>(va, vp0);
-        lds_read_tr8<4096>(vb, vp1);
-        pv(8);
-      }
-      if constexpr (MBW > 16) {
-        lds_read_tr8<8192>(va, vp0);
-        lds_read_tr8<8192>(vb, vp1);
-        pv(16);
-        lds_read_tr8<12288>(va, vp0);
-        lds_read_tr8<12288>(vb, vp1);
-        pv(24);
+      for (int mb = 0; mb < MBW; ++mb) {
+        const u32x2_t va = lds_tr16(vp0 + 512 * mb), vb = lds_tr16(vp1 + 512 * mb);
+        const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, u32x4_t{va[0], va[1], vb[0], vb[1]});
+        o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, ph), o[mb], 0, 0, 0);
+        if constexpr (OUT_F32)
+          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, pl), o[mb], 0, 0, 0);
       }
     };
 
@@ -1038,7 +1004,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         // step k is in LDS (each wave waited for its own DMA) and every wave is done with
         // step k-1, whose slot the prefetch below overwrites.  A bare s_barrier: a fenced
         // __syncthreads would also wait for the prefetches still in flight.
-        asm volatile("" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (k + SLOTS - 1 < steps) issue_step(k + SLOTS - 1);
@@ -1053,6 +1019,14 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         }
         if (!use0 && !use1) continue;
         st = lds + (k % SLOTS) * (SB * kBlockBytes);
+        if (!use0 || !use1) {
+          // rare: one block of the step is past the end or has an out-of-range table entry
+          // (its rows may hold anything): zero the V^T columns this wave reads in that block,
+          // 2 chunks of 16 tokens x 16 B per 16-column block (every wave that reads them writes
+          // the same zeros first)
+          LDS_AS uint8_t* zb = st + (use0 ? kBlockBytes : 0) + 512 * mb0;
+          for (int u = lane; u < 32 * MBW; u += 64) *(LDS_AS u32x4_t*)(zb + 16 * u) = u32x4_t{0u, 0u, 0u, 0u};
+        }
         scores(st, use0 ? lim - tok0 : 0, s);
         scores(st + kBlockBytes, use1 ? lim - tok1 : 0, s + 4);
         float m8 = s[0];
@@ -1063,7 +1037,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
           rescale = true;
           break;
         }
-        accumulate(st, s, use0, use1);
+        accumulate(st, s);
       }
       if (!rescale) break;
       // rare path: the running max grew past the slack; move the reference and rescale
@@ -1074,7 +1048,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         lsum *= f;
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) o[mb] *= f;
-        accumulate(st, s, use0, use1);
+        accumulate(st, s);
         ++k;
       }
     }

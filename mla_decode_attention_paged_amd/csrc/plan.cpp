@@ -34,13 +34,17 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
   const int32_t B = p.batch;
   const int64_t R = (int64_t)p.q_len * p.num_heads;
   pl.rows = (int32_t)R;
-  // query rows per work-group: 16 (one wave each), 32 or 64 (grouped waves sharing KV);
-  // more rows run as several row groups over the same token ranges
-  // Rows per work-group: 16 by default (the 16-row kernel, in R/16 row groups whose
-  // work-groups share a token range on one XCD).  Measured on MI355X, it beats the
-  // grouped kernel at R = 32 by ~30% and matches it at R = 64 and 128; 32 or 64 can
-  // still be asked for.
-  pl.rows_per_group = rows_per_group != 0 ? rows_per_group : 16;
+  // Query rows per work-group: 16 (the 16-row kernel, one wave per 16-token block, in R/16
+  // row groups whose work-groups share a token range on one XCD), or 32 / 64 (the grouped
+  // kernel: four waves share each 32-token step in LDS).  When not asked for: 64 if R is a
+  // multiple of 64 and the cache is bf16, else 16.  Measured on MI355X: at R = 128 (ragged
+  // workload) 64 rows per work-group take 1,178 us against 1,380 us with 16; at R = 32
+  // (two-token workload) 16 rows take 122 us against 159 us with 32.  Larger rows come in
+  // as more row groups over the same token ranges.
+  if (rows_per_group != 0)
+    pl.rows_per_group = rows_per_group;
+  else
+    pl.rows_per_group = (R % 64 == 0 && p.kv_dtype != MLA_KV_FP8_E4M3) ? 64 : 16;
   pl.row_groups = (int32_t)(R / pl.rows_per_group);
   pl.granule = kBlock;
 

@@ -227,10 +227,11 @@ def test_more_query_rows(heads, q_len):
 
 
 @pytest.mark.parametrize("heads,q_len,rpg", [(16, 2, 32), (32, 1, 32), (64, 1, 64), (128, 1, 64), (16, 4, 64),
-                                          (64, 2, 64)])
+                                          (64, 2, 64), (128, 1, 16), (64, 1, 16)])
 @pytest.mark.parametrize("out_fp32", [True, False])
 def test_grouped_kernel(heads, q_len, rpg, out_fp32):
-    """The grouped kernel (32 or 64 rows per work-group), asked for through the plan option."""
+    """Rows per work-group asked for through the plan option: the grouped kernel (32 or 64),
+    and the 16-row kernel in several row groups where 64 would be chosen by default."""
     prob = gen.make_problem(batch=4, q_len=q_len, num_heads=heads, page_size=64, lengths=[700, 2000, 33, 1],
                             seed=18, tail="nan", extra_pages=1, out_fp32=out_fp32)
     r = Runner(prob, rows_per_group=rpg)
