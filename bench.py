@@ -287,7 +287,8 @@ def main():
                    "parallelism": "single GPU, split-KV over 256 CUs"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "split_decode_kernel", "kernel_us": round(split_us, 2),
+                     "kernel": "split_decode_kernel" if info["rows_per_group"] == 16 else "group_decode_kernel",
+                     "kernel_us": round(split_us, 2),
                      "algorithmic_bytes_per_launch": algo},
         "timing_us": {"call_event_p10": round(float(np.percentile(call_us, 10)), 2),
                       "call_event_p50": round(float(np.percentile(call_us, 50)), 2),
