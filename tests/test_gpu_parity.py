@@ -276,6 +276,27 @@ def test_out_of_range_block_table_entry_is_flagged():
     check_dropped_page(prob, out, lse, seq=1, page_idx=3)
 
 
+@pytest.mark.parametrize("heads,rpg", [(128, 0), (32, 32), (64, 16)])
+def test_out_of_range_entry_drops_one_block(heads, rpg):
+    """Page size 16 (one block per page): an out-of-range entry makes one block of a 32-token
+    step of the grouped kernel unused (the first block of a step in sequence 0, the second in
+    sequence 1); its tokens are dropped and the status bit is set.  Unmapped pages hold NaN."""
+    prob = gen.make_problem(batch=2, q_len=1, num_heads=heads, page_size=16, lengths=[640, 650], seed=22,
+                            tail="nan", extra_pages=2)
+    bt = prob.block_table.copy()
+    bt[0, 10] = -1
+    bt[1, 5] = prob.num_pages + 3
+    bad = gen.Problem(q=prob.q, kv_cache=prob.kv_cache, block_table=bt, cache_seqlens=prob.cache_seqlens,
+                      softmax_scale=prob.softmax_scale, page_size=16)
+    r = Runner(bad, rows_per_group=rpg)
+    assert r.plan.info()["rows_per_group"] == (rpg or 64)
+    r()
+    out, lse = r.results()
+    assert B.mla_read_status(r.ws) & 1
+    check_dropped_page(prob, out, lse, seq=0, page_idx=10)
+    check_dropped_page(prob, out, lse, seq=1, page_idx=5)
+
+
 def check_dropped_page(prob, out, lse, seq, page_idx, tol=(RMSE_TOL, MAX_TOL, LSE_TOL)):
     """Sequence `seq` must equal attention over its tokens outside table entry `page_idx`."""
     P, L = prob.page_size, int(prob.cache_seqlens[seq])
