@@ -286,6 +286,7 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
     m.lse = lse;
     m.rows = p.rows;
     m.num_merges = (int32_t)p.merges.size();
+    m.uniform_ns = p.merge_uniform;
     int e = mla::launch_merge(m, f32, stream);
     if (e) return fail(MLA_ERR_HIP, "merge launch: %s", mla::hip_error_string(e));
   }

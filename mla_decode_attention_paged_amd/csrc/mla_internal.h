@@ -48,6 +48,7 @@ struct PlanImpl {
   std::vector<int32_t> worker_off;         // num_workers + 1
   std::vector<Piece> pieces;
   std::vector<MergeItem> merges;
+  int32_t merge_uniform = 0;               // ns when item b merges slots [b*ns, (b+1)*ns) for every b
   std::vector<int64_t> worker_cost;
   int32_t num_partials = 0;
   // workspace layout
@@ -96,6 +97,7 @@ struct MergeArgs {
   float* lse;
   int32_t rows;
   int32_t num_merges;
+  int32_t uniform_ns;            // > 0: item i is sequence i with slots [i*ns, (i+1)*ns)
   const int32_t* seq_info;       // device schedule (merge_dev_kernel)
   int32_t batch;
 };

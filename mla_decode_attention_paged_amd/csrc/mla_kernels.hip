@@ -1128,10 +1128,17 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   const int item = blockIdx.x / per_item;
   const int rem = blockIdx.x % per_item;
   const int rg = rem / col_groups, cg = rem % col_groups;
-  const CST_AS int32_t* merges = as_const(a.merges);
-  const int b = merges[4 * item + 0];
-  const int s0 = merges[4 * item + 1];
-  const int ns = merges[4 * item + 2];
+  int b, s0, ns;
+  if (a.uniform_ns > 0) {          // item i is sequence i with slots [i*ns, (i+1)*ns): no table read
+    b = item;
+    s0 = item * a.uniform_ns;
+    ns = a.uniform_ns;
+  } else {
+    const CST_AS int32_t* merges = as_const(a.merges);
+    b = merges[4 * item + 0];
+    s0 = merges[4 * item + 1];
+    ns = merges[4 * item + 2];
+  }
   const int r = rg * 16 + (threadIdx.x >> 4);
   const int d = cg * kMergeCols + 4 * (threadIdx.x & 15);
   const float* lse_col = a.part_lse + (int64_t)s0 * R + r;                 // stride R per slot

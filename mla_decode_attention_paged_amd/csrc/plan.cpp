@@ -146,6 +146,17 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
     }
   }
   pl.num_partials = slots;
+  // every sequence split into the same number of pieces: the merge kernel can derive its
+  // items from the work-group index instead of reading them
+  if (!pl.merges.empty() && (int64_t)pl.merges.size() == B) {
+    const int32_t ns = pl.merges[0].num_slots;
+    bool uniform = true;
+    for (int b = 0; b < B; ++b) {
+      const MergeItem& mi = pl.merges[b];
+      if (mi.seq != b || mi.slot_begin != b * ns || mi.num_slots != ns) uniform = false;
+    }
+    pl.merge_uniform = uniform ? ns : 0;
+  }
   std::vector<int32_t> next_slot = first_slot;
   pl.worker_off.push_back(0);
   for (auto& v : per_worker) {
