@@ -8,7 +8,10 @@ A step is one mla_decode call (split-decode kernel + merge kernel) over inputs
 already resident in HBM.  Prints one JSON line:
   value      = algorithmic bytes per call / wall time per call  (GB/s, whole job)
   roofline   = the split-decode kernel alone: algorithmic bytes / its mean
-               duration (HIP events on the launch stream) vs 8 TB/s HBM
+               duration (HIP events on the launch stream) vs 8 TB/s HBM, and vs
+               a 1 GiB device-to-device copy timed on the same box
+  timing_us  = per-call event percentiles, the cache-flushed per-call time, the
+               device-scheduled entry point (mla_decode_devplan) on the same inputs
   cpu_baseline = the fp64 oracle on a bounded sample of the same workload, on
                this host's cores (context only)
 
@@ -257,6 +260,39 @@ def main():
     del flush
 
     status = B.mla_read_status(r.ws)
+
+    # the same workload through the device-scheduled entry point (no host plan); FP8 and
+    # every R run there on the 16-row kernel
+    from mla_decode_attention_paged_amd.device import DevplanRunner
+    dr = DevplanRunner(prob, dev=r.dev)
+    for _ in range(10):
+        dr()
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(args.steps):
+        dr()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    devplan_us = d0.elapsed_time(d1) * 1e3 / args.steps
+    del dr
+
+    # read-bandwidth reference on this machine: a 1 GiB device-to-device copy (reads 1 GiB,
+    # writes 1 GiB), best of 10
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    cps = []
+    for _ in range(10):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cps.append(c0.elapsed_time(c1) * 1e-3)
+    copy_gbs = 2 * src.numel() * 4 / min(cps) / 1e9
+    del src, dst
+
     layer = None
     if not args.no_layer:
         print("[bench] timing the steps around the decode", file=sys.stderr, flush=True)
@@ -289,14 +325,17 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "split_decode_kernel" if info["rows_per_group"] == 16 else "group_decode_kernel",
                      "kernel_us": round(split_us, 2),
-                     "algorithmic_bytes_per_launch": algo},
+                     "algorithmic_bytes_per_launch": algo,
+                     "copy_probe_GBps": round(copy_gbs, 1),
+                     "frac_of_copy_probe": round(achieved / copy_gbs, 4)},
         "timing_us": {"call_event_p10": round(float(np.percentile(call_us, 10)), 2),
                       "call_event_p50": round(float(np.percentile(call_us, 50)), 2),
                       "call_event_p90": round(float(np.percentile(call_us, 90)), 2),
                       "call_flushed_p50": round(float(np.median(fl)), 2),
                       "split_kernel_mean": round(split_us, 2),
                       "merge_and_gap_p50": round(float(np.percentile(call_us, 50)) - split_us, 2),
-                      "plan_host_us": round(plan_us, 1)},
+                      "plan_host_us": round(plan_us, 1),
+                      "devplan_call_mean": round(devplan_us, 2)},
         "plan": {k: info[k] for k in ("num_workers", "grid_size", "num_segments", "num_partials", "num_combine")},
         "status_word": status,
         "layer_steps": layer,

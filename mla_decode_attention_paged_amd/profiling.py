@@ -11,6 +11,8 @@ summaries below read its `top_kernels` and `counters_collection` views.
          CALIB_FETCH_DIR CALIB_WRITE_DIR OUT.md "COMMANDS"
       HBM bytes per launch of KERNEL from FETCH_SIZE / WRITE_SIZE passes, each scaled by
       what the same counter reads for the 1 GiB copy; updates profiles/counters.json
+  python -m mla_decode_attention_paged_amd.profiling sq KERNEL BLOCKS OUT.md "COMMANDS" DIR [DIR ...]
+      mean SQ counters per dispatch of KERNEL over `rocprofv3 --pmc SQ_...` passes
 """
 from __future__ import annotations
 
@@ -134,6 +136,41 @@ def counters(config, kernel, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir,
     print("\n".join(lines))
 
 
+def sq(kernel, blocks, out_md, commands, *dirs):
+    """Mean per dispatch of every SQ counter found in the `rocprofv3 --pmc` directories, for
+    dispatches whose kernel name contains `kernel`; with `blocks` (16-token block visits per
+    launch, 16 rows each) also instructions per block.  Derived: MFMA busy share of the wave
+    cycles (SQ_WAVE_CYCLES counts in units of 4 cycles; one wave per SIMD)."""
+    import sqlite3
+    sums, disp = {}, {}
+    for d in dirs:
+        for f in _dbs(d):
+            con = sqlite3.connect(f)
+            for dsp, kname, cname, value in con.execute(
+                    "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+                if kernel not in kname or not cname.startswith("SQ_"):
+                    continue
+                sums[cname] = sums.get(cname, 0.0) + float(value)
+                disp.setdefault(cname, set()).add((f, dsp))
+            con.close()
+    if not sums:
+        raise SystemExit(f"no SQ counters for {kernel}")
+    mean = {c: sums[c] / len(disp[c]) for c in sums}
+    blocks = int(blocks)
+    lines = [f"# SQ counters of `{kernel}`", "", "Commands (run from /tmp with TMPDIR=/tmp):", "", "```", commands, "```",
+             "", "| counter | mean per dispatch | per block |", "|---|---|---|"]
+    for c in sorted(mean):
+        per = f"{mean[c] / blocks:.1f}" if blocks > 0 else ""
+        lines.append(f"| {c} | {mean[c]:.0f} | {per} |")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "SQ_WAVE_CYCLES" in mean:
+        lines += ["", f"- MFMA busy / wave cycles: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * mean['SQ_WAVE_CYCLES']):.3f}"]
+    if blocks > 0 and "SQ_WAVE_CYCLES" in mean:
+        lines += [f"- wave cycles per block visit: {4 * mean['SQ_WAVE_CYCLES'] / blocks:.0f}"]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     cmd = sys.argv[1]
     if cmd == "calib":
@@ -142,5 +179,7 @@ if __name__ == "__main__":
         stats(sys.argv[2], sys.argv[3], sys.argv[4])
     elif cmd == "counters":
         counters(*sys.argv[2:10])
+    elif cmd == "sq":
+        sq(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)
