@@ -190,82 +190,51 @@ __device__ __forceinline__ void dma_f8_block(const uint8_t* row0, uint32_t voff,
 #undef MLA_F8_DMA_TAIL
 }
 
-// One bf16 block into an LDS stage: 18 loads of 16 B per lane, load j reading chunk block
-// j / 2 (bytes 128 (j / 2) ..) of the lane's row for even (p0) or odd (p1) loads and
-// writing 1 KB at stage + 1024 j.  The instruction offset (128 (j / 2)) applies to the
-// global and the LDS address alike, so M0 is stepped to stage + 1024 j - 128 (j / 2)
-// before each load (saved and restored around them).  Like dma_f8_block it first waits
-// for the LDS reads issued before it, and it is hidden from the compiler's counters.
+// One bf16 block into an LDS stage: 18 loads of 16 B per lane.  Load j = 4m + q reads chunk
+// block j / 2 (bytes 128 (j / 2) ..) of the lane's row (vo0: its byte offset from the block's
+// first row for even loads, vo1 for odd ones) and writes 1 KB at stage + 1024 j.  It is a
+// global load with an SGPR base: address = base_m + voff_q + 1024 q with base_m = row0 +
+// 256 m - 3072 and voff_q = vo_(q & 1) + 128 (q >> 1) - 1024 q + 3072 (>= 0), and the same
+// instruction offset 1024 q lands in LDS at M0 + 1024 q with M0 = stage + 4096 m, so M0
+// changes once per four loads (saved and restored around them).  Like dma_f8_block it first
+// waits for the LDS reads issued before it, and it is hidden from the compiler's counters.
 template <bool NT>
-__device__ __forceinline__ void dma_bf16_block(const uint16_t* p0, const uint16_t* p1, uint32_t lds) {
+__device__ __forceinline__ void dma_bf16_block(const uint8_t* row0, uint32_t vo0, uint32_t vo1, uint32_t lds) {
+  const uint32_t v0 = vo0 + 3072, v1 = vo1 + 2048, v2 = vo0 + 1152, v3 = vo1 + 128;
+  const uint8_t* b0 = row0 - 3072;
+  const uint8_t* b1 = row0 - 2816;
+  const uint8_t* b2 = row0 - 2560;
+  const uint8_t* b3 = row0 - 2304;
+  const uint8_t* b4 = row0 - 2048;
   uint32_t sv;
+#define MLA_BF16_DMA4(B, NTS)                                                                     \
+  "global_load_lds_dwordx4 %1, " B NTS "\n\t"                                                     \
+  "global_load_lds_dwordx4 %2, " B " offset:1024" NTS "\n\t"                                      \
+  "global_load_lds_dwordx4 %3, " B " offset:2048" NTS "\n\t"                                      \
+  "global_load_lds_dwordx4 %4, " B " offset:3072" NTS "\n\t"
 #define MLA_BF16_DMA(NTS)                                                                         \
   asm volatile(                                                                                   \
-      "s_waitcnt lgkmcnt(0)\n\t"                                                              \
-      "s_mov_b32 %0, m0\n\t"                                                              \
-      "s_mov_b32 m0, %3\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %1, off" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 1024\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %2, off" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 896\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %1, off offset:128" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 1024\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %2, off offset:128" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 896\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %1, off offset:256" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 1024\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %2, off offset:256" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 896\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %1, off offset:384" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 1024\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %2, off offset:384" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 896\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %1, off offset:512" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 1024\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %2, off offset:512" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 896\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %1, off offset:640" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 1024\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %2, off offset:640" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 896\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %1, off offset:768" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 1024\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %2, off offset:768" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 896\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %1, off offset:896" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 1024\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %2, off offset:896" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 896\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %1, off offset:1024" NTS "\n\t"                                                   \
-      "s_add_u32 m0, m0, 1024\n\t"                                                              \
-      "s_nop 0\n\t"                                                              \
-      "global_load_lds_dwordx4 %2, off offset:1024" NTS "\n\t"                                                   \
-      "s_mov_b32 m0, %0\n\t"                                                              \
+      "s_waitcnt lgkmcnt(0)\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %5\n\ts_nop 0\n\t"               \
+      MLA_BF16_DMA4("%6", NTS)                                                                    \
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"                                                   \
+      MLA_BF16_DMA4("%7", NTS)                                                                    \
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"                                                   \
+      MLA_BF16_DMA4("%8", NTS)                                                                    \
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"                                                   \
+      MLA_BF16_DMA4("%9", NTS)                                                                    \
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"                                                   \
+      "global_load_lds_dwordx4 %1, %10" NTS "\n\t"                                                \
+      "global_load_lds_dwordx4 %2, %10 offset:1024" NTS "\n\t"                                    \
+      "s_mov_b32 m0, %0"                                                                          \
       : "=&s"(sv)                                                                                 \
-      : "v"(p0), "v"(p1), "s"(lds)                                                                \
+      : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(lds), "s"(b0), "s"(b1), "s"(b2), "s"(b3), "s"(b4) \
       : "memory", "scc")
   if constexpr (NT)
     MLA_BF16_DMA(" nt");
   else
     MLA_BF16_DMA("");
 #undef MLA_BF16_DMA
+#undef MLA_BF16_DMA4
 }
 // gfx950 LDS transpose read of 16-bit elements (the V^T operand)
 __device__ __forceinline__ u32x2_t lds_tr16(LDS_AS const uint8_t* p) {
@@ -365,8 +334,8 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     // false for an out-of-range table entry (then page 0 is read, in bounds, and the block
     // is skipped).  Rows past the end of the piece re-read its last valid row.
     struct Src {
-      const uint16_t* p[2];   // bf16: this lane's source for even / odd instructions
-      const uint8_t* row0;    // FP8: the block's first row
+      const uint8_t* row0;    // the block's first row
+      uint32_t vo[2];         // bf16: this lane's byte offsets from it for even / odd loads
     };
     auto source = [&](int k, bool& ok) -> Src {
       const int tok0 = tb + kBlock * blk_of(k);
@@ -378,8 +347,9 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       if constexpr (FP8) {
         r.row0 = kv8 + base * kF8Row;
       } else {
-        r.p[0] = a.kv + (base + min(ld_tok0, last)) * kDqk + ld_col0;
-        r.p[1] = a.kv + (base + min(ld_tok1, last)) * kDqk + ld_col1;
+        r.row0 = (const uint8_t*)(a.kv + base * kDqk);
+        r.vo[0] = (uint32_t)(min(ld_tok0, last) * kRowBytesBf16 + 2 * ld_col0);
+        r.vo[1] = (uint32_t)(min(ld_tok1, last) * kRowBytesBf16 + 2 * ld_col1);
       }
       return r;
     };
@@ -398,9 +368,9 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       } else {
         const uint32_t l = (uint32_t)(uintptr_t)stage;
         if (stream)
-          dma_bf16_block<true>(src.p[0], src.p[1], l);
+          dma_bf16_block<true>(src.row0, src.vo[0], src.vo[1], l);
         else
-          dma_bf16_block<false>(src.p[0], src.p[1], l);
+          dma_bf16_block<false>(src.row0, src.vo[0], src.vo[1], l);
       }
     };
     // S^T for one block and its V^T operands: the K and V^T reads are ordinary LDS loads the
