@@ -243,6 +243,44 @@ def test_grouped_kernel(heads, q_len, rpg, out_fp32):
                          None if out_fp32 else softmax_abs_v(prob))
 
 
+def with_score_ramp(prob, slope=0.1):
+    """The same problem with rope column 512 of every cached row set to slope * t (t the
+    token's position in its sequence) and the queries' column 512 set to 1, so each score
+    gains sigma * slope * t: the running max keeps climbing along the context."""
+    kv = prob.kv_cache.copy()
+    q = prob.q.copy()
+    q[..., 512] = gen.f32_to_bf16_bits(np.float32(1.0))
+    for b in range(prob.batch):
+        t = np.arange(int(prob.cache_seqlens[b]))
+        bits = gen.f32_to_bf16_bits((slope * t).astype(np.float32))
+        pages, rows = prob.block_table[b, t // prob.page_size], t % prob.page_size
+        if kv.dtype == np.uint8:       # fp8 rows: the rope columns are bf16 at bytes 512..639
+            kv[pages, rows, 512] = (bits & 0xFF).astype(np.uint8)
+            kv[pages, rows, 513] = (bits >> 8).astype(np.uint8)
+        else:
+            kv[pages, rows, 512] = bits
+    return gen.Problem(q=q, kv_cache=kv, block_table=prob.block_table, cache_seqlens=prob.cache_seqlens,
+                       softmax_scale=prob.softmax_scale, page_size=prob.page_size, out_fp32=prob.out_fp32)
+
+
+@pytest.mark.parametrize("heads,q_len,rpg,kv", [(16, 1, 0, "bf16"), (16, 2, 0, "bf16"), (16, 2, 32, "bf16"),
+                                             (128, 1, 0, "bf16"), (16, 1, 0, "fp8"), (64, 1, 0, "fp8")])
+@pytest.mark.parametrize("out_fp32", [True, False])
+def test_climbing_scores_move_the_running_max(heads, q_len, rpg, kv, out_fp32):
+    """Scores that grow along the context (about 31 log2 units over 3,000 tokens) with 8
+    work-groups, so every wave's running max passes its lazy-rescale slack (8) several times
+    in mid-stream and O and l are rescaled with weights already accumulated."""
+    base = gen.make_problem(batch=3, q_len=q_len, num_heads=heads, page_size=64, lengths=[3000, 777, 1285],
+                            seed=31, kv_format=kv, out_fp32=out_fp32, tail="nan", extra_pages=1)
+    prob = with_score_ramp(base)
+    r = Runner(prob, num_cus=8, rows_per_group=rpg)
+    r()
+    out, lse = r.results()
+    ref_o, ref_l = oracle(prob)
+    check_short_contexts(out, lse, ref_o, ref_l, out_fp32, f"climbing H={heads} S_q={q_len} rpg={rpg} {kv}",
+                         None if out_fp32 else softmax_abs_v(prob))
+
+
 def test_two_token_query_equals_two_single_token_calls():
     prob = gen.make_problem(batch=2, q_len=2, num_heads=16, page_size=64, lengths=[1500, 300], seed=12,
                             out_fp32=True)
