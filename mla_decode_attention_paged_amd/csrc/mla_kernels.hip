@@ -397,10 +397,10 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       if (nx) issue(ns, st);
       sacc += acc2;
     };
-    // O^T += V^T P^T for one block, p = exp2(s - m_ref).  p is split into two bf16
-    // terms, p = hi + lo (hi = bf16(p), lo = bf16(p - hi)), and both go through the
-    // MFMA, so the weights carry ~16 mantissa bits instead of bf16's 8; the running
-    // sum l takes p in fp32.
+    // O^T += V^T P^T for one block, p = exp2(s - m_ref); the running sum l takes p in fp32.
+    // bf16 output: p enters the MFMA in bf16.  fp32 output: p is split into two bf16 terms,
+    // p = hi + lo (hi = bf16(p), lo = bf16(p - hi)), and both go through the MFMA, so the
+    // weights carry ~16 mantissa bits instead of bf16's 8.
     auto accumulate = [&](const float (&s)[4], const u32x2_t (&vf0)[16], const u32x2_t (&vf1)[16]) {
       float p[4];
 #pragma unroll
@@ -818,14 +818,16 @@ __device__ __forceinline__ void dma_group_share(const uint16_t* src, uint32_t ld
 }
 
 // Grouped split-decode kernel for 16 * RG query rows per work-group.  The four
-// waves consume the same KV stream: wave (rg, dh) owns query rows 16*rg..16*rg+15
-// and output columns [512*dh/DH, 512*(dh+1)/DH) with DH = 4 / RG.  Each step is
-// 32 tokens (two 16-token blocks); the work-group keeps four step slots in LDS
-// (three steps in flight), filled by global->LDS DMA split evenly over the waves
-// (9 loads each per step), and moves from step to step behind one barrier that
-// publishes the step's data and frees the slot read in the previous step.  Every
-// wave computes S^T for its rows over all 576 columns (the waves of a row group
-// repeat it) and O^T += V^T P^T for its columns on 16x16x32 MFMA with K = 32 tokens.
+// waves consume the same KV stream.  Each step is 32 tokens (two 16-token blocks);
+// the work-group keeps four step slots in LDS (three steps in flight), filled by
+// global->LDS DMA split evenly over the waves (9 loads each per step), and moves from
+// step to step behind one barrier that publishes the step's data and frees the slot
+// read in the previous step.
+//
+// RG = 4 (64 rows): wave rg owns query rows 16*rg..16*rg+15 and all 512 output columns,
+// computes S^T over both blocks of the step and O^T += V^T P^T on 16x16x32 MFMA with
+// K = 32 tokens.  (The code also has the column split DH = 4 / RG of the waves of a row
+// group for RG < 4, each repeating S^T; RG = 2 uses the token split below instead.)
 //
 // TS (token split, RG = 2 only): wave w owns rows 16 (w & 1) .. + 15, all 512 columns, and
 // block w >> 1 of every step, with its own online-softmax state, so the two row groups share
