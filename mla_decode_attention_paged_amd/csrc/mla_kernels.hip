@@ -826,8 +826,7 @@ __device__ __forceinline__ void dma_group_share(const uint16_t* src, uint32_t ld
 //
 // RG = 4 (64 rows): wave rg owns query rows 16*rg..16*rg+15 and all 512 output columns,
 // computes S^T over both blocks of the step and O^T += V^T P^T on 16x16x32 MFMA with
-// K = 32 tokens.  (The code also has the column split DH = 4 / RG of the waves of a row
-// group for RG < 4, each repeating S^T; RG = 2 uses the token split below instead.)
+// K = 32 tokens.  RG = 2 (32 rows) takes the token split below.
 //
 // TS (token split, RG = 2 only): wave w owns rows 16 (w & 1) .. + 15, all 512 columns, and
 // block w >> 1 of every step, with its own online-softmax state, so the two row groups share
@@ -835,12 +834,11 @@ __device__ __forceinline__ void dma_group_share(const uint16_t* src, uint32_t ld
 // through LDS at the end of a piece.
 template <int RG, bool OUT_F32, bool TS>
 __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a) {
-  static_assert(!TS || RG == 2, "the token split pairs two row groups");
-  constexpr int DH = TS ? 1 : kWaves / RG;              // column parts
+  static_assert(TS ? RG == 2 : RG == kWaves, "32 rows: token split; 64 rows: one row group per wave");
   constexpr int SB = 2;                                 // blocks per step
   constexpr int SLOTS = kWaves * kStages / SB;          // step slots (4)
   constexpr int LOADS = kLoadsPerBlock * SB / kWaves;   // DMA instructions per wave and step (9)
-  constexpr int MBW = kVBlocks / DH;                    // 16-column output blocks per wave
+  constexpr int MBW = kVBlocks;                         // 16-column output blocks per wave
   static_assert(LOADS * kWaves == kLoadsPerBlock * SB && LOADS == 9 && SB == 2 && MBW % 8 == 0, "layout");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
@@ -848,7 +846,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int rg = TS ? (wave & 1) : wave / DH, dh = TS ? 0 : wave % DH;
+  const int rg = TS ? (wave & 1) : wave;
   const int th = TS ? (wave >> 1) : 0;                  // TS: the block of each step this wave takes
 
   int worker, rgroup;
@@ -864,11 +862,10 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
   const int R = a.rows;
   const bool stream = a.row_groups == 1;   // KV loads: non-temporal when no other row group re-reads
   const int row0 = rgroup * 16 * RG + 16 * rg;
-  const int mb0 = dh * MBW;
 
   const int k_lane = (g * 16 + (n ^ ((g & 1) * kSwz))) * 16;
   const int e = n >> 2, qq = n & 3;
-  const int v_lane = ((qq >> 1) * 16 + ((4 * g + e) ^ ((qq >> 1) * kSwz))) * 16 + (qq & 1) * 8 + mb0 * 512;
+  const int v_lane = ((qq >> 1) * 16 + ((4 * g + e) ^ ((qq >> 1) * kSwz))) * 16 + (qq & 1) * 8;
   const int ld_token = n ^ ((g & 1) * kSwz);
 
   const CST_AS int32_t* worker_off = as_const(a.worker_off);
@@ -1042,10 +1039,10 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         st = lds + (k % SLOTS) * (SB * kBlockBytes);
         if (!use0 || !use1) {
           // rare: one block of the step is past the end or has an out-of-range table entry
-          // (its rows may hold anything): zero the V^T columns this wave reads in that block,
-          // 2 chunks of 16 tokens x 16 B per 16-column block (every wave that reads them writes
-          // the same zeros first)
-          LDS_AS uint8_t* zb = st + (use0 ? kBlockBytes : 0) + 512 * mb0;
+          // (its rows may hold anything): zero that block's 512 V^T columns, 2 chunks of 16
+          // tokens x 16 B per 16-column block (every wave reads them all and writes the same
+          // zeros first)
+          LDS_AS uint8_t* zb = st + (use0 ? kBlockBytes : 0);
           for (int u = lane; u < 32 * MBW; u += 64) *(LDS_AS u32x4_t*)(zb + 16 * u) = u32x4_t{0u, 0u, 0u, 0u};
         }
         scores(st, use0 ? lim - tok0 : 0, s);
@@ -1134,14 +1131,13 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         }
       }
     } else {
-    // ---- write: every wave holds complete rows for its columns (all waves of a row
-    // group agree on m_ref and l, having computed the same scores)
+    // ---- write: every wave holds its 16 rows complete
       const float l = wave_sum_over_groups(lsum);
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       const int grow = row0 + n;
 #pragma unroll
       for (int mb = 0; mb < MBW; ++mb) {
-        const int d = 16 * (mb0 + mb) + 4 * g;
+        const int d = 16 * mb + 4 * g;
         const f32x4_t v = o[mb] * inv;
         if (slot < 0) {
           const int64_t off = ((int64_t)b * R + grow) * kDv + d;
@@ -1157,7 +1153,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
           *(f32x4_t*)(a.part_o + ((int64_t)slot * R + grow) * kDv + d) = v;
         }
       }
-      if (dh == 0 && g == 0) {
+      if (g == 0) {
         const float lse = l > 0.f ? (m_ref + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
         if (slot < 0) {
           if (a.lse) a.lse[(int64_t)b * R + grow] = lse;
