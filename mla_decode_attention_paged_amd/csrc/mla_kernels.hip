@@ -374,9 +374,9 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       }
     };
     // S^T for one block and its V^T operands: the K and V^T reads are ordinary LDS loads the
-    // compiler interleaves with the S^T MFMAs; then the stage is refilled with the block after
-    // next (`ns`, if `nx`; the DMA first waits for the reads) while the softmax and
-    // O^T += V^T P^T are computed.
+    // compiler interleaves with the S^T MFMAs; halfway through the MFMAs the stage is refilled
+    // with the block after next (`ns`, if `nx`; the DMA first waits for the reads), while the
+    // rest of S^T, the softmax and O^T += V^T P^T are computed.
     auto scores = [&](LDS_AS uint8_t* st, f32x4_t& sacc, u32x2_t (&vf0)[16], u32x2_t (&vf1)[16], const Src& ns,
                       bool nx) {
       u32x4_t kf[kKSteps];
@@ -393,8 +393,8 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       for (int kk = 0; kk < kKSteps; ++kk) {
         f32x4_t& acc = (kk & 1) ? acc2 : sacc;
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]), qf[kk], acc, 0, 0, 0);
+        if (kk == 8 && nx) issue(ns, st);
       }
-      if (nx) issue(ns, st);
       sacc += acc2;
     };
     // O^T += V^T P^T for one block, p = exp2(s - m_ref); the running sum l takes p in fp32.
