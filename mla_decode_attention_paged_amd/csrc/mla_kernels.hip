@@ -484,8 +484,8 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     if constexpr (FP8) {
       // ---- FP8 rows: three stages per wave; block k is in stage k % 3 while blocks k + 1
       // and k + 2 are in flight.  All of block k's operands are read from the stage (the
-      // compiler interleaves the reads with the S^T MFMAs), then the stage is refilled with
-      // block k + 3.  S^T takes K = code * scale from the conversion (which applies the
+      // compiler interleaves the reads with the S^T MFMAs), and halfway through S^T the
+      // stage is refilled with block k + 3.  S^T takes K = code * scale from the conversion (which applies the
       // scale's exponent); O^T takes V^T = code and folds each token's group scale 2^e into
       // P (exact for powers of two): O^T[d] += sum_t code[t][d] (p_t 2^e[t][d/128]).
       uint32_t okq = 0;   // bit i: the table entry of the block now in stage i was in range
@@ -545,15 +545,15 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
             kf[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[kk][1], sc, true));
             f32x4_t& acc = (kk & 1) ? acc2 : sacc;
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf), qf[kk], acc, 0, 0, 0);
+            if (kk == 8) {
+              // refill the stage with block k + 3 (the DMA waits for the block's reads first)
+              bool nok = true;
+              if (k + kF8Stages < my_n) issue(source(k + kF8Stages, nok), st);
+              okq = (okq & ~(1u << slot)) | ((nok ? 1u : 0u) << slot);
+            }
           }
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rope0), qf[16], sacc, 0, 0, 0);
           acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, rope1), qf[17], acc2, 0, 0, 0);
-          // refill the stage with block k + 3 (the DMA waits for the reads above first)
-          {
-            bool nok = true;
-            if (k + kF8Stages < my_n) issue(source(k + kF8Stages, nok), st);
-            okq = (okq & ~(1u << slot)) | ((nok ? 1u : 0u) << slot);
-          }
           sacc += acc2;
           const int nvalid = ok ? lim - tok0 : 0;   // tokens of the block this row sees (may be <= 0)
 #pragma unroll
