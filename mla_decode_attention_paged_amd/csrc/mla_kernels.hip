@@ -393,8 +393,11 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
       for (int kk = 0; kk < kKSteps; ++kk) {
         f32x4_t& acc = (kk & 1) ? acc2 : sacc;
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kk]), qf[kk], acc, 0, 0, 0);
-        if (kk == 8 && nx) issue(ns, st);
+        if (!DEV && kk == 8 && nx) issue(ns, st);
       }
+      // (the device-scheduled variant refills after S^T: halfway, its fp32-output build would
+      // need a few scratch registers)
+      if (DEV && nx) issue(ns, st);
       sacc += acc2;
     };
     // O^T += V^T P^T for one block, p = exp2(s - m_ref); the running sum l takes p in fp32.
