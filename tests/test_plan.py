@@ -136,3 +136,16 @@ def test_rows_per_group_rejected():
         B.Plan(prob, [10], num_cus=256, rows_per_group=32)      # R = 16 is not a multiple of 32
     with pytest.raises(B.MlaError):
         B.Plan(prob, [10], num_cus=256, rows_per_group=24)
+    fp8 = B.make_problem(1, 1, 128, 64, 1, 1, kv_fp8=True)
+    with pytest.raises(B.MlaError) as ei:
+        B.Plan(fp8, [10], num_cus=256, rows_per_group=64)       # the grouped kernel reads bf16 rows only
+    assert ei.value.status == B.MLA_ERR_UNSUPPORTED
+
+
+def test_default_rows_per_group():
+    """64 rows per work-group when R is a multiple of 64 and the cache is bf16, else 16."""
+    for heads, q_len, kv, want in [(16, 1, 0, 16), (16, 2, 0, 16), (48, 1, 0, 16), (64, 1, 0, 64), (128, 1, 0, 64),
+                                   (32, 2, 0, 64), (64, 1, 1, 16), (128, 1, 1, 16)]:
+        prob = B.make_problem(1, q_len, heads, 64, 1, 1, kv_fp8=bool(kv))
+        info = B.Plan(prob, [10], num_cus=256).info()
+        assert info["rows_per_group"] == want, (heads, q_len, kv, info["rows_per_group"])
