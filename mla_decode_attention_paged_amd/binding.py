@@ -223,7 +223,6 @@ def mla_decode(plan: Plan, q, kv_cache, block_table, cache_seqlens, softmax_scal
     """Launch paged MLA decode (asynchronous on `stream`, default: torch's current stream)."""
     import torch
     p = plan.problem
-    R = p.q_len * p.num_heads
     _require(q, "q", (torch.bfloat16,), (p.batch, p.q_len, p.num_heads, 576))
     _require(kv_cache, "kv_cache", *_kv_spec(p))
     _require(block_table, "block_table", (torch.int32,), (p.batch, p.max_pages_per_seq))
@@ -233,7 +232,6 @@ def mla_decode(plan: Plan, q, kv_cache, block_table, cache_seqlens, softmax_scal
     if lse is not None:
         _require(lse, "lse", (torch.float32,), (p.batch, p.q_len, p.num_heads))
     _require(workspace, "workspace", (torch.uint8,))
-    del R
     _check(lib().mla_decode_stages(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens),
                                    float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), _nbytes(workspace),
                                    _stream(stream), stages), "mla_decode")
