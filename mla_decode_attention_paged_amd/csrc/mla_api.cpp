@@ -264,6 +264,7 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   a.rows = p.rows;
   a.page_size = p.prob.page_size;
+  a.page_shift = mla::page_shift_of(p.prob.page_size);
   a.num_pages = p.prob.num_pages;
   a.bt_stride = p.prob.max_pages_per_seq;
   a.num_workers = p.num_workers;
@@ -361,6 +362,7 @@ mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_worker
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   a.rows = p.q_len * p.num_heads;
   a.page_size = p.page_size;
+  a.page_shift = mla::page_shift_of(p.page_size);
   a.num_pages = p.num_pages;
   a.bt_stride = p.max_pages_per_seq;
   a.num_workers = d.workers;

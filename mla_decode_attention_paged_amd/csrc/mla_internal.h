@@ -62,6 +62,14 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
                         int32_t force_splits, int32_t rows_per_group, PlanImpl& out, std::string& err);
 
 // Parameters of the split-decode kernel.
+// log2(page_size) when the page size is a power of two, else -1 (the kernels then divide)
+inline int32_t page_shift_of(int32_t page_size) {
+  if (page_size <= 0 || (page_size & (page_size - 1)) != 0) return -1;
+  int32_t s = 0;
+  while ((1 << s) < page_size) ++s;
+  return s;
+}
+
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* kv;
@@ -77,6 +85,7 @@ struct DecodeArgs {
   float scale_log2;              // softmax_scale * log2(e)
   int32_t rows;                  // R
   int32_t page_size;
+  int32_t page_shift;              // log2(page_size) for a power of two, else -1
   int32_t num_pages;
   int32_t bt_stride;
   int32_t num_workers;

@@ -79,13 +79,22 @@ constexpr int kSplitSmemFp8 = kSmemFp8 > kMergeBytes ? kSmemFp8 : kMergeBytes;
 constexpr int kSwz = 8;
 
 // Physical row of logical token t of sequence b (the page walk).  Returns -1
-// when the block-table entry is outside [0, num_pages).
+// when the block-table entry is outside [0, num_pages).  page_shift = log2(page_size)
+// when the page size is a power of two (shift and mask), else -1 (a division).
 template <class TablePtr>
-__device__ __forceinline__ int64_t kv_row_of(TablePtr block_table, int bt_stride, int page_size,
+__device__ __forceinline__ int64_t kv_row_of(TablePtr block_table, int bt_stride, int page_size, int page_shift,
                                              int num_pages, int b, int t) {
-  const int page = block_table[(int64_t)b * bt_stride + t / page_size];
+  int pi, r;
+  if (page_shift >= 0) {
+    pi = t >> page_shift;
+    r = t & (page_size - 1);
+  } else {
+    pi = t / page_size;
+    r = t - pi * page_size;
+  }
+  const int page = block_table[(int64_t)b * bt_stride + pi];
   if (page < 0 || page >= num_pages) return -1;
-  return (int64_t)page * page_size + (t % page_size);
+  return (int64_t)page * page_size + r;
 }
 
 __device__ __forceinline__ float wave_max_over_groups(float x) {
@@ -339,7 +348,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     };
     auto source = [&](int k, bool& ok) -> Src {
       const int tok0 = tb + kBlock * blk_of(k);
-      int64_t base = kv_row_of(block_table, a.bt_stride, a.page_size, a.num_pages, b, tok0);
+      int64_t base = kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok0);
       ok = base >= 0;
       if (!ok) base = 0;
       const int last = te - 1 - tok0;
@@ -903,7 +912,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
     auto source = [&](int blk) -> const uint16_t* {
       const int bb = min(blk, nblk - 1);
       const int tok0 = tb + kBlock * bb;
-      int64_t base = kv_row_of(block_table, a.bt_stride, a.page_size, a.num_pages, b, tok0);
+      int64_t base = kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok0);
       if (base < 0) base = 0;
       const int t = min(ld_token, te - 1 - tok0);
       return a.kv + (base + t) * kDqk + 8 * g;
@@ -1019,8 +1028,8 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         const int tok0 = tb + kBlock * blk0, tok1 = tok0 + kBlock;
         use0 = blk0 < nblk;
         use1 = blk0 + 1 < nblk;
-        if (use0 && kv_row_of(block_table, a.bt_stride, a.page_size, a.num_pages, b, tok0) < 0) use0 = false;
-        if (use1 && kv_row_of(block_table, a.bt_stride, a.page_size, a.num_pages, b, tok1) < 0) use1 = false;
+        if (use0 && kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok0) < 0) use0 = false;
+        if (use1 && kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok1) < 0) use1 = false;
         if ((blk0 < nblk && !use0) || (blk0 + 1 < nblk && !use1)) {
           if (lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -1309,7 +1318,7 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* kv, const in
   const int t = (int)(idx / chunks);
   const int c = (int)(idx % chunks);
   if (t >= length) return;
-  const int64_t row = kv_row_of(block_table, bt_stride, page_size, num_pages, seq, t);
+  const int64_t row = kv_row_of(block_table, bt_stride, page_size, -1, num_pages, seq, t);
   if (row < 0) return;
   *(u32x4_t*)(rows_out + (row_offset + t) * row_bytes + 16 * c) = *(const u32x4_t*)(kv + row * row_bytes + 16 * c);
 }

@@ -61,7 +61,7 @@ def test_fp8_gather_bit_exact(page):
 
 
 @pytest.mark.parametrize("out_fp32", [True, False])
-@pytest.mark.parametrize("page", [16, 64])
+@pytest.mark.parametrize("page", [16, 48, 64])
 def test_fp8_edge_lengths_nan_tails(page, out_fp32):
     lengths = [1, 2, 15, 16, 17, 63, 64, 65, 1000, 5000]
     prob = gen.make_problem(batch=len(lengths), q_len=1, num_heads=16, page_size=page, lengths=lengths, seed=52,

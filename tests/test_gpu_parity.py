@@ -151,7 +151,7 @@ def test_parity_full_size_sampled(name, sample):
 
 
 # ----------------------------------------------------------------------------- edge cases
-@pytest.mark.parametrize("page", [16, 64, 1024])
+@pytest.mark.parametrize("page", [16, 48, 64, 80, 1024])
 @pytest.mark.parametrize("out_fp32", [True, False])
 def test_edge_lengths_nan_tails(page, out_fp32):
     lengths = [1, 15, 16, 17, 63, 64, 65, 1000]
@@ -160,6 +160,19 @@ def test_edge_lengths_nan_tails(page, out_fp32):
     out, lse = run(prob)
     ref_o, ref_l = oracle(prob)
     check_short_contexts(out, lse, ref_o, ref_l, out_fp32, f"edges P={page}", None if out_fp32 else softmax_abs_v(prob))
+
+
+@pytest.mark.parametrize("heads,page,kv", [(128, 48, "bf16"), (128, 80, "bf16"), (32, 48, "bf16"),
+                                          (64, 80, "fp8")])
+def test_non_power_of_two_pages(heads, page, kv):
+    """Page sizes that are multiples of 16 but not powers of two take the division in the
+    page walk (powers of two take a shift): the grouped kernel, the 16-row kernel at R = 32
+    and the FP8 path."""
+    prob = gen.make_problem(batch=3, q_len=1, num_heads=heads, page_size=page, lengths=[page * 7 + 5, 33, 2000],
+                            seed=23, tail="nan", extra_pages=2, kv_format=kv)
+    out, lse = run(prob)
+    ref_o, ref_l = oracle(prob)
+    check_short_contexts(out, lse, ref_o, ref_l, False, f"P={page} H={heads} {kv}", softmax_abs_v(prob))
 
 
 @pytest.mark.parametrize("out_fp32", [False, True])
