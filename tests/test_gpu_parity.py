@@ -375,6 +375,27 @@ def test_repeated_calls_are_deterministic():
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def test_two_streams_at_once():
+    """Two decodes with their own plans and workspaces, launched on two streams without a
+    synchronisation between them (the library keeps no per-call state outside the
+    workspace), each matching the oracle."""
+    import torch
+    p1 = gen.make_problem(batch=3, q_len=1, num_heads=16, page_size=64, lengths=[5000, 70, 2600], seed=41)
+    p2 = gen.make_problem(batch=2, q_len=2, num_heads=64, page_size=16, lengths=[3333, 900], seed=42,
+                          kv_format="fp8")
+    r1, r2 = Runner(p1), Runner(p2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        r1(stream=s1)
+        r2(stream=s2)
+    torch.cuda.synchronize()
+    for prob, r, what in ((p1, r1, "stream 1"), (p2, r2, "stream 2 (fp8)")):
+        out, lse = r.results()
+        ref_o, ref_l = oracle(prob)
+        compare(out, lse, ref_o, ref_l, what=what)
+
+
 def test_graph_capture_replays_match_eager():
     """The decode launches are capturable in a HIP graph (no memset nodes); every replay,
     with other GPU work in between, gives the eager result bit for bit."""
