@@ -53,6 +53,23 @@ def test_causal_edge_lengths(heads, q_len, out_fp32):
           None if out_fp32 else softmax_abs_v(prob, causal=True))
 
 
+@pytest.mark.parametrize("heads,q_len,rpg", [(16, 2, 32), (8, 4, 32), (16, 4, 64), (32, 2, 16), (16, 8, 16)])
+@pytest.mark.parametrize("out_fp32", [True, False])
+def test_causal_rows_per_group(heads, q_len, rpg, out_fp32):
+    """The causal limit in every kernel layout asked for explicitly: the grouped kernel's
+    token split (32 rows) and its 64-row form, and the 16-row kernel where the default
+    would be the grouped kernel."""
+    prob = gen.make_problem(batch=len(EDGE_LENGTHS), q_len=q_len, num_heads=heads, page_size=16,
+                            lengths=EDGE_LENGTHS, seed=24, tail="nan", extra_pages=2, out_fp32=out_fp32)
+    r = Runner(prob, causal=True, rows_per_group=rpg)
+    assert r.plan.info()["rows_per_group"] == rpg
+    r()
+    out, lse = r.results()
+    ref_o, ref_l = oracle(prob)
+    check(out, lse, ref_o, ref_l, out_fp32, f"causal H={heads} S_q={q_len} rpg={rpg}",
+          None if out_fp32 else softmax_abs_v(prob, causal=True))
+
+
 @pytest.mark.parametrize("heads,q_len", [(8, 2), (16, 2), (64, 2)])
 @pytest.mark.parametrize("force", [2, 3, 1000])
 def test_causal_forced_splits(heads, q_len, force):
