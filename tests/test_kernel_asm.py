@@ -1,8 +1,9 @@
 """Static checks on the gfx950 assembly of the kernels (CPU only; needs hipcc).
 
-- Batched LDS reads written in inline asm: no read's destination registers may be an
-  address register of a later read in the same batch (a returning read would clobber
-  the address before it is used).
+- Runs of consecutive LDS reads: no read's destination registers may be an address
+  register of a later read in the same run (a returning read would clobber the address
+  before it is used).  The compiler schedules these reads; the check guards the inline
+  asm around them (DMA blocks, explicit waits) against upsetting that.
 - No scalar-memory stores or atomics anywhere; every kernel runs without scratch memory.
 """
 import os
