@@ -87,7 +87,7 @@ typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_dtype_t;
 typedef struct {
   int32_t batch;              /* B >= 1 */
   int32_t q_len;              /* S_q >= 1 query tokens per sequence */
-  int32_t num_heads;          /* H >= 1; R = q_len * num_heads must be a multiple of 16, <= 128 */
+  int32_t num_heads;          /* H >= 1; R = q_len * num_heads must be a multiple of 16, <= 256 */
   int32_t head_dim_qk;        /* must be 576 (512 latent + 64 rope) */
   int32_t head_dim_v;         /* must be 512 */
   int32_t page_size;          /* P: tokens per cache page, a positive multiple of 16 */

@@ -49,7 +49,7 @@ mla_status_t check_problem(const mla_problem_t* p) {
     return fail(MLA_ERR_UNSUPPORTED, "page_size must be a multiple of 16 (got %d)", p->page_size);
   const int64_t R = (int64_t)p->q_len * p->num_heads;
   if (R % 16 != 0 || R > mla::kMaxRows)
-    return fail(MLA_ERR_UNSUPPORTED, "q_len*num_heads must be a multiple of 16 and <= 128 (got %lld)",
+    return fail(MLA_ERR_UNSUPPORTED, "q_len*num_heads must be a multiple of 16 and <= 256 (got %lld)",
                 (long long)R);
   if ((int64_t)p->max_pages_per_seq * p->page_size > INT32_MAX)
     return fail(MLA_ERR_UNSUPPORTED, "max_pages_per_seq * page_size exceeds int32");

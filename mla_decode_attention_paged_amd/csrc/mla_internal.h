@@ -15,7 +15,7 @@ constexpr int kDv = 512;           // latent columns, also V
 constexpr int kBlock = 16;         // tokens per KV block (one MFMA M tile)
 constexpr int kWaves = 4;          // waves per work-group in the split-decode kernel
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxRows = 128;
+constexpr int kMaxRows = 256;   // q_len * num_heads: two query tokens over 128 heads
 constexpr int kRowBytesBf16 = kDqk * 2;   // 1,152
 constexpr int kRowBytesFp8 = 656;         // 512 E4M3 + 64 bf16 rope + 4 float32 scales
 

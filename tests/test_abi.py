@@ -50,7 +50,7 @@ def _plan(batch=2, q_len=1, heads=16, page=64, lens=(100, 200), num_pages=None, 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(heads=8), B.MLA_ERR_UNSUPPORTED),                 # R = 8
-    (dict(heads=16, q_len=9), B.MLA_ERR_UNSUPPORTED),       # R = 144 > 128
+    (dict(heads=16, q_len=17), B.MLA_ERR_UNSUPPORTED),      # R = 272 > 256
     (dict(page=8), B.MLA_ERR_UNSUPPORTED),
     (dict(page=24), B.MLA_ERR_UNSUPPORTED),
     (dict(head_dim_qk=512), B.MLA_ERR_UNSUPPORTED),

@@ -42,7 +42,7 @@ def check(out, lse, ref_o, ref_l, out_fp32, what, wabs=None):
         assert excess <= F32_MAX_TOL and lerr <= F32_LSE_TOL, (what, excess, lerr)
 
 
-@pytest.mark.parametrize("heads,q_len", [(8, 2), (16, 2), (16, 3), (32, 2), (64, 2), (16, 8)])
+@pytest.mark.parametrize("heads,q_len", [(8, 2), (16, 2), (16, 3), (32, 2), (64, 2), (16, 8), (128, 2)])
 @pytest.mark.parametrize("out_fp32", [True, False])
 def test_causal_edge_lengths(heads, q_len, out_fp32):
     prob = gen.make_problem(batch=len(EDGE_LENGTHS), q_len=q_len, num_heads=heads, page_size=16,
@@ -53,7 +53,8 @@ def test_causal_edge_lengths(heads, q_len, out_fp32):
           None if out_fp32 else softmax_abs_v(prob, causal=True))
 
 
-@pytest.mark.parametrize("heads,q_len,rpg", [(16, 2, 32), (8, 4, 32), (16, 4, 64), (32, 2, 16), (16, 8, 16)])
+@pytest.mark.parametrize("heads,q_len,rpg", [(16, 2, 32), (8, 4, 32), (16, 4, 64), (32, 2, 16), (16, 8, 16),
+                                          (128, 2, 64)])
 @pytest.mark.parametrize("out_fp32", [True, False])
 def test_causal_rows_per_group(heads, q_len, rpg, out_fp32):
     """The causal limit in every kernel layout asked for explicitly: the grouped kernel's

@@ -65,7 +65,7 @@ def test_devplan_worker_counts(workers):
 
 
 @pytest.mark.parametrize("heads,q_len,causal", [(16, 2, False), (16, 2, True), (32, 1, False), (64, 1, False),
-                                                (128, 1, False), (48, 1, False), (8, 2, True)])
+                                                (128, 1, False), (48, 1, False), (8, 2, True), (128, 2, True)])
 def test_devplan_more_rows(heads, q_len, causal):
     prob = gen.make_problem(batch=3, q_len=q_len, num_heads=heads, page_size=64, lengths=[700, 2000, 33], seed=63,
                             out_fp32=True)

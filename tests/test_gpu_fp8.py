@@ -71,7 +71,7 @@ def test_fp8_edge_lengths_nan_tails(page, out_fp32):
     check(out, lse, ref_o, ref_l, out_fp32, f"fp8 edges P={page}", None if out_fp32 else softmax_abs_v(prob))
 
 
-@pytest.mark.parametrize("heads,q_len", [(16, 2), (32, 1), (64, 1), (128, 1), (48, 1)])
+@pytest.mark.parametrize("heads,q_len", [(16, 2), (32, 1), (64, 1), (128, 1), (48, 1), (128, 2)])
 def test_fp8_more_query_rows(heads, q_len):
     prob = gen.make_problem(batch=3, q_len=q_len, num_heads=heads, page_size=64, lengths=[700, 2000, 33], seed=53,
                             out_fp32=True, kv_format="fp8")

@@ -62,7 +62,7 @@ def check_mfma(got, ref, abs_sum, bf16_out, what):
     assert np.all(excess <= 0), what
 
 
-SHAPES = [(1, 1, 16), (3, 2, 16), (16, 1, 16), (5, 7, 16), (4, 1, 128), (2, 2, 64), (32, 2, 16)]
+SHAPES = [(1, 1, 16), (3, 2, 16), (16, 1, 16), (5, 7, 16), (4, 1, 128), (2, 2, 64), (32, 2, 16), (2, 2, 128)]
 
 
 @pytest.mark.parametrize("batch,q_len,heads", SHAPES)

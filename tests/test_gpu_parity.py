@@ -231,7 +231,7 @@ def test_many_pieces_per_work_group(out_fp32):
     check_short_contexts(out, lse, ref_o, ref_l, out_fp32, "many pieces", None if out_fp32 else softmax_abs_v(prob))
 
 
-@pytest.mark.parametrize("heads,q_len", [(16, 2), (32, 1), (64, 1), (48, 1), (128, 1), (64, 2)])
+@pytest.mark.parametrize("heads,q_len", [(16, 2), (32, 1), (64, 1), (48, 1), (128, 1), (64, 2), (128, 2), (16, 9)])
 def test_more_query_rows(heads, q_len):
     prob = gen.make_problem(batch=3, q_len=q_len, num_heads=heads, page_size=64, lengths=[700, 2000, 33], seed=11)
     out, lse = run(prob)
@@ -240,7 +240,7 @@ def test_more_query_rows(heads, q_len):
 
 
 @pytest.mark.parametrize("heads,q_len,rpg", [(16, 2, 32), (32, 1, 32), (64, 1, 64), (128, 1, 64), (16, 4, 64),
-                                          (64, 2, 64), (128, 1, 16), (64, 1, 16)])
+                                          (64, 2, 64), (128, 1, 16), (64, 1, 16), (128, 2, 64), (128, 2, 16)])
 @pytest.mark.parametrize("out_fp32", [True, False])
 def test_grouped_kernel(heads, q_len, rpg, out_fp32):
     """Rows per work-group asked for through the plan option: the grouped kernel (32 or 64),

@@ -62,7 +62,7 @@ CASES = {
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_plan_covers_every_token_once(name):
     lens = CASES[name]
-    for heads, q_len in ((16, 1), (16, 2), (128, 1)):
+    for heads, q_len in ((16, 1), (16, 2), (128, 1), (128, 2)):
         plan = make_plan(lens, heads=heads, q_len=q_len)
         seg, off, info = check_plan(plan, lens)
         R = heads * q_len
@@ -145,7 +145,7 @@ def test_rows_per_group_rejected():
 def test_default_rows_per_group():
     """64 rows per work-group when R is a multiple of 64 and the cache is bf16, else 16."""
     for heads, q_len, kv, want in [(16, 1, 0, 16), (16, 2, 0, 16), (48, 1, 0, 16), (64, 1, 0, 64), (128, 1, 0, 64),
-                                   (32, 2, 0, 64), (64, 1, 1, 16), (128, 1, 1, 16)]:
+                                   (32, 2, 0, 64), (64, 1, 1, 16), (128, 1, 1, 16), (128, 2, 0, 64), (128, 2, 1, 16)]:
         prob = B.make_problem(1, q_len, heads, 64, 1, 1, kv_fp8=bool(kv))
         info = B.Plan(prob, [10], num_cus=256).info()
         assert info["rows_per_group"] == want, (heads, q_len, kv, info["rows_per_group"])
