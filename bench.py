@@ -191,7 +191,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this build runs the decode "
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): the library runs the decode "
               "on a single MI355X and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
