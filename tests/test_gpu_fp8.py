@@ -71,6 +71,24 @@ def test_fp8_edge_lengths_nan_tails(page, out_fp32):
     check(out, lse, ref_o, ref_l, out_fp32, f"fp8 edges P={page}", None if out_fp32 else softmax_abs_v(prob))
 
 
+@pytest.mark.parametrize("out_fp32", [True, False])
+def test_fp8_many_pieces_per_work_group(out_fp32):
+    """Few work-groups, each walking many short FP8 sequences (the three stages reused
+    from piece to piece), with empty and one-token sequences among them."""
+    rng = np.random.default_rng(53)
+    lengths = rng.integers(0, 120, size=300)
+    lengths[::13] = 0
+    lengths[3::19] = 1
+    prob = gen.make_problem(batch=300, q_len=1, num_heads=16, page_size=16, lengths=lengths.tolist(), seed=53,
+                            tail="nan", out_fp32=out_fp32, kv_format="fp8")
+    r = Runner(prob, num_cus=16)
+    assert max(np.diff(r.plan.segments()[1])) > 10
+    r()
+    out, lse = r.results()
+    ref_o, ref_l = oracle(prob)
+    check(out, lse, ref_o, ref_l, out_fp32, "fp8 many pieces", None if out_fp32 else softmax_abs_v(prob))
+
+
 @pytest.mark.parametrize("heads,q_len", [(16, 2), (32, 1), (64, 1), (128, 1), (48, 1), (128, 2)])
 def test_fp8_more_query_rows(heads, q_len):
     prob = gen.make_problem(batch=3, q_len=q_len, num_heads=heads, page_size=64, lengths=[700, 2000, 33], seed=53,
