@@ -12,6 +12,8 @@ already resident in HBM.  Prints one JSON line:
                a 1 GiB device-to-device copy timed on the same box
   timing_us  = per-call event percentiles, the cache-flushed per-call time, the
                device-scheduled entry point (mla_decode_devplan) on the same inputs
+  compute    = the call's matrix work as TFLOP/s (kernel and whole call), and for
+               the long workload the pages' H20 figure at that shape (context only)
   cpu_baseline = the fp64 oracle on a bounded sample of the same workload, on
                this host's cores (context only)
 
@@ -67,6 +69,22 @@ def measured_traffic(config: str):
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def compute_context(prob, kernel_us: float, call_s: float, config: str):
+    """Matrix work of the call (2 flops per multiply-add: 576 for S^T and 512 for O^T per
+    cached token and query row) as a rate, and, for the long workload, the pages' figure at
+    the same shape on other hardware (context only: another GPU, another flop count may be
+    meant)."""
+    R = prob.q_len * prob.num_heads
+    flops = float(np.sum(prob.cache_seqlens)) * R * 2 * (576 + 512)
+    out = {"flops_per_call": flops,
+           "kernel_tflops": round(flops / (kernel_us * 1e-6) / 1e12, 1),
+           "call_tflops": round(flops / call_s / 1e12, 1)}
+    if config == "long":
+        out["pages_figure"] = ("FlashMLA-ETAP 89 TFLOP/s against FlashMLA 32 TFLOP/s (2.78x) at 64K tokens, "
+                               "batch 16, on an NVIDIA H20 ([ETAP] 'Experimental results'); not comparable")
+    return out
 
 
 def cpu_baseline(prob, budget_s: float = 15.0):
@@ -338,6 +356,7 @@ def main():
                       "devplan_call_mean": round(devplan_us, 2)},
         "plan": {k: info[k] for k in ("num_workers", "grid_size", "num_segments", "num_partials", "num_combine")},
         "status_word": status,
+        "compute": compute_context(prob, split_us, wall, args.config),
         "layer_steps": layer,
     }
     if not args.no_cpu_baseline:
