@@ -447,3 +447,55 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         o, l = r.results()
         assert np.array_equal(o, ref_o) and np.array_equal(l, ref_l), f"replay {i}"
+
+
+def _spread_beyond_4gib(prob, big_pages, seed):
+    """The same problem with its pages placed at physical pages of a cache of big_pages
+    pages (> 4 GiB): most referenced pages land past the 4-GiB byte offset, a few near the
+    start.  Returns (problem whose num_pages is big_pages, device tensors)."""
+    import dataclasses
+    import torch
+    rng = np.random.default_rng(seed)
+    n = prob.num_pages
+    page_bytes = prob.kv_cache[0].nbytes
+    first_high = (4 << 30) // page_bytes + 1
+    assert big_pages - first_high >= n
+    remap = rng.choice(np.arange(first_high, big_pages), size=n, replace=False)
+    remap[: min(2, n)] = np.arange(min(2, n))                 # a couple at the start of the cache
+    bt = prob.block_table
+    bt_big = np.where(bt >= 0, remap[np.clip(bt, 0, n - 1)], -1).astype(np.int32)
+    # a cache array that reports big_pages pages without holding them (only its shape is used)
+    fake = np.lib.stride_tricks.as_strided(prob.kv_cache[:1], shape=(big_pages,) + prob.kv_cache.shape[1:],
+                                           strides=(0,) + prob.kv_cache.strides[1:], writeable=False)
+    big_prob = dataclasses.replace(prob, kv_cache=fake, block_table=bt_big)
+    small = to_device(prob)
+    big = torch.empty((big_pages,) + tuple(small["kv_cache"].shape[1:]), dtype=small["kv_cache"].dtype,
+                      device="cuda")
+    assert big.numel() * big.element_size() > (4 << 30)
+    big.index_copy_(0, torch.from_numpy(remap).to("cuda"), small["kv_cache"])
+    dev = dict(small, kv_cache=big, block_table=torch.from_numpy(bt_big).to("cuda"))
+    return big_prob, dev
+
+
+@pytest.mark.parametrize("heads,rpg,kv", [(16, 16, "bf16"), (64, 64, "bf16"), (16, 16, "fp8")])
+def test_cache_beyond_4gib(heads, rpg, kv):
+    """A cache larger than 4 GiB with the sequences' pages past the 4-GiB byte offset: the
+    page walk and the DMA addresses are 64-bit.  The result equals the same problem on a
+    compact cache bit for bit, and the oracle within the fp32-path bounds."""
+    import torch
+    prob = gen.make_problem(batch=3, q_len=1, num_heads=heads, page_size=64, lengths=[3000, 700, 65],
+                            seed=19, out_fp32=True, kv_format=kv)
+    big_pages = 65536 if kv == "bf16" else 110000
+    _say(f"  cache beyond 4 GiB: heads={heads} rpg={rpg} kv={kv} pages={big_pages}")
+    big_prob, dev = _spread_beyond_4gib(prob, big_pages, seed=19)
+    r_big = Runner(big_prob, dev=dev, rows_per_group=rpg)
+    r_big()
+    out_b, lse_b = r_big.results()
+    r_small = Runner(prob, rows_per_group=rpg)
+    r_small()
+    out_s, lse_s = r_small.results()
+    assert np.array_equal(out_b, out_s) and np.array_equal(lse_b, lse_s)
+    ref_o, ref_l = oracle(prob)
+    compare(out_b, lse_b, ref_o, ref_l, what=f"beyond 4 GiB {kv}", tol=(F32_RMSE_TOL, F32_MAX_TOL, F32_LSE_TOL))
+    del r_big, dev
+    torch.cuda.empty_cache()
