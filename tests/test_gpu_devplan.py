@@ -133,3 +133,24 @@ def test_devplan_workloads(name, sample):
     tol = TIGHT if prob.out_fp32 else (RMSE_TOL, MAX_TOL, LSE_TOL)
     compare(out, lse, ref_o, ref_l, batch_idx=sample, what=f"devplan {name}", tol=tol)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_devplan_cache_beyond_4gib(kv):
+    """The device schedule on a cache larger than 4 GiB with pages past the 4-GiB offset:
+    bit-identical to the same problem on a compact cache, and within the fp32 bounds of
+    the oracle."""
+    import torch
+    from tests.test_gpu_parity import _spread_beyond_4gib
+    prob = gen.make_problem(batch=3, q_len=1, num_heads=16, page_size=64, lengths=[3000, 700, 65], seed=29,
+                            out_fp32=True, kv_format=kv)
+    big_pages = 65536 if kv == "bf16" else 110000
+    _say(f"  devplan cache beyond 4 GiB: kv={kv} pages={big_pages}")
+    big_prob, dev = _spread_beyond_4gib(prob, big_pages, seed=29)
+    r_big, (out_b, lse_b) = run(big_prob, dev=dev)
+    r_small, (out_s, lse_s) = run(prob)
+    assert np.array_equal(out_b, out_s) and np.array_equal(lse_b, lse_s)
+    ref_o, ref_l = oracle(prob)
+    check(out_b, lse_b, ref_o, ref_l, True, f"devplan beyond 4 GiB {kv}")
+    del r_big, dev
+    torch.cuda.empty_cache()
