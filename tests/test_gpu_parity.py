@@ -499,3 +499,29 @@ def test_cache_beyond_4gib(heads, rpg, kv):
     compare(out_b, lse_b, ref_o, ref_l, what=f"beyond 4 GiB {kv}", tol=(F32_RMSE_TOL, F32_MAX_TOL, F32_LSE_TOL))
     del r_big, dev
     torch.cuda.empty_cache()
+
+
+_MILLION = {}
+
+
+@pytest.mark.parametrize("devplan", [False, True])
+def test_one_sequence_of_a_million_tokens(devplan):
+    """One sequence of 2^20 tokens: the planner (or the device schedule) cuts it over every
+    work-group and the merge combines a few hundred partial results."""
+    from mla_decode_attention_paged_amd.device import DevplanRunner
+    if not _MILLION:                      # inputs and oracle shared by both cases
+        p = gen.make_problem(batch=1, q_len=1, num_heads=16, page_size=64, lengths=[1 << 20], seed=23, out_fp32=True)
+        _MILLION.update(prob=p, ref=oracle(p))
+    prob = _MILLION["prob"]
+    ref_o, ref_l = _MILLION["ref"]
+    _say(f"  one sequence of {1 << 20} tokens, devplan={devplan}")
+    if devplan:
+        r = DevplanRunner(prob)
+    else:
+        r = Runner(prob)
+        assert r.plan.info()["num_partials"] >= 200
+    r()
+    out, lse = r.results()
+    compare(out, lse, ref_o, ref_l, what="2^20 tokens", tol=(F32_RMSE_TOL, F32_MAX_TOL, F32_LSE_TOL))
+    if devplan:
+        _MILLION.clear()
