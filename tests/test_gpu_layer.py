@@ -86,7 +86,7 @@ def test_q_absorb(batch, q_len, heads):
 @pytest.mark.parametrize("fp32", [False, True])
 def test_out_absorb(batch, q_len, heads, fp32):
     import torch
-    if (q_len * heads) % 16 or q_len * heads > 128:
+    if (q_len * heads) % 16 or q_len * heads > 256:
         pytest.skip("q_len * heads outside the decode's row range")
     rng = np.random.default_rng(batch * 999 + q_len * 7 + heads + fp32)
     li = gen.make_layer_inputs(batch, q_len, heads, seed=int(rng.integers(1 << 30)))
