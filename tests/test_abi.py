@@ -180,3 +180,32 @@ def test_layer_step_validation():
     assert oa(lat=None) == B.MLA_ERR_INVALID_ARGUMENT
     assert oa(o=fake + 8) == B.MLA_ERR_INVALID_ARGUMENT
     assert oa(w=fake + 2) == B.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_last_error_is_per_thread():
+    """mla_last_error keeps one message per thread: two threads failing with different
+    errors at the same time each read back their own."""
+    import threading
+    cases = [(B.make_problem(2, 1, 16, 24, 4, 2), "page_size must be a multiple of 16"),
+             (B.make_problem(2, 1, 8, 64, 4, 2), "q_len*num_heads must be a multiple of 16")]
+    bad = []
+
+    def worker(prob, want):
+        for _ in range(300):
+            try:
+                B.Plan(prob, np.array([10, 10], dtype=np.int32), num_cus=256)
+            except B.MlaError:
+                msg = B.last_error()
+                if want not in msg:
+                    bad.append(msg)
+            except Exception as e:          # anything else fails the test, not just the thread
+                bad.append(repr(e))
+            else:
+                bad.append("no error")
+
+    threads = [threading.Thread(target=worker, args=c) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]
