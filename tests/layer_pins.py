@@ -111,3 +111,41 @@ def append_pins(append_rows):
                     assert np.all(np.abs(wide[:512] - x) <= np.maximum(step / 2, 2.0 ** -10 * np.repeat(sc, 128)) + 1e-12)
                     got_pe = wide[512:]
                 assert np.max(np.abs(got_pe - want_pe) / np.maximum(np.abs(want_pe), 1e-3)) <= 2.0 ** -8
+
+
+def bf16_rounding_pins(to_bf16_bits):
+    """float64 -> bf16 rounding to nearest, ties to even, in one step.  The reference here is
+    the definition itself, written independently: the two bf16 neighbours of x from the sorted
+    table of every finite positive bf16 value, their distances to x (exact in float64 by
+    Sterbenz's lemma, as the neighbours lie within a factor two of x), the nearer one, and on
+    a tie the one with the even code.  Exact midpoints must go to the even code; values a
+    sixteenth of a float32 unit off a midpoint must go to the nearer side (rounding through
+    float32 first would land them on the midpoint)."""
+    codes = np.arange(0x0080, 0x7F80, dtype=np.uint16)           # positive normal bf16 values
+    vals = orc.widen_bf16(codes)
+
+    def reference(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        i = np.searchsorted(vals, a, side="right") - 1            # vals[i] <= a < vals[i + 1]
+        lo, hi = vals[i], vals[i + 1]
+        dl, dh = a - lo, hi - a
+        even_lo = (codes[i] & 1) == 0
+        pick = np.where(dl < dh, codes[i], np.where(dh < dl, codes[i + 1], np.where(even_lo, codes[i], codes[i + 1])))
+        return (pick | np.where(x < 0, 0x8000, 0)).astype(np.uint16)
+
+    rng = np.random.default_rng(11)
+    k = np.concatenate([np.arange(0x3E00, 0x4200, dtype=np.uint16), rng.integers(0x0100, 0x7F00, 4000).astype(np.uint16)])
+    lo, hi = orc.widen_bf16(k), orc.widen_bf16(k + 1)
+    mid = (lo + hi) / 2.0                                       # exact in float64
+    ulp = hi - lo
+    want_mid = np.where(k % 2 == 0, k, k + 1).astype(np.uint16)
+    assert np.array_equal(to_bf16_bits(mid), want_mid), "exact midpoints must round to the even code"
+    assert np.array_equal(to_bf16_bits(-mid), want_mid | np.uint16(0x8000)), "negative midpoints"
+    off = ulp * 2.0 ** -20                                      # 1/16 of a float32 unit at this scale
+    assert np.array_equal(to_bf16_bits(mid + off), (k + 1).astype(np.uint16)), "just above a midpoint"
+    assert np.array_equal(to_bf16_bits(mid - off), k), "just below a midpoint"
+    assert np.array_equal(to_bf16_bits(lo), k), "representable values are kept"
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-20, 20, 20000))
+    assert np.array_equal(to_bf16_bits(x), reference(x)), "random values"
+    assert np.array_equal(reference(mid), want_mid) and np.array_equal(reference(mid + off), (k + 1).astype(np.uint16))

@@ -11,7 +11,7 @@ from mla_decode_attention_paged_amd import inputs as gen
 from mla_decode_attention_paged_amd.device import Runner
 from oracle import mla_oracle as orc
 from tests.test_gpu_parity import (F32_LSE_TOL, F32_MAX_TOL, F32_RMSE_TOL, LSE_TOL, MAX_TOL, RMSE_TOL, _say,
-                                   bf16_out_excess, compare, softmax_abs_v)
+                                   bf16_out_excess, compare, compare_every_sequence, softmax_abs_v)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,11 +94,10 @@ def test_causal_last_token_matches_unmasked_call():
     assert np.max(np.abs(oc[:, 0] - o[:, 0])) > 1e-4, "the mask changed nothing for token 0"
 
 
-def test_causal_two_token_full_size_sampled():
+def test_causal_two_token_full_size():
     _say("generating two_token")
     prob = gen.make_config("two_token")
     out, lse = run(prob)
-    sample = [0, 17, 31]
-    ref_o, ref_l = oracle(prob, sample)
-    compare(out, lse, ref_o, ref_l, batch_idx=sample, what="two_token causal", tol=(RMSE_TOL, MAX_TOL, LSE_TOL))
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    _say(f"oracle on all {prob.batch} sequences")
+    ref_o, ref_l = oracle(prob)
+    compare_every_sequence(out, lse, ref_o, ref_l, "two_token causal")

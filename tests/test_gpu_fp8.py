@@ -13,7 +13,7 @@ from mla_decode_attention_paged_amd import inputs as gen
 from mla_decode_attention_paged_amd.device import Runner, to_device
 from oracle import mla_oracle as orc
 from tests.test_gpu_parity import (F32_LSE_TOL, F32_MAX_TOL, F32_RMSE_TOL, _say, bf16_out_excess, check_dropped_page,
-                                   compare, softmax_abs_v)
+                                   compare, compare_every_sequence, softmax_abs_v)
 
 pytestmark = pytest.mark.gpu
 
@@ -132,14 +132,15 @@ def test_fp8_equals_bf16_cache_with_the_same_values():
     assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
 
 
-@pytest.mark.parametrize("name,sample", [("long", [0, 15]), ("paged", [3])])
-def test_fp8_full_size_sampled(name, sample):
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", ["paged", "two_token", "long", "ragged"])
+def test_fp8_full_size(name):
     _say(f"generating {name} (fp8)")
     prob = gen.make_config(name, kv_format="fp8")
     out, lse = run(prob)
-    ref_o, ref_l = oracle(prob, sample)
-    compare(out, lse, ref_o, ref_l, batch_idx=sample, what=f"{name} fp8")
-    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    _say(f"oracle on all {prob.batch} sequences")
+    ref_o, ref_l = oracle(prob)
+    compare_every_sequence(out, lse, ref_o, ref_l, f"{name} fp8")
 
 
 def test_fp8_out_of_range_block_table_entry_drops_its_tokens():

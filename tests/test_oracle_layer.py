@@ -23,6 +23,10 @@ def test_append():
     pins.append_pins(L.append_rows)
 
 
+def test_bf16_rounding():
+    pins.bf16_rounding_pins(L._f64_to_bf16_bits)
+
+
 def _rope_variant(kind):
     def rope(x, pos, base=10000.0):
         x = np.asarray(x, dtype=np.float64)
@@ -68,12 +72,30 @@ def _encode_ties_up(x):
     return np.where(tie, (out & 0x7F) + np.where((out & 1) == 0, 1, 0) | (out & 0x80), out).astype(np.uint8)
 
 
+def _bf16_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    q = np.sign(m) * np.floor(np.abs(m) * 256.0 + 0.5)
+    y = (q / 256.0) * np.exp2(e.astype(np.float64))
+    return (y.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_double_rounding(x):
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def _bf16_truncating(x):
+    return (np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def _exponent_off_by_one(amax):
     return L.fp8_group_exponent(amax) + (1 if amax != 0 else 0)
 
 
 @pytest.mark.parametrize("name", ["rope_sign", "rope_halves", "rope_wrong_dim", "q_absorb_transposed",
-                                  "out_absorb_other_head", "encode_ties_up", "exponent_off_by_one"])
+                                  "out_absorb_other_head", "encode_ties_up", "exponent_off_by_one",
+                                  "bf16_ties_away", "bf16_double_rounding", "bf16_truncating"])
 def test_layer_pins_catch_planted_mistake(name, monkeypatch):
     caught = False
     try:
@@ -88,6 +110,9 @@ def test_layer_pins_catch_planted_mistake(name, monkeypatch):
             pins.fp8_encoding_pins(_encode_ties_up, L.fp8_group_exponent)
         elif name == "exponent_off_by_one":
             pins.fp8_encoding_pins(L.encode_e4m3, _exponent_off_by_one)
+        elif name.startswith("bf16_"):
+            pins.bf16_rounding_pins({"bf16_ties_away": _bf16_ties_away, "bf16_double_rounding": _bf16_double_rounding,
+                                     "bf16_truncating": _bf16_truncating}[name])
     except AssertionError:
         caught = True
     assert caught, f"planted mistake {name!r} passed the pins"
