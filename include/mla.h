@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 
 typedef enum {
   MLA_OK = 0,
@@ -65,7 +65,8 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 2,        /* valid but not implemented (head dims, R, page size) */
   MLA_ERR_WORKSPACE_TOO_SMALL = 3,
   MLA_ERR_HIP = 4,                /* a HIP runtime call failed; see mla_last_error() */
-  MLA_ERR_PLAN_MISMATCH = 5       /* plan used with a problem it was not made for */
+  MLA_ERR_PLAN_MISMATCH = 5       /* mla_decode with a workspace that last received another plan's
+                                     schedule (or none) through mla_plan_upload */
 } mla_status_t;
 
 typedef enum { MLA_DTYPE_BF16 = 0, MLA_DTYPE_FP32 = 1 } mla_dtype_t;
@@ -129,10 +130,17 @@ typedef struct {
 
 typedef struct mla_plan_s* mla_plan_t;   /* opaque, host memory only */
 
-/* Build a split-KV schedule for `problem` and the given context lengths.
+/* ---- Split-KV schedule.  The pages do not describe one: splitting each sequence's context
+ * over the compute units is this library's answer to the long-context bandwidth pressure of
+ * decode with a short query ("Problem statement", FlashMLA-ETAP summary), where one sequence
+ * alone must keep every compute unit streaming.  The schedule, its workspace and the merge of
+ * split results are this library's; the merge follows from the online-softmax identity
+ * (section 三 of the juejin.cn FlashMLA explainer).
+ *
+ * mla_plan: build a schedule for `problem` and the given context lengths.
  * Host only; launches nothing.  cache_seqlens_host: B int32 values, each in
- * [0, max_pages_per_seq * page_size].  The plan copies everything it needs.
- * A plan is valid for the same problem and the same cache_seqlens values. */
+ * [0, max_pages_per_seq * page_size].  The plan copies everything it needs and gets an id
+ * of its own.  A plan is valid for the same problem and the same cache_seqlens values. */
 mla_status_t mla_plan(const mla_problem_t* problem, const int32_t* cache_seqlens_host,
                       const mla_plan_options_t* options /* may be NULL */, mla_plan_t* plan_out);
 
@@ -149,14 +157,15 @@ mla_status_t mla_plan_get_segments(mla_plan_t plan, int32_t* segments, int64_t s
  * (schedule + fp32 partial results + a status word).  Returns 0 for a NULL plan. */
 size_t mla_plan_workspace_bytes(mla_plan_t plan);
 
-/* Copy the schedule into `workspace` (device, >= mla_plan_workspace_bytes bytes, 256-B
- * aligned) and clear its status word, asynchronously on `stream`.  Must run once
- * before the first mla_decode with this plan and workspace; the plan must stay
- * alive until the copy has completed on the stream. */
+/* Copy the schedule and the plan's id into `workspace` (device, >= mla_plan_workspace_bytes
+ * bytes, 256-B aligned) and clear its status word, asynchronously on `stream`.  Must run
+ * once before the first mla_decode with this plan and workspace; the plan must stay alive
+ * until the copy has completed on the stream.  The library records (host side) which plan
+ * each workspace address last received. */
 mla_status_t mla_plan_upload(mla_plan_t plan, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Paged MLA decode (two launches on `stream`: split decode, then the merge of
- * split sequences).
+ * split sequences): the computation defined at the top of this file.
  *   q             [B, q_len, H, 576] bf16, contiguous, 16-B aligned
  *   kv_cache      [num_pages, page_size, row] rows of problem->kv_dtype (1,152 or 656 bytes),
  *                 contiguous, 16-B aligned
@@ -164,11 +173,17 @@ mla_status_t mla_plan_upload(mla_plan_t plan, void* workspace, size_t workspace_
  *                 [0, num_pages).  An entry outside that range is not dereferenced: its
  *                 tokens are dropped and the workspace status word gets bit 0 set.
  *   cache_seqlens [B] int32 on the device, the values the plan was made with (a smaller
- *                 device value shortens the context; a larger one is clipped to the plan)
+ *                 device value shortens the context; a larger one is clipped to the plan's
+ *                 and sets bit 2 of the workspace status word)
  *   softmax_scale multiplies q . k before the softmax
  *   out           [B, q_len, H, 512] of problem->out_dtype, 16-B aligned
  *   lse           [B, q_len, H] fp32 natural-log LSE, or NULL
- *   workspace     as uploaded by mla_plan_upload for this plan
+ *   workspace     as uploaded by mla_plan_upload for this plan: MLA_ERR_PLAN_MISMATCH (and no
+ *                 launch) when the host record says the address last received another plan,
+ *                 or none.  The kernels also compare the id stored in the workspace with the
+ *                 plan's (which covers a captured graph replayed after another upload): on a
+ *                 mismatch nothing is read from the schedule, out and lse are left untouched
+ *                 and bit 3 of the status word is set.
  * Sequences with L = 0 get out = 0 and lse = -inf.
  * Calls that share a workspace must not overlap in time. */
 mla_status_t mla_decode(mla_plan_t plan, const void* q, const void* kv_cache,
@@ -192,11 +207,16 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
 
 /* Test aid: write every sequence's logical rows, in token order, to rows_out
  * [sum_b L_b, row bytes] (sequence b starts at row sum_{b'<b} L_b'), using the
- * same page walk as mla_decode.  Bit-exact copy of the stored rows; async on `stream`. */
+ * same page walk as mla_decode (the block table of PagedAttention, listed under "Builds on"
+ * on the mlsanity.com page of the FlashMLA-ETAP paper: token t of sequence b is row
+ * t % page_size of page block_table[b][t / page_size]).  Bit-exact copy of the stored rows;
+ * async on `stream`.  Entries outside [0, num_pages) are skipped (their rows are not written). */
 mla_status_t mla_debug_gather(mla_plan_t plan, const void* kv_cache, const int32_t* block_table,
                               void* rows_out, void* stream);
 
 /* ---- Device-scheduled decode (no host plan; graph-capturable with changing lengths).
+ * Not on the pages: the split-KV schedule above, computed by the kernels themselves, for
+ * callers that capture the decode in a graph while the lengths change.
  *
  * The work-groups cut the batch's 16-token blocks among themselves at run time from the
  * device cache_seqlens (with W = min(num_workers, T / 4), at least 1, work-group w < W takes
@@ -272,8 +292,14 @@ mla_status_t mla_kv_append(const mla_problem_t* problem, const void* c_kv, const
 mla_status_t mla_out_absorb(const mla_problem_t* problem, const void* out_latent, const void* w_uv, void* o,
                             void* stream);
 
-/* Read the workspace status word (synchronises `stream`).  Bit 0: a block_table
- * entry was out of range in some mla_decode since the last mla_plan_upload. */
+/* Read the workspace status word (synchronises `stream`); this library's own diagnostic.
+ * Bits, each sticky since the last mla_plan_upload (or mla_devplan_prepare):
+ *   bit 0 (1): a used block_table entry was outside [0, num_pages); its tokens were dropped;
+ *   bit 2 (4): a device cache_seqlens value exceeded the plan's (host schedule only); the
+ *              tokens past the plan's length were not attended;
+ *   bit 3 (8): the workspace held another plan's schedule (host schedule only); that launch
+ *              computed nothing.
+ * Bit 1 is not used here (mla_kv_append's own status word uses it). */
 mla_status_t mla_read_status(const void* workspace, void* stream, int32_t* status_out);
 
 void mla_plan_destroy(mla_plan_t plan);            /* NULL is a no-op */

@@ -1,11 +1,17 @@
 // C-ABI entry points: argument validation, workspace layout, launches.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
+#include <unordered_map>
+
+#include <unistd.h>
 
 #include "mla.h"
 #include "mla_internal.h"
@@ -61,6 +67,42 @@ mla_status_t hip_fail(hipError_t e, const char* what) {
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Plan ids: unique within the process and unlikely to repeat across processes (a salt from
+// the process id and the clock in the high half); never zero, so a cleared workspace
+// matches no plan.
+uint64_t next_plan_id() {
+  static const uint64_t salt =
+      ((uint64_t)getpid() << 40) ^ (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  static std::atomic<uint64_t> counter{0};
+  uint64_t id = (salt << 20) ^ (counter.fetch_add(1) + 1);
+  return id ? id : 1;
+}
+
+// Which plan each workspace address last received with mla_plan_upload (host side).
+std::mutex g_ws_mu;
+std::unordered_map<uintptr_t, uint64_t> g_ws_plan;
+
+void register_upload(const void* ws, uint64_t id) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  g_ws_plan[(uintptr_t)ws] = id;
+}
+
+bool holds_plan(const void* ws, uint64_t id) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = g_ws_plan.find((uintptr_t)ws);
+  return it != g_ws_plan.end() && it->second == id;
+}
+
+void forget_plan(uint64_t id) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (auto it = g_ws_plan.begin(); it != g_ws_plan.end();) {
+    if (it->second == id)
+      it = g_ws_plan.erase(it);
+    else
+      ++it;
+  }
+}
 
 // Device-scheduled decode: workers per row group and the workspace layout
 // [status | per-sequence cut (4 x batch + 2 int32) | partial lse (2W x R) | partial out (2W x R x 512)].
@@ -154,7 +196,8 @@ mla_status_t mla_plan(const mla_problem_t* problem, const int32_t* cache_seqlens
   mla_plan_s* pl = new (std::nothrow) mla_plan_s();
   if (!pl) return fail(MLA_ERR_INVALID_ARGUMENT, "out of host memory");
   std::string err;
-  s = mla::build_plan(*problem, cache_seqlens_host, cus, opt.force_splits, opt.rows_per_group, pl->impl, err);
+  s = mla::build_plan(*problem, cache_seqlens_host, cus, opt.force_splits, opt.rows_per_group, next_plan_id(),
+                      pl->impl, err);
   if (s != MLA_OK) {
     delete pl;
     return fail(s, "%s", err.c_str());
@@ -220,6 +263,7 @@ mla_status_t mla_plan_upload(mla_plan_t plan, void* workspace, size_t workspace_
   hipError_t e = hipMemcpyAsync(workspace, plan->impl.meta_host.data(), plan->impl.meta_end,
                                 hipMemcpyHostToDevice, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan upload)");
+  register_upload(workspace, plan->impl.plan_id);
   return MLA_OK;
 }
 
@@ -247,6 +291,9 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
   if (workspace_bytes < p.ws_bytes)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < required %zu B", workspace_bytes, p.ws_bytes);
   if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  if (!holds_plan(workspace, p.plan_id))
+    return fail(MLA_ERR_PLAN_MISMATCH, "workspace %p last received another plan's schedule, or none "
+                "(mla_plan_upload this plan into it first)", workspace);
 
   char* ws = (char*)workspace;
   mla::DecodeArgs a{};
@@ -261,6 +308,9 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
   a.part_lse = (float*)(ws + p.off_lse);
   a.part_o = (float*)(ws + p.off_o);
   a.status = (int32_t*)ws;
+  a.ws_plan_id = (const uint64_t*)(ws + mla::kPlanIdOffset);
+  a.plan_id = p.plan_id;
+  a.plan_len = (const int32_t*)(ws + p.off_lens);
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   a.rows = p.rows;
   a.page_size = p.prob.page_size;
@@ -281,6 +331,8 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
   if ((stages & MLA_STAGE_MERGE) && !p.merges.empty()) {
     mla::MergeArgs m{};
     m.merges = (const int32_t*)(ws + p.off_merges);
+    m.ws_plan_id = a.ws_plan_id;
+    m.plan_id = p.plan_id;
     m.part_lse = a.part_lse;
     m.part_o = a.part_o;
     m.out = out;
@@ -481,6 +533,10 @@ mla_status_t mla_out_absorb(const mla_problem_t* problem, const void* out_latent
   return MLA_OK;
 }
 
-void mla_plan_destroy(mla_plan_t plan) { delete plan; }
+void mla_plan_destroy(mla_plan_t plan) {
+  if (!plan) return;
+  forget_plan(plan->impl.plan_id);
+  delete plan;
+}
 
 }  // extern "C"

@@ -20,11 +20,18 @@ constexpr int kRowBytesBf16 = kDqk * 2;   // 1,152
 constexpr int kRowBytesFp8 = 656;         // 512 E4M3 + 64 bf16 rope + 4 float32 scales
 
 // Workspace layout (byte offsets from the workspace base).
-//   [0, 256)              status word (int32) + padding
-//   [kMetaOffset, ...)    worker offsets, pieces, merge items (int32)
+//   [0, 4)                status word (int32, bits kStatus*)
+//   [8, 16)               id of the plan whose schedule the workspace holds (uint64)
+//   [kMetaOffset, ...)    worker offsets, pieces, merge items, the plan's lengths (int32)
 //   [off_lse, ...)        partial lse   [num_partials][R] fp32
 //   [off_o, ...)          partial out   [num_partials][R][512] fp32
+constexpr size_t kPlanIdOffset = 8;
 constexpr size_t kMetaOffset = 256;
+
+// Bits of the workspace status word (mla_read_status).
+constexpr int32_t kStatusBadPage = 1;        // a used block_table entry was outside [0, num_pages)
+constexpr int32_t kStatusLongerThanPlan = 4; // a device cache_seqlens value exceeded the plan's
+constexpr int32_t kStatusPlanMismatch = 8;   // the workspace held another plan's schedule: nothing ran
 
 struct Piece {            // one (sequence, token range) handled by one work-group
   int32_t seq, tok_begin, tok_end, slot;   // slot -1: write out/lse directly
@@ -51,15 +58,17 @@ struct PlanImpl {
   int32_t merge_uniform = 0;               // ns when item b merges slots [b*ns, (b+1)*ns) for every b
   std::vector<int64_t> worker_cost;
   int32_t num_partials = 0;
+  uint64_t plan_id = 0;                    // nonzero, unique per plan in the process
   // workspace layout
-  size_t off_worker = 0, off_pieces = 0, off_merges = 0, meta_end = 0;
+  size_t off_worker = 0, off_pieces = 0, off_merges = 0, off_lens = 0, meta_end = 0;
   size_t off_lse = 0, off_o = 0, ws_bytes = 0;
   std::vector<uint8_t> meta_host;          // bytes [0, meta_end) as uploaded
 };
 
 // Planner (pure host code).  Returns MLA_OK or an error with `err` filled.
 mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t num_cus,
-                        int32_t force_splits, int32_t rows_per_group, PlanImpl& out, std::string& err);
+                        int32_t force_splits, int32_t rows_per_group, uint64_t plan_id, PlanImpl& out,
+                        std::string& err);
 
 // Parameters of the split-decode kernel.
 // log2(page_size) when the page size is a power of two, else -1 (the kernels then divide)
@@ -82,6 +91,9 @@ struct DecodeArgs {
   float* part_lse;
   float* part_o;
   int32_t* status;
+  const uint64_t* ws_plan_id;    // the plan id stored in the workspace (host schedule only)
+  uint64_t plan_id;              // the id of the plan this launch was made from
+  const int32_t* plan_len;       // [batch] the lengths the plan was made for (host schedule only)
   float scale_log2;              // softmax_scale * log2(e)
   int32_t rows;                  // R
   int32_t page_size;
@@ -100,6 +112,8 @@ struct DecodeArgs {
 
 struct MergeArgs {
   const int32_t* merges;         // int32 quadruples
+  const uint64_t* ws_plan_id;    // host schedule: the plan id stored in the workspace (null: no check)
+  uint64_t plan_id;
   const float* part_lse;
   const float* part_o;
   void* out;

@@ -97,6 +97,23 @@ __device__ __forceinline__ int64_t kv_row_of(TablePtr block_table, int bt_stride
   return (int64_t)page * page_size + r;
 }
 
+// Host schedule: the workspace must hold the schedule of the plan the launch was made from
+// (its id is written by the upload).  Otherwise nothing is read from it: the status word gets
+// kStatusPlanMismatch and every work-group returns.
+__device__ __forceinline__ bool schedule_matches(const DecodeArgs& a) {
+  if (*as_const(a.ws_plan_id) == a.plan_id) return true;
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_or(a.status, kStatusPlanMismatch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+
+// Host schedule: the piece that ends sequence b in the plan (tok_end = the planned length)
+// flags a device length beyond it (those tokens are not attended).
+__device__ __forceinline__ void check_planned_length(const DecodeArgs& a, int b, int te_in, int L) {
+  if (te_in == as_const(a.plan_len)[b] && L > te_in && threadIdx.x == 0)
+    __hip_atomic_fetch_or(a.status, kStatusLongerThanPlan, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float wave_max_over_groups(float x) {
   // lanes l, l^16, l^32, l^48 hold the same query row
   int xi = __float_as_int(x);
@@ -277,6 +294,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     worker = (y / a.row_groups) * 8 + x;
   }
   if (worker >= a.num_workers) return;
+  if (!DEV && !schedule_matches(a)) return;
   const int row0 = rgroup * 16;
   const int R = a.rows;
   const bool stream = a.row_groups == 1;   // KV loads: non-temporal when no other row group re-reads
@@ -315,6 +333,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
 
   // one piece: tokens [tb, min(te_in, L)) of sequence b; slot -1 writes out/lse, else a partial
   auto run_piece = [&](const int b, const int tb, const int te_in, const int slot) {
+    if (!DEV) check_planned_length(a, b, te_in, seqlens[b]);
     const int te = min(te_in, seqlens[b]);
     const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
     // end of the tokens this lane's query row sees: te, or for a causal problem the
@@ -527,7 +546,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           // A block whose table entry was out of range (its DMA read page 0) takes the same
           // path with every row zeroed and every score masked, so it adds nothing; one loop
           // body without a skip keeps the accumulators in place across iterations.
-          if (!ok && lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (!ok && lane == 0) __hip_atomic_fetch_or(a.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const int tok0 = tb + kBlock * blk_of(k);
           const int vvalid = ok ? te - tok0 : 0;    // rows of the block inside the piece
           if (vvalid < kBlock) {
@@ -549,7 +568,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < 16; ++kk) {
-            const float sc = __uint_as_float(ksc[kk >> 2]);
+            const float sc = __uint_as_float(ksc[kk >> 2] & 0x7F800000u);   // the scale's exponent only
             u32x4_t kf;
             kf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[kk][0], sc, false));
             kf[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[kk][0], sc, true));
@@ -616,7 +635,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
           const bool ok = (k & 1) ? ok1 : ok0;
           if (k & 1) ok1 = nok; else ok0 = nok;   // the stage's next occupant
           if (!ok) {
-            if (lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_fetch_or(a.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (nx) issue(nsrc, st);
             continue;
           }
@@ -871,6 +890,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
     worker = (y / a.row_groups) * 8 + x;
   }
   if (worker >= a.num_workers) return;
+  if (!schedule_matches(a)) return;
   const int R = a.rows;
   const bool stream = a.row_groups == 1;   // KV loads: non-temporal when no other row group re-reads
   const int row0 = rgroup * 16 * RG + 16 * rg;
@@ -889,6 +909,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
   for (int pi = p_begin; pi < p_end; ++pi) {
     const int b = pieces[4 * pi + 0];
     const int tb = pieces[4 * pi + 1];
+    check_planned_length(a, b, pieces[4 * pi + 2], seqlens[b]);
     const int te = min(pieces[4 * pi + 2], seqlens[b]);
     const int slot = pieces[4 * pi + 3];
     const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
@@ -1031,7 +1052,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         if (use0 && kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok0) < 0) use0 = false;
         if (use1 && kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok1) < 0) use1 = false;
         if ((blk0 < nblk && !use0) || (blk0 + 1 < nblk && !use1)) {
-          if (lane == 0) __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0) __hip_atomic_fetch_or(a.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if constexpr (TS) {
           // this wave's block of the step; an unused block is skipped (no other wave of the
@@ -1210,6 +1231,7 @@ __device__ __forceinline__ void merge_batch(const float (&l)[kMergeBatch], const
 constexpr int kMergeCols = 64;
 template <bool OUT_F32>
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
+  if (*as_const(a.ws_plan_id) != a.plan_id) return;   // another plan's schedule: the split launch flagged it
   const int R = a.rows;
   const int col_groups = kDv / kMergeCols;
   const int per_item = (R / 16) * col_groups;

@@ -27,9 +27,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
 mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t num_cus,
-                        int32_t force_splits, int32_t rows_per_group, PlanImpl& pl, std::string& err) {
+                        int32_t force_splits, int32_t rows_per_group, uint64_t plan_id, PlanImpl& pl,
+                        std::string& err) {
   pl = PlanImpl{};
   pl.prob = p;
+  pl.plan_id = plan_id;
   pl.num_cus = num_cus;
   const int32_t B = p.batch;
   const int64_t R = (int64_t)p.q_len * p.num_heads;
@@ -180,12 +182,16 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
   pl.off_worker = kMetaOffset;
   pl.off_pieces = align_up(pl.off_worker + 4 * pl.worker_off.size(), 16);
   pl.off_merges = align_up(pl.off_pieces + sizeof(Piece) * pl.pieces.size(), 16);
-  pl.meta_end = align_up(pl.off_merges + sizeof(MergeItem) * pl.merges.size(), 256);
+  pl.off_lens = align_up(pl.off_merges + sizeof(MergeItem) * pl.merges.size(), 16);
+  pl.meta_end = align_up(pl.off_lens + 4 * (size_t)B, 256);
   pl.off_lse = pl.meta_end;
   pl.off_o = align_up(pl.off_lse + 4 * (size_t)pl.num_partials * R, 256);
   pl.ws_bytes = align_up(pl.off_o + 4 * (size_t)pl.num_partials * R * kDv, 256);
 
+  // bytes [0, meta_end) as uploaded: a cleared status word, the plan id, the schedule
   pl.meta_host.assign(pl.meta_end, 0);
+  std::memcpy(pl.meta_host.data() + kPlanIdOffset, &pl.plan_id, sizeof pl.plan_id);
+  std::memcpy(pl.meta_host.data() + pl.off_lens, seqlens, 4 * (size_t)B);
   std::memcpy(pl.meta_host.data() + pl.off_worker, pl.worker_off.data(), 4 * pl.worker_off.size());
   if (!pl.pieces.empty())
     std::memcpy(pl.meta_host.data() + pl.off_pieces, pl.pieces.data(), sizeof(Piece) * pl.pieces.size());

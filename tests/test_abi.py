@@ -23,7 +23,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) >= 12
     for n in names:
         assert hasattr(lib, n), f"libmla.so does not export {n}"
-    assert B.abi_version() == 4
+    assert B.abi_version() == 5
 
 
 def test_status_strings():
@@ -209,3 +209,41 @@ def test_last_error_is_per_thread():
     for t in threads:
         t.join()
     assert not bad, bad[:3]
+
+
+def test_every_declared_status_code_is_returned():
+    """Each status code mla.h declares comes back from some call on this (GPU-less) host, before
+    anything is launched."""
+    import torch
+    lib = B.lib()
+    prob = B.make_problem(2, 1, 16, 64, 4, 2)
+    sl = (C.c_int32 * 2)(100, 50)
+    h = C.c_void_p()
+    seen = {}
+    opt = B.mla_plan_options_t(256, 0)
+    seen[B.MLA_OK] = lib.mla_plan(C.byref(prob), sl, C.byref(opt), C.byref(h))
+    n = lib.mla_plan_workspace_bytes(h)
+    fake = 1 << 20
+    bad = B.make_problem(2, 1, 8, 64, 4, 2)
+    h2 = C.c_void_p()
+    seen[B.MLA_ERR_UNSUPPORTED] = lib.mla_plan(C.byref(bad), sl, C.byref(opt), C.byref(h2))
+    seen[B.MLA_ERR_INVALID_ARGUMENT] = lib.mla_plan(None, sl, C.byref(opt), C.byref(h2))
+    seen[B.MLA_ERR_WORKSPACE_TOO_SMALL] = lib.mla_plan_upload(h, fake, n - 1, None)
+    # a workspace that never received this plan's schedule: refused before any launch
+    seen[B.MLA_ERR_PLAN_MISMATCH] = lib.mla_decode(h, fake, fake, fake, fake, C.c_float(0.1), fake, fake, fake, n,
+                                                   None)
+    assert "mla_plan_upload" in B.last_error()
+    for code, got in seen.items():
+        assert got == code, (code, got, B.last_error())
+    if not torch.cuda.is_available():
+        opt0 = B.mla_plan_options_t(0, 0)          # ask the (absent) device for its CU count
+        assert lib.mla_plan(C.byref(prob), sl, C.byref(opt0), C.byref(h2)) == B.MLA_ERR_HIP
+        assert "hipGetDevice" in B.last_error()
+        assert lib.mla_plan_upload(h, fake, n, None) == B.MLA_ERR_HIP
+        # a failed upload records nothing: the decode is still refused
+        assert lib.mla_decode(h, fake, fake, fake, fake, C.c_float(0.1), fake, fake, fake, n, None) == \
+            B.MLA_ERR_PLAN_MISMATCH
+    declared = set(int(x) for x in re.findall(r"MLA_(?:OK|ERR_[A-Z_]+) = (\d+)", open(os.path.join(
+        ROOT, "include", "mla.h")).read()))
+    assert declared == set(range(6))
+    lib.mla_plan_destroy(h)

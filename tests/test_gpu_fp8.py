@@ -143,6 +143,26 @@ def test_fp8_full_size(name):
     compare_every_sequence(out, lse, ref_o, ref_l, f"{name} fp8")
 
 
+@pytest.mark.parametrize("out_fp32", [True, False])
+def test_fp8_scales_with_mantissa_bits_use_the_exponent_only(out_fp32):
+    """Group scales that are not powers of two (1.5 * 2^e, 1.9375 * 2^e): only their exponent
+    counts (the row format; the oracle decodes it that way).  Equal, bit for bit, to the same
+    cache with the scales' mantissas cleared, and to the oracle within the usual bounds."""
+    prob = gen.make_problem(batch=3, q_len=1, num_heads=64, page_size=64, lengths=[2100, 333, 64], seed=57,
+                            kv_format="fp8", out_fp32=out_fp32)
+    kv = prob.kv_cache.copy()
+    sc = np.ascontiguousarray(kv[..., 640:656]).view(np.uint32)
+    mant = np.where(np.arange(sc.size).reshape(sc.shape) % 2 == 0, 0x00400000, 0x00780000).astype(np.uint32)
+    kv[..., 640:656] = (sc | mant).view(np.uint8)
+    odd = gen.Problem(q=prob.q, kv_cache=kv, block_table=prob.block_table, cache_seqlens=prob.cache_seqlens,
+                      softmax_scale=prob.softmax_scale, page_size=64, out_fp32=out_fp32)
+    o1, l1 = run(odd)
+    o0, l0 = run(prob)
+    assert np.array_equal(o1, o0) and np.array_equal(l1, l0)
+    ref_o, ref_l = oracle(odd)
+    check(o1, l1, ref_o, ref_l, out_fp32, "scales with mantissa bits", None if out_fp32 else softmax_abs_v(odd))
+
+
 def test_fp8_out_of_range_block_table_entry_drops_its_tokens():
     """A used table entry outside [0, num_pages): its 16-token blocks are masked out (their DMA
     reads page 0), bit 0 of the status word is set, and the rest is exact."""

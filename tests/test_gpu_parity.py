@@ -382,6 +382,87 @@ def test_out_of_range_entry_drops_one_block(heads, rpg):
     check_dropped_page(prob, out, lse, seq=1, page_idx=5)
 
 
+def test_workspace_of_another_plan_is_refused():
+    """Two plans, one workspace: after plan B's upload, a decode with plan A is refused on the
+    host (MLA_ERR_PLAN_MISMATCH, nothing launched); plan B decodes; A decodes again after its
+    own upload."""
+    import torch
+    pa = gen.make_problem(batch=2, q_len=1, num_heads=16, page_size=64, lengths=[3000, 500], seed=43)
+    pb = gen.make_problem(batch=2, q_len=1, num_heads=16, page_size=64, lengths=[700, 5000], seed=44)
+    ra, rb = Runner(pa), Runner(pb)
+    ws = ra.ws if ra.ws.numel() >= rb.ws.numel() else rb.ws
+    ra.ws = rb.ws = ws
+    for r in (ra, rb):
+        d = r.dev
+        r._bound = B.BoundDecode(r.plan, d["q"], d["kv_cache"], d["block_table"], d["cache_seqlens"],
+                                 r.prob.softmax_scale, r.out, r.lse, ws)
+    ra.plan.upload(ws)
+    rb.plan.upload(ws)
+    ra.out.fill_(7.0)
+    with pytest.raises(B.MlaError) as ei:
+        ra()
+    assert ei.value.status == B.MLA_ERR_PLAN_MISMATCH
+    torch.cuda.synchronize()
+    assert bool(torch.all(ra.out == 7.0))
+    rb()
+    out, lse = rb.results()
+    compare(out, lse, *oracle(pb), what="plan B in the shared workspace")
+    ra.plan.upload(ws)
+    ra()
+    out, lse = ra.results()
+    compare(out, lse, *oracle(pa), what="plan A after its own upload")
+    assert B.mla_read_status(ws) == 0
+
+
+@pytest.mark.parametrize("heads", [16, 128])
+def test_overwritten_plan_id_is_caught_on_the_device(heads):
+    """The host record says the workspace holds the plan, but its id bytes were overwritten (as
+    by another upload after a graph capture): the kernels read no schedule, out and lse stay
+    as they were, and status bit 3 is set."""
+    import torch
+    prob = gen.make_problem(batch=2, q_len=1, num_heads=heads, page_size=64, lengths=[3000, 500], seed=45)
+    r = Runner(prob)
+    r.ws[8:16].zero_()
+    r.out.fill_(7.0)
+    r.lse.fill_(3.0)
+    r()
+    torch.cuda.synchronize()
+    assert bool(torch.all(r.out == 7.0)) and bool(torch.all(r.lse == 3.0))
+    assert B.mla_read_status(r.ws) == 8
+    r.plan.upload(r.ws)                       # a fresh upload restores the id and clears the status
+    r()
+    out, lse = r.results()
+    compare(out, lse, *oracle(prob), what="after a fresh upload")
+    assert B.mla_read_status(r.ws) == 0
+
+
+@pytest.mark.parametrize("heads", [16, 128])
+def test_device_length_beyond_the_plan_is_flagged(heads):
+    """Device cache_seqlens above the planned ones: the extra tokens are not attended (the
+    result is the plan's), and status bit 2 is set; shorter device lengths are honoured
+    without a flag."""
+    import torch
+    prob = gen.make_problem(batch=3, q_len=1, num_heads=heads, page_size=64, lengths=[3000, 500, 64], seed=46,
+                            extra_pages=4)
+    r = Runner(prob)
+    longer = prob.cache_seqlens.copy()
+    longer[1] += 100                          # past the sequence's mapped pages: never read
+    r.dev["cache_seqlens"].copy_(torch.from_numpy(longer.astype(np.int32)))
+    r()
+    out, lse = r.results()
+    assert B.mla_read_status(r.ws) == 4
+    compare(out, lse, *oracle(prob), what="clipped to the planned lengths")
+    r.plan.upload(r.ws)
+    shorter = prob.cache_seqlens.copy()
+    shorter[0] -= 1000
+    r.dev["cache_seqlens"].copy_(torch.from_numpy(shorter.astype(np.int32)))
+    r()
+    out, lse = r.results()
+    assert B.mla_read_status(r.ws) == 0
+    ref_o, ref_l = orc.decode(prob.q, prob.kv_cache, prob.block_table, shorter, prob.softmax_scale, prob.page_size)
+    compare(out, lse, ref_o, ref_l, what="shorter device lengths")
+
+
 def check_dropped_page(prob, out, lse, seq, page_idx, tol=(RMSE_TOL, MAX_TOL, LSE_TOL)):
     """Sequence `seq` must equal attention over its tokens outside table entry `page_idx`."""
     P, L = prob.page_size, int(prob.cache_seqlens[seq])
