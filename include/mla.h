@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 5
+#define MLA_ABI_VERSION 6
 
 typedef enum {
   MLA_OK = 0,
@@ -239,6 +239,23 @@ mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_worker
                                 const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
                                 float softmax_scale, void* out, float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* The device-scheduled decode for callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same computation and
+ * kernels as mla_decode_devplan, with its workspace taken from a scratch array the library
+ * holds in device memory, MLA_NOALLOC_SCRATCH_BYTES per GPU, from the first call on that GPU
+ * until the process ends.  Nothing is allocated (no hipMalloc, no hipFree); the caller passes
+ * inputs and outputs only.  A problem whose device schedule needs more scratch than that
+ * (mla_devplan_workspace_bytes(problem, num_workers) > MLA_NOALLOC_SCRATCH_BYTES; with
+ * num_workers = 0 on a 256-CU MI355X it needs about 16.8 MB plus 16 bytes per sequence) is
+ * refused with MLA_ERR_WORKSPACE_TOO_SMALL before any launch.  Every call on a GPU uses that
+ * GPU's one array: calls that overlap in time on one GPU (two streams, two threads) race and
+ * must not be made.  Its status word is not reported. */
+#define MLA_NOALLOC_SCRATCH_BYTES (24u << 20)
+mla_status_t mla_decode_devplan_noalloc(const mla_problem_t* problem, int32_t num_workers, const void* q,
+                                        const void* kv_cache, const int32_t* block_table,
+                                        const int32_t* cache_seqlens, float softmax_scale, void* out, float* lse,
+                                        void* stream);
 
 /* ---- The steps on either side of the decode (an absorbed MLA attention layer).
  *

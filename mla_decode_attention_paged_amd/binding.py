@@ -77,6 +77,9 @@ _SIGS = {
     "mla_decode_devplan": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                      C.c_void_p]),
+    "mla_decode_devplan_noalloc": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_void_p,
+                                             C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p,
+                                             C.c_void_p]),
     "mla_q_absorb": (C.c_int, [C.POINTER(mla_problem_t), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                C.c_float, C.c_void_p, C.c_void_p]),
     "mla_kv_append": (C.c_int, [C.POINTER(mla_problem_t), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -324,6 +327,24 @@ class BoundDevplanDecode:
         st = self._fn(*self._args, stream_handle)
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_devplan", last_error())
+
+
+def mla_decode_devplan_noalloc(problem: mla_problem_t, num_workers, q, kv_cache, block_table, cache_seqlens,
+                               softmax_scale, out, lse, stream=None):
+    """Device-scheduled decode with the library's own device scratch (allocates nothing)."""
+    import torch
+    p = problem
+    _require(q, "q", (torch.bfloat16,), (p.batch, p.q_len, p.num_heads, 576))
+    _require(kv_cache, "kv_cache", *_kv_spec(p))
+    _require(block_table, "block_table", (torch.int32,), (p.batch, p.max_pages_per_seq))
+    _require(cache_seqlens, "cache_seqlens", (torch.int32,), (p.batch,))
+    odt = torch.float32 if p.out_dtype == MLA_DTYPE_FP32 else torch.bfloat16
+    _require(out, "out", (odt,), (p.batch, p.q_len, p.num_heads, 512))
+    if lse is not None:
+        _require(lse, "lse", (torch.float32,), (p.batch, p.q_len, p.num_heads))
+    _check(lib().mla_decode_devplan_noalloc(C.byref(p), num_workers, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                            _ptr(cache_seqlens), C.c_float(float(softmax_scale)), _ptr(out),
+                                            _ptr(lse), _stream(stream)), "mla_decode_devplan_noalloc")
 
 
 def mla_read_status(workspace, stream=None) -> int:

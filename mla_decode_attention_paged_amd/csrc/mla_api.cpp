@@ -135,6 +135,19 @@ mla_status_t dev_layout(const mla_problem_t* p, int32_t num_workers, DevLayout& 
   return MLA_OK;
 }
 
+// Pointer and scale checks shared by the device-scheduled entry points.
+mla_status_t check_devplan_args(const void* q, const void* kv_cache, const int32_t* block_table,
+                                const int32_t* cache_seqlens, float softmax_scale, const void* out, const float* lse) {
+  if (!q || !kv_cache || !block_table || !cache_seqlens || !out)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if ((uintptr_t)q % 16 || (uintptr_t)kv_cache % 16 || (uintptr_t)out % 16)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "q, kv_cache and out must be 16-B aligned");
+  if ((uintptr_t)block_table % 4 || (uintptr_t)cache_seqlens % 4 || (uintptr_t)lse % 4)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "block_table, cache_seqlens and lse must be 4-B aligned");
+  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -389,16 +402,12 @@ mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_worker
   DevLayout d;
   mla_status_t s = dev_layout(problem, num_workers, d);
   if (s != MLA_OK) return s;
-  if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !workspace)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
-  if ((uintptr_t)q % 16 || (uintptr_t)kv_cache % 16 || (uintptr_t)out % 16)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "q, kv_cache and out must be 16-B aligned");
-  if ((uintptr_t)block_table % 4 || (uintptr_t)cache_seqlens % 4 || (uintptr_t)lse % 4)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "block_table, cache_seqlens and lse must be 4-B aligned");
+  s = check_devplan_args(q, kv_cache, block_table, cache_seqlens, softmax_scale, out, lse);
+  if (s != MLA_OK) return s;
+  if (!workspace) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if ((uintptr_t)workspace % 256 != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace must be 256-B aligned");
   if (workspace_bytes < d.bytes)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu B < required %zu B", workspace_bytes, d.bytes);
-  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
   const mla_problem_t& p = *problem;
   char* ws = (char*)workspace;
   mla::DecodeArgs a{};
@@ -440,6 +449,26 @@ mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_worker
   e = mla::launch_merge_dev(m, f32, stream);
   if (e) return fail(MLA_ERR_HIP, "device-scheduled merge launch: %s", mla::hip_error_string(e));
   return MLA_OK;
+}
+
+mla_status_t mla_decode_devplan_noalloc(const mla_problem_t* problem, int32_t num_workers, const void* q,
+                                        const void* kv_cache, const int32_t* block_table,
+                                        const int32_t* cache_seqlens, float softmax_scale, void* out, float* lse,
+                                        void* stream) {
+  DevLayout d;
+  mla_status_t s = dev_layout(problem, num_workers, d);
+  if (s != MLA_OK) return s;
+  s = check_devplan_args(q, kv_cache, block_table, cache_seqlens, softmax_scale, out, lse);
+  if (s != MLA_OK) return s;
+  if (d.bytes > MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "the device schedule needs %zu B of scratch; the library holds %u B per GPU", d.bytes,
+                (unsigned)MLA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const int e = mla::noalloc_scratch(&ws);
+  if (e) return fail(MLA_ERR_HIP, "scratch address: %s", mla::hip_error_string(e));
+  return mla_decode_devplan(problem, num_workers, q, kv_cache, block_table, cache_seqlens, softmax_scale, out, lse,
+                            ws, MLA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 mla_status_t mla_read_status(const void* workspace, void* stream, int32_t* status_out) {

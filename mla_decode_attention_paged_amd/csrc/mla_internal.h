@@ -160,5 +160,8 @@ int launch_gather(const void* kv, const int32_t* block_table, void* rows_out, in
                   int64_t row_offset, int32_t page_size, int32_t bt_stride, int32_t num_pages, int32_t row_bytes,
                   void* stream);
 const char* hip_error_string(int code);
+// Device address of this GPU's scratch array (MLA_NOALLOC_SCRATCH_BYTES) for the entry point that
+// allocates nothing; looked up once per device.  Returns a HIP error code (0 = success).
+int noalloc_scratch(void** out);
 
 }  // namespace mla

@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "mla_internal.h"
 
@@ -1435,5 +1436,29 @@ int launch_gather(const void* kv, const int32_t* block_table, void* rows_out, in
 }
 
 const char* hip_error_string(int code) { return hipGetErrorString((hipError_t)code); }
+
+// Workspace of mla_decode_devplan_noalloc: one array per GPU, held until the process ends.  In
+// host code `scratch` only names the symbol; its device address comes from hipGetSymbolAddress,
+// once per device with that device current, and only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+int noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return 0;
+}
 
 }  // namespace mla

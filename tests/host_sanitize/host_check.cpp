@@ -28,6 +28,7 @@ int launch_q_absorb(const LayerArgs&, void*) { no_kernels("q_absorb"); }
 int launch_kv_append(const LayerArgs&, void*) { no_kernels("kv_append"); }
 int launch_out_absorb(const LayerArgs&, bool, bool, void*) { no_kernels("out_absorb"); }
 const char* hip_error_string(int) { return "no kernels in the host check"; }
+int noalloc_scratch(void**) { no_kernels("noalloc_scratch"); }
 }  // namespace mla
 
 #define CHECK(c)                                                              \
@@ -187,6 +188,15 @@ static bool validation_paths() {
   CHECK(mla_devplan_prepare(&p, 256, fake, dn - 1, nullptr) == MLA_ERR_WORKSPACE_TOO_SMALL);
   CHECK(mla_decode_devplan(&p, 256, fake + 8, fake, (int32_t*)fake, (int32_t*)fake, 0.1f, fake, (float*)fake, fake,
                            dn, nullptr) == MLA_ERR_INVALID_ARGUMENT);
+  // the entry point without a workspace: a schedule larger than its scratch is refused first
+  CHECK(mla_decode_devplan_noalloc(&p, 1 << 20, fake, fake, (int32_t*)fake, (int32_t*)fake, 0.1f, fake,
+                                   (float*)fake, nullptr) == MLA_ERR_WORKSPACE_TOO_SMALL);
+  CHECK(mla_decode_devplan_noalloc(&p, -1, fake, fake, (int32_t*)fake, (int32_t*)fake, 0.1f, fake, (float*)fake,
+                                   nullptr) == MLA_ERR_INVALID_ARGUMENT);
+  CHECK(mla_decode_devplan_noalloc(&p, 256, nullptr, fake, (int32_t*)fake, (int32_t*)fake, 0.1f, fake,
+                                   (float*)fake, nullptr) == MLA_ERR_INVALID_ARGUMENT);
+  CHECK(mla_decode_devplan_noalloc(&p, 256, fake, fake, (int32_t*)fake, (int32_t*)fake, __builtin_inff(), fake,
+                                   (float*)fake, nullptr) == MLA_ERR_INVALID_ARGUMENT);
   CHECK(mla_q_absorb(&p, nullptr, fake, fake, (int32_t*)fake, 10000.f, fake, nullptr) == MLA_ERR_INVALID_ARGUMENT);
   CHECK(mla_kv_append(&p, fake, fake, (int32_t*)fake, (int32_t*)fake, -1.f, fake, nullptr, nullptr) ==
         MLA_ERR_INVALID_ARGUMENT);
