@@ -1203,6 +1203,480 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Wide split-decode kernel: 128 query rows per work-group, 32 per wave, on 32x32x16 bf16 MFMA.
+//
+// The four waves consume every 32-token block of a piece from a shared ring of four LDS slots
+// (three blocks in flight while one is computed); wave w moves token octet w of each block
+// (9 global->LDS loads of 1 KB).  Wave w owns query rows 32w..32w+31 of the row group:
+//   S^T = K Q^T     M = 32 tokens, N = 32 rows, K = 576 (36 MFMAs); Q^T's 512 latent columns
+//                   resident in VGPRs, its 64 rope columns in the LDS left beside the slots
+//   P^T = exp2(S^T - m)                                   (16 scores per lane)
+//   O^T += V^T P^T  M = 32 columns, N = 32 rows, K = 16 tokens (2 MFMAs per 32-column tile)
+// so every K and V^T byte read from LDS feeds 32 query rows (the transposed flow of the
+// FlashMLA-ETAP summary, "Core mechanism", with the matrix unit's wide 32x32 shape filled by
+// tokens and rows alike).  O^T (512 x 32 per wave) stays in accumulation registers.
+//
+// Softmax without mid-stream rescaling: each row's reference m is the maximum of its scores in
+// the piece's first block, and p = exp2(s - m) is accumulated as is while every later score
+// stays within kWSlack (log2 units) of m (p <= 2^32: no overflow in bf16 or fp32).  A piece in
+// which some score exceeds that is computed once more from the start with m set to the row's
+// true maximum, which the first pass has found; so the accumulators are only ever touched by
+// MFMAs.
+//
+// Block layout in LDS (16-B units): chunk c (columns 8c..8c+7) of token t sits at unit
+// 256 (c / 8) + 8 t + ((c % 8) ^ wswz(t)).  One DMA load fills 8 tokens x 8 chunks; the swizzle
+// makes the K reads (32 tokens x one chunk) and the V^T transpose reads (4 tokens x 16 columns
+// per 16 lanes) hit distinct banks.
+constexpr int kWBlock = 32;                              // tokens per block
+constexpr int kWBlockBytes = kWBlock * kRowBytesBf16;    // 36,864
+constexpr int kWSlots = 4;
+constexpr int kWQRope = kWSlots * kWBlockBytes;          // the query's rope columns: [wave][4][64 lanes] x 16 B
+constexpr int kWSmem = kWQRope + kWaves * 4 * 64 * 16;   // 163,840: all of the LDS
+constexpr float kWSlack = 32.0f;
+constexpr int kWRing = 4;                                // K operands in flight in S^T
+constexpr int kWVRing = 3;                               // V^T operands (32-column tiles) in flight in O^T
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int wswz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+// byte offset of chunk c of token t within a block
+__device__ __forceinline__ int wunit(int t, int c) { return 16 * (256 * (c >> 3) + 8 * t + ((c & 7) ^ wswz(t))); }
+
+// One wave's token octet of a block: load cg (0..8) reads 16 B per lane at base + voff + 128 cg
+// and writes 1 KB at m0 + 4096 cg (the instruction offset applies to both addresses, so M0
+// steps by 3,968).  Saves and restores M0; hidden from the compiler's counters.
+template <bool NT>
+__device__ __forceinline__ void dma_wide_octet(const uint8_t* base, uint32_t voff, uint32_t m0) {
+  uint32_t sv;
+#define MLA_W1(OFF, NTS) "s_add_u32 m0, m0, 3968\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3 offset:" OFF NTS "\n\t"
+#define MLA_WIDE_DMA(NTS)                                                                       \
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"                          \
+               "global_load_lds_dwordx4 %1, %3" NTS "\n\t"                                    \
+               MLA_W1("128", NTS) MLA_W1("256", NTS) MLA_W1("384", NTS) MLA_W1("512", NTS)    \
+               MLA_W1("640", NTS) MLA_W1("768", NTS) MLA_W1("896", NTS) MLA_W1("1024", NTS)   \
+               "s_mov_b32 m0, %0"                                                             \
+               : "=&s"(sv)                                                                    \
+               : "v"(voff), "s"(m0), "s"(base)                                                \
+               : "memory", "scc")
+  if constexpr (NT)
+    MLA_WIDE_DMA(" nt");
+  else
+    MLA_WIDE_DMA("");
+#undef MLA_WIDE_DMA
+#undef MLA_W1
+}
+
+// S^T steps on a 32x32x16 bf16 MFMA with the accumulator in VGPRs: the 512 x 32 O^T tile fills
+// all 256 accumulation registers, and the builtin would borrow 16 of them (moving an O^T tile out
+// and back around every block).  acc = a b (first step, no accumulator input), acc += a b, and the
+// last step, which adds 20 wait states so that vector instructions may read acc right after it
+// (an 8-pass MFMA result read by the VALU needs 11; back-to-back accumulation into the same
+// registers needs none).
+__device__ __forceinline__ void mfma32_vfirst(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_vacc(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_vlast(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+template <bool OUT_F32, bool NT>
+__global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWSmem];
+  LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 31, h = lane >> 5;
+
+  int worker, rgroup;
+  if (a.row_groups == 1) {
+    worker = blockIdx.x;
+    rgroup = 0;
+  } else {
+    // the row groups of one token range land on the same XCD (ids are dealt round-robin to 8 XCDs)
+    const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+    rgroup = y % a.row_groups;
+    worker = (y / a.row_groups) * 8 + x;
+  }
+  if (worker >= a.num_workers) return;
+  if (!schedule_matches(a)) return;
+  const int R = a.rows;
+  const int rbase = rgroup * 128 + 32 * wave;
+  const int row = rbase + i;
+  LDS_AS uint8_t* const qrope = lds + kWQRope + 4096 * wave + 16 * lane;   // this lane's rope operands
+
+  // LDS read offsets within a block.  K, k-step kk: token i, chunk 2 kk + h, at
+  // kb0 ^ 32 (kk % 4) + 4096 (kk / 4) (chunk bits 1-2 sit at byte bits 5-6, above the xor's reach)
+  const int kb0 = wunit(i, h);
+  // V^T, 32-column tile cc, token half u, part jp: lane n = 4e + qq of 16-lane group g addresses
+  // token 16u + 8jp + 4(g / 2) + e, the 8 bytes of columns 32cc + 16(g % 2) + 4qq..+3; the
+  // transpose hands lane (i, h) column 32cc + i of tokens 16u + 8jp + 4h + 0..3.
+  //   offset = (vb[jp] ^ 64 (cc % 2)) + 4096 (cc / 2) + 2048 u  (an odd tile flips chunk bit 2, byte bit 6)
+  int vb[2];
+  {
+    const int g = lane >> 4, n = lane & 15, e = n >> 2, qq = n & 3;
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) vb[jp] = wunit(8 * jp + 4 * (g >> 1) + e, 2 * (g & 1) + (qq >> 1)) + 8 * (qq & 1);
+  }
+  // DMA: lane L moves token 8 wave + L / 8 of the block, chunks 8 cg + ((L % 8) ^ wswz(token))
+  const int dma_tok = 8 * wave + (lane >> 3);
+  const uint32_t dma_col = 16u * (uint32_t)((lane & 7) ^ wswz(dma_tok));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+
+  const CST_AS int32_t* worker_off = as_const(a.worker_off);
+  const CST_AS int32_t* pieces = as_const(a.pieces);
+  const CST_AS int32_t* seqlens = as_const(a.seqlens);
+  const CST_AS int32_t* block_table = as_const(a.block_table);
+  const uint8_t* const kv8 = (const uint8_t*)a.kv;
+
+  const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
+  for (int pi = p_begin; pi < p_end; ++pi) {
+    const int b = pieces[4 * pi + 0];
+    const int tb = pieces[4 * pi + 1];
+    check_planned_length(a, b, pieces[4 * pi + 2], seqlens[b]);
+    const int L = seqlens[b];
+    const int te = min(pieces[4 * pi + 2], L);
+    const int slot = pieces[4 * pi + 3];
+    const int nblk = te > tb ? (te - tb + kWBlock - 1) / kWBlock : 0;
+    // end of the tokens this lane's row sees (causal: the first L - (q_len - 1 - i)); the
+    // smallest over the wave's rows is its first row's (rows increase with the query token)
+    const int lim = a.causal ? min(te, L - (a.q_len - 1 - row / a.num_heads)) : te;
+    const int lim_min = a.causal ? min(te, L - (a.q_len - 1 - rbase / a.num_heads)) : te;
+
+    // query rows as MFMA B operands: lane (i, h) holds row i, columns 16 kk + 8 h .. + 7; the
+    // latent k-steps (kk < 32) in VGPRs, the rope ones in this lane's LDS area (only this wave
+    // reads it, in program order after the writes)
+    bf16x8_t qf[32];
+    {
+      // the wave's first row (uniform) plus a 32-bit lane offset
+      const uint8_t* qw = (const uint8_t*)(a.q + ((int64_t)b * R + rbase) * kDqk);
+      const uint32_t qo = (uint32_t)i * kRowBytesBf16 + 16u * h;
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) qf[kk] = *(const bf16x8_t*)(qw + qo + 32 * kk);
+#pragma unroll
+      for (int kr = 0; kr < 4; ++kr) *(LDS_AS u32x4_t*)(qrope + 1024 * kr) = *(const u32x4_t*)(qw + qo + 1024 + 32 * kr);
+      // every query load has landed (an s_waitcnt the compiler sees, so that it does not wait
+      // for them again inside the block loop, where its count would include the DMA loads)
+      __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+    }
+
+    // Block k's page walk: the rows of its two 16-token halves' first tokens (clamped to the
+    // piece; -1 for an out-of-range table entry).  A half never spans two pages (pieces start on
+    // 16-token boundaries and pages hold a multiple of 16 tokens).
+    struct Walk {
+      int64_t row[2];
+    };
+    auto walk = [&](int k) -> Walk {
+      const int t0 = tb + kWBlock * k;
+      const int t1 = min(t0 + 16, te - 1);
+      return Walk{{kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, t0),
+                   kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, t1)}};
+    };
+    auto halves_ok = [&](const Walk& w) -> uint32_t { return (w.row[0] >= 0 ? 1u : 0u) | (w.row[1] >= 0 ? 2u : 0u); };
+    // This wave's octet of block k (half wave / 2, 8 (wave % 2) tokens into it): its SGPR row
+    // base, page 0 for an out-of-range entry (the octet is then zeroed and masked).  Lanes past
+    // the end re-read the last row of the piece.
+    auto octet_base = [&](int k, const Walk& w) -> const uint8_t* {
+      const int64_t r = (wave >> 1) ? w.row[1] : w.row[0];
+      const int t_half = min(tb + kWBlock * k + 16 * (wave >> 1), te - 1);     // the half's first row
+      const int ts = min(tb + kWBlock * k + 8 * wave, te - 1);                  // the octet's first row
+      return kv8 + (r < 0 ? 0 : r + (ts - t_half)) * kRowBytesBf16;
+    };
+    auto octet_voff = [&](int k) -> uint32_t {
+      const int tok0 = tb + kWBlock * k;
+      const int ts = min(tok0 + 8 * wave, te - 1);
+      const int t = min(tok0 + dma_tok, te - 1);
+      return (uint32_t)(t - ts) * kRowBytesBf16 + dma_col;
+    };
+    // NT: non-temporal loads (one row group: no other work-group re-reads these rows)
+    auto issue = [&](int k, const uint8_t* base) {
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((k % kWSlots) * kWBlockBytes + 1024 * wave));
+      dma_wide_octet<NT>(base, octet_voff(k), m0);
+    };
+
+    float m_run = -INFINITY;     // the row's largest scaled score so far (log2 units)
+    bool bad_page = false;       // an octet of this wave read an out-of-range table entry
+    // scale * log2(e), kept away from zero (|c| >= 2^-100: with a smaller scale every weight
+    // is 1 in float32 either way), so that the masked-token score s_hide scales to -inf
+    const float c_log2 = fabsf(a.scale_log2) >= 0x1p-100f ? a.scale_log2 : copysignf(0x1p-100f, a.scale_log2);
+    const float s_hide = c_log2 > 0.f ? -INFINITY : INFINITY;
+    f32x16_t o[16];
+    float m_ref, lsum;
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) o[c][q] = 0.f;
+      m_ref = pass ? fmaxf(m_run, kNegBig) : kNegBig;
+      lsum = 0.f;
+      bool ovf = false;
+      uint32_t okq = 0;          // bits 2 (k % 4) + 0..1: block k's halves were in range
+      // Blocks 0 and 1 go out first; block k + 2 is issued once block k is published.  Block
+      // k's O^T update runs in iteration k + 1, interleaved with block k + 1's softmax, so the
+      // slots hold: block k - 1 (its V^T being read), block k (S^T), blocks k + 1 and k + 2
+      // (in flight).
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (k < nblk) {
+          const Walk w = walk(k);
+          issue(k, octet_base(k, w));
+          okq |= halves_ok(w) << (2 * k);
+        }
+      // Publish block k: wait for this wave's octet, zero it if its table entry was out of
+      // range, barrier (every wave's octet of block k is in LDS and every wave is done with
+      // block k - 2, whose slot then receives block k + 2).  Returns block k's halves' state.
+      auto publish = [&](int k) -> uint32_t {
+        const bool nx = k + 2 < nblk;
+        const Walk nw = nx ? walk(k + 2) : Walk{{0, 0}};        // scalar table reads overlap the wait
+        const uint8_t* nbase = octet_base(k + 2, nw);
+        const uint32_t nok = nx ? halves_ok(nw) : 3u;
+        if (k + 1 < nblk)
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int sl = k % kWSlots;
+        const uint32_t hok = (okq >> (2 * sl)) & 3u;
+        if (((hok >> (wave >> 1)) & 1u) == 0) {
+          // out-of-range table entry: this octet read page 0; zero its rows (V enters the
+          // products; its scores are masked).  Flagged after the piece, outside the DMA waits.
+          bad_page = true;
+          LDS_AS uint8_t* st = lds + sl * kWBlockBytes;
+#pragma unroll
+          for (int cg = 0; cg < 9; ++cg)
+            *(LDS_AS u32x4_t*)(st + 4096 * cg + 1024 * wave + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (nx) {
+          issue(k + 2, nbase);
+          const int ns = (k + 2) % kWSlots;
+          okq = (okq & ~(3u << (2 * ns))) | (nok << (2 * ns));
+        }
+        return hok;
+      };
+      // S^T = K Q^T for block k: lane (i, h) gets row i, tokens 8jj + 4h + r as sa[4jj + r].
+      // The K operands stream through a ring of kWRing registers, each read issued kWRing
+      // MFMAs ahead of its use (the scheduling barriers keep the compiler from hoisting them
+      // all, which would push the query operands out of registers).  Tokens the rows must not
+      // see (past the piece or the causal limit, or in a dropped half) get the score that
+      // scales to -inf.
+      auto scores = [&](int k, uint32_t hok) -> f32x16_t {
+        LDS_AS const uint8_t* st = lds + (k % kWSlots) * kWBlockBytes;
+        f32x16_t sa;
+        auto kload = [&](int kk) -> bf16x8_t {
+          return __builtin_bit_cast(bf16x8_t, lds_ld128(st + (kb0 ^ (32 * (kk & 3))) + 4096 * (kk >> 2)));
+        };
+        // the rope k-steps (kk >= 32) take their query operand from LDS, two steps ahead
+        auto qload = [&](int kk) -> bf16x8_t { return __builtin_bit_cast(bf16x8_t, lds_ld128(qrope + 1024 * (kk - 32))); };
+        bf16x8_t kr[kWRing], qr[2];
+#pragma unroll
+        for (int j = 0; j < kWRing; ++j) kr[j] = kload(j);
+#pragma unroll
+        for (int kk = 0; kk < kKSteps * 2; ++kk) {
+          if (kk == 30 || kk == 31) qr[kk & 1] = qload(kk + 2);
+          const bf16x8_t qv = kk < 32 ? qf[kk & 31] : qr[kk & 1];
+          if (kk == 0)
+            mfma32_vfirst(sa, kr[0], qv);
+          else if (kk == kKSteps * 2 - 1)
+            mfma32_vlast(sa, kr[kk % kWRing], qv);
+          else
+            mfma32_vacc(sa, kr[kk % kWRing], qv);
+          if (kk + kWRing < kKSteps * 2) kr[kk % kWRing] = kload(kk + kWRing);
+          if (kk >= 32 && kk + 2 < kKSteps * 2) qr[kk & 1] = qload(kk + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const int tok0 = tb + kWBlock * k;
+        if (hok != 3u || tok0 + kWBlock > lim_min) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int t = tok0 + 8 * (q >> 2) + 4 * h + (q & 3);
+            if (!(t < lim && ((hok >> (q >> 3)) & 1u) != 0)) sa[q] = s_hide;   // position 8 (q / 4) + ..: half q / 8
+          }
+        }
+        return sa;
+      };
+      // softmax of one block's scores: p = exp2(s c - m_ref) (c = scale * log2 e), summed into
+      // lsum, returned as bf16 P^T operands for the two token halves u (K index 8h + 4jp + r is
+      // token 16u + 8jp + 4h + r, held in sa[8u + 4jp + r]); pl: the bf16 remainders (fp32 output)
+      auto softmax = [&](const f32x16_t& sa, bool first, u32x4_t (&ph)[2], u32x4_t (&pl)[2]) {
+        float sc[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) sc[q] = sa[q] * c_log2;
+        float mx = sc[0];
+#pragma unroll
+        for (int q = 1; q < 16; ++q) mx = fmaxf(mx, sc[q]);
+        {
+          const int xi = __float_as_int(mx);
+          const auto sw = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+          mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+        }
+        m_run = fmaxf(m_run, mx);
+        if (first) m_ref = fmaxf(mx, kNegBig);
+        ovf |= mx > m_ref + kWSlack;
+        float pv[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          pv[q] = __builtin_amdgcn_exp2f(sc[q] - m_ref);
+          lsum += pv[q];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float a0 = pv[8 * u + 2 * e2], a1 = pv[8 * u + 2 * e2 + 1];
+            ph[u][e2] = bf16x2_rne(a0, a1);
+            if constexpr (OUT_F32)
+              pl[u][e2] = bf16x2_rne(a0 - __uint_as_float(ph[u][e2] << 16), a1 - __uint_as_float(ph[u][e2] & 0xFFFF0000u));
+          }
+        }
+      };
+      // O^T += V^T P^T for block kp (P^T in php / plp), with the softmax of the next block's
+      // scores sa spread over its 32 steps (tile t = 16u + cc, u the token half).  V^T tiles
+      // stream through a ring of kWVRing operands; each step is one MFMA (two with fp32 output),
+      // the next tile's two transpose reads and a slice of the softmax, fenced so that the
+      // compiler keeps this order (the MFMAs then run under the softmax's vector work).
+      auto update = [&](int kp, const u32x4_t (&php)[2], const u32x4_t (&plp)[2], const f32x16_t& sa,
+                        u32x4_t (&ph)[2], u32x4_t (&pl)[2]) {
+        LDS_AS const uint8_t* st = lds + (kp % kWSlots) * kWBlockBytes;
+        auto vload = [&](int t) -> bf16x8_t {
+          const int u = t >> 4, cc = t & 15;
+          const int off = 4096 * (cc >> 1) + 2048 * u;
+          const u32x2_t v0 = lds_tr16(st + (vb[0] ^ (64 * (cc & 1))) + off);
+          const u32x2_t v1 = lds_tr16(st + (vb[1] ^ (64 * (cc & 1))) + off);
+          return __builtin_bit_cast(bf16x8_t, u32x4_t{v0[0], v0[1], v1[0], v1[1]});
+        };
+        bf16x8_t vr[kWVRing];
+#pragma unroll
+        for (int j = 0; j < kWVRing; ++j) vr[j] = vload(j);
+        float sc[16], mx = -INFINITY;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+          const int u = t >> 4, cc = t & 15;
+          const bf16x8_t vv = vr[t % kWVRing];
+          o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, __builtin_bit_cast(bf16x8_t, php[u]), o[cc], 0, 0, 0);
+          if constexpr (OUT_F32)
+            o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, __builtin_bit_cast(bf16x8_t, plp[u]), o[cc], 0, 0, 0);
+          if (t + kWVRing < 32) vr[t % kWVRing] = vload(t + kWVRing);
+          // the softmax slice of this step
+          if (t < 4) {
+#pragma unroll
+            for (int q = 4 * t; q < 4 * t + 4; ++q) {
+              sc[q] = sa[q] * c_log2;
+              mx = fmaxf(mx, sc[q]);
+            }
+          } else if (t == 4) {
+            const int xi = __float_as_int(mx);
+            const auto sw = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+            mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+            m_run = fmaxf(m_run, mx);
+            ovf |= mx > m_ref + kWSlack;
+          } else if (t < 21) {
+            const int q = t - 5;
+            sc[q] = __builtin_amdgcn_exp2f(sc[q] - m_ref);
+            lsum += sc[q];
+          } else if (t < 29) {
+            const int e = t - 21, uu = e >> 2, e2 = e & 3;      // pair e2 of half uu
+            const float a0 = sc[8 * uu + 2 * e2], a1 = sc[8 * uu + 2 * e2 + 1];
+            ph[uu][e2] = bf16x2_rne(a0, a1);
+            if constexpr (OUT_F32)
+              pl[uu][e2] = bf16x2_rne(a0 - __uint_as_float(ph[uu][e2] << 16), a1 - __uint_as_float(ph[uu][e2] & 0xFFFF0000u));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      u32x4_t ph_prev[2], pl_prev[2];
+      if (nblk > 0) {
+        const uint32_t hok = publish(0);
+        const f32x16_t sa = scores(0, hok);
+        softmax(sa, pass == 0, ph_prev, pl_prev);
+      }
+      for (int k = 1; k <= nblk; ++k) {
+        f32x16_t sa;
+        if (k < nblk) {
+          const uint32_t hok = publish(k);
+          sa = scores(k, hok);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) sa[q] = s_hide;       // past the last block: no weight
+        }
+        u32x4_t ph[2], pl[2];
+        update(k - 1, ph_prev, pl_prev, sa, ph, pl);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          ph_prev[u] = ph[u];
+          pl_prev[u] = pl[u];
+        }
+      }
+      // any wave whose scores left the slack: every wave runs the piece again (the slots are
+      // shared); the second pass starts from each row's true maximum and cannot overflow.  The
+      // waves' votes go through slot 0, free once every wave has passed this barrier.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (lane == 0) lds[wave] = __any(ovf) ? 1 : 0;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const uint32_t again = *(LDS_AS const uint32_t*)lds;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (again == 0 || pass > 0) break;
+    }
+    {
+        // ---- write: every wave holds its 32 rows complete
+        float l = lsum;
+        {
+          const int xi = __float_as_int(l);
+          const auto sw = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+          l = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+        }
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        // lane (i, h) holds columns 32cc + 8jj + 4h + 0..3 of row i as o[cc][4jj + 0..3]; the
+        // destination is the wave's first row (uniform) plus a 32-bit lane offset
+        if (slot < 0 && !OUT_F32) {
+          uint8_t* dst = (uint8_t*)((uint16_t*)a.out + ((int64_t)b * R + rbase) * kDv);
+          const uint32_t lo = (uint32_t)i * (2 * kDv) + 8u * h;
+#pragma unroll
+          for (int cc = 0; cc < 16; ++cc) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              *(u32x2_t*)(dst + lo + 64 * cc + 16 * jj) =
+                  u32x2_t{bf16x2_rne(o[cc][4 * jj] * inv, o[cc][4 * jj + 1] * inv),
+                          bf16x2_rne(o[cc][4 * jj + 2] * inv, o[cc][4 * jj + 3] * inv)};
+            __builtin_amdgcn_sched_barrier(0);   // one tile at a time out of the accumulators
+          }
+        } else {
+          uint8_t* dst = (uint8_t*)(slot < 0 ? (float*)a.out + ((int64_t)b * R + rbase) * kDv
+                                             : a.part_o + ((int64_t)slot * R + rbase) * kDv);
+          const uint32_t lo = (uint32_t)i * (4 * kDv) + 16u * h;
+#pragma unroll
+          for (int cc = 0; cc < 16; ++cc) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              *(f32x4_t*)(dst + lo + 128 * cc + 32 * jj) =
+                  f32x4_t{o[cc][4 * jj], o[cc][4 * jj + 1], o[cc][4 * jj + 2], o[cc][4 * jj + 3]} * inv;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (h == 0) {
+          const float lse = l > 0.f ? (m_ref + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
+          float* lbase = slot < 0 ? a.lse + ((int64_t)b * R + rbase) : a.part_lse + ((int64_t)slot * R + rbase);
+          if (slot >= 0 || a.lse) *(float*)((uint8_t*)lbase + 4u * (uint32_t)i) = lse;
+        }
+        if (bad_page && lane == 0)
+          __hip_atomic_fetch_or(a.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Log-sum-exp merge of one batch of partial results into a running (M, L, acc): with
 // M' = max(M, l_u), acc and L are scaled by e^(M - M') and each partial u adds
 // w_u = e^(l_u - M') times its o (and w_u to L).  Partials with l = -inf (no tokens) add
@@ -1398,6 +1872,19 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
       hipLaunchKernelGGL((group_decode_kernel<4, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((group_decode_kernel<4, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else if (rows_per_group == 128) {
+    const bool nt = a.row_groups == 1;
+    if (out_fp32) {
+      if (nt)
+        hipLaunchKernelGGL((wide_decode_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((wide_decode_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    } else {
+      if (nt)
+        hipLaunchKernelGGL((wide_decode_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((wide_decode_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+    }
   } else {
     return (int)hipErrorInvalidValue;
   }

@@ -54,6 +54,7 @@ def test_causal_edge_lengths(heads, q_len, out_fp32):
 
 
 @pytest.mark.parametrize("heads,q_len,rpg", [(16, 2, 32), (8, 4, 32), (16, 4, 64), (32, 2, 16), (16, 8, 16),
+                                          (64, 2, 128), (128, 2, 128), (32, 4, 128),
                                           (128, 2, 64)])
 @pytest.mark.parametrize("out_fp32", [True, False])
 def test_causal_rows_per_group(heads, q_len, rpg, out_fp32):

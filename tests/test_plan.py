@@ -66,7 +66,8 @@ def test_plan_covers_every_token_once(name):
         plan = make_plan(lens, heads=heads, q_len=q_len)
         seg, off, info = check_plan(plan, lens)
         R = heads * q_len
-        assert info["rows_per_group"] == (64 if R % 64 == 0 else 16)   # bf16 cache: 64 rows when they fit
+        # bf16 cache: 128 rows per work-group when they fit, else 64, else 16
+        assert info["rows_per_group"] == (128 if R % 128 == 0 else 64 if R % 64 == 0 else 16)
         assert info["row_groups"] == R // info["rows_per_group"]
         workers = 256 // info["row_groups"]
         assert info["num_workers"] <= max(1, workers)
@@ -120,7 +121,8 @@ def test_grid_padding_for_row_groups():
     assert info["grid_size"] == ((info["num_workers"] + 7) // 8 * 8) * 3
 
 
-@pytest.mark.parametrize("heads,q_len,rpg", [(32, 1, 32), (64, 1, 64), (16, 4, 64), (128, 1, 32)])
+@pytest.mark.parametrize("heads,q_len,rpg", [(32, 1, 32), (64, 1, 64), (16, 4, 64), (128, 1, 32), (128, 1, 64),
+                                          (128, 2, 128), (64, 2, 128)])
 def test_forced_rows_per_group(heads, q_len, rpg):
     lens = [5000, 300]
     maxp = max((l + 63) // 64 for l in lens)
@@ -140,12 +142,17 @@ def test_rows_per_group_rejected():
     with pytest.raises(B.MlaError) as ei:
         B.Plan(fp8, [10], num_cus=256, rows_per_group=64)       # the grouped kernel reads bf16 rows only
     assert ei.value.status == B.MLA_ERR_UNSUPPORTED
+    with pytest.raises(B.MlaError) as ei:
+        B.Plan(B.make_problem(1, 1, 64, 64, 1, 1), [10], num_cus=256, rows_per_group=128)   # R = 64
+    assert ei.value.status == B.MLA_ERR_UNSUPPORTED
 
 
 def test_default_rows_per_group():
-    """64 rows per work-group when R is a multiple of 64 and the cache is bf16, else 16."""
-    for heads, q_len, kv, want in [(16, 1, 0, 16), (16, 2, 0, 16), (48, 1, 0, 16), (64, 1, 0, 64), (128, 1, 0, 64),
-                                   (32, 2, 0, 64), (64, 1, 1, 16), (128, 1, 1, 16), (128, 2, 0, 64), (128, 2, 1, 16)]:
+    """With a bf16 cache: 128 rows per work-group when R is a multiple of 128, else 64 when R is a
+    multiple of 64, else 16; with FP8 rows, 16."""
+    for heads, q_len, kv, want in [(16, 1, 0, 16), (16, 2, 0, 16), (48, 1, 0, 16), (64, 1, 0, 64), (128, 1, 0, 128),
+                                   (32, 2, 0, 64), (64, 1, 1, 16), (128, 1, 1, 16), (128, 2, 0, 128), (128, 2, 1, 16),
+                                   (64, 2, 0, 128), (96, 2, 0, 64)]:
         prob = B.make_problem(1, q_len, heads, 64, 1, 1, kv_fp8=bool(kv))
         info = B.Plan(prob, [10], num_cus=256).info()
         assert info["rows_per_group"] == want, (heads, q_len, kv, info["rows_per_group"])
