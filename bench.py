@@ -1,23 +1,32 @@
 """Benchmark: paged MLA decode on one MI355X.
 
-Workload (default): long-context decode, batch 16, q_len 1, 16 heads, 65,536
-cached tokens per sequence in 64-token pages of 576 bf16 (512 latent + 64
-rope), random page table, N(0,1) values, scale 1/sqrt(192), bf16 out.
+Headline workload (default): long-context decode, batch 16, q_len 1, 16 heads, 65,536 cached
+tokens per sequence in 64-token pages of 576 bf16 (512 latent + 64 rope), random page table,
+N(0,1) values, scale 1/sqrt(192), bf16 out.
 
-A step is one mla_decode call (split-decode kernel + merge kernel) over inputs
-already resident in HBM.  Prints one JSON line:
-  value      = algorithmic bytes per call / wall time per call  (GB/s, whole job)
-  roofline   = the split-decode kernel alone: algorithmic bytes / its mean
-               duration (HIP events on the launch stream) vs 8 TB/s HBM, and vs
-               a 1 GiB device-to-device copy timed on the same box
-  timing_us  = per-call event percentiles, the cache-flushed per-call time, the
-               device-scheduled entry point (mla_decode_devplan) on the same inputs
-  compute    = the call's matrix work as TFLOP/s (kernel and whole call), and for
-               the long workload the pages' H20 figure at that shape (context only)
-  cpu_baseline = the fp64 oracle on a bounded sample of the same workload, on
-               this host's cores (context only)
+A step is one mla_decode call (split-decode kernel + merge kernel) over inputs already resident
+in HBM.  Prints one JSON line:
+  value        = algorithmic bytes per call / wall time per call (GB/s, whole job)
+  roofline     = the split-decode kernel alone: algorithmic bytes / its mean duration (HIP events
+                 on the launch stream) against 8 TB/s, beside a read-only probe that streams the
+                 same number of bytes into LDS with the decode's own non-temporal loads
+                 (mla_stream_probe) on the same box
+  timing_us    = per-call event percentiles, the cache-flushed per-call time, the device-scheduled
+                 entry point (mla_decode_devplan) on the same inputs
+  configs      = every workload (tiny, paged, two_token, long, ragged) with bf16 and with FP8 cache
+                 rows: call and kernel time, flushed call time, GB/s and fraction of 8 TB/s
+  compute      = the call's matrix work as TFLOP/s, and for the long workload the pages' H20 figure
+                 at that shape (context only)
+  cpu_baseline = the fp64 oracle on a bounded sample of the headline workload, on this host's
+                 cores (context only)
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long]
+Inputs: lengths and page tables follow the recipe (inputs.config_layout, the seeded numpy draws);
+the cache and query values are N(0,1) drawn on the GPU with torch's generator seeded with the
+workload's seed and rounded to bf16 (FP8 rows: E4M3 codes of x / 2^e per 128-column group, as in
+the recipe).  Same shapes, lengths, page tables and value distribution as the recipe, drawn in
+seconds instead of minutes; the parity tests use the recipe's own numpy values.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long] [--kv bf16|fp8]
 """
 from __future__ import annotations
 
@@ -26,6 +35,7 @@ import json
 import os
 import sys
 import time
+from types import SimpleNamespace
 
 import numpy as np
 
@@ -34,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+HEADLINE_METRIC = "µs/call and achieved HBM GB/s (% of peak), MLA decode bs=16 H=16 ctx=64K"
 
 WORKLOAD_TEXT = {
     "tiny": "MLA decode: batch 1, q_len 1, 16 heads, one contiguous 1024-token page, fp32 out",
@@ -42,6 +53,9 @@ WORKLOAD_TEXT = {
     "long": "long-context paged MLA decode: batch 16, q_len 1, 16 heads, 65536 tokens each, page 64, bf16 out",
     "ragged": "ragged paged MLA decode: batch 64, q_len 1, 128 heads, lengths U[1024, 65536], page 64, bf16 out",
 }
+KERNEL_NAME = {16: "split_decode_kernel", 32: "group_decode_kernel", 64: "group_decode_kernel",
+               128: "wide_decode_kernel"}
+FLUSH_BYTES = 512 << 20          # read between calls: more than the 256 MB last-level cache
 
 
 def algorithmic_bytes(prob) -> int:
@@ -56,51 +70,179 @@ def algorithmic_bytes(prob) -> int:
                + prob.batch * R * 4 + pages * 4)
 
 
-def measured_traffic(config: str):
-    """HBM bytes per split-decode launch from the committed counter summary, or None when
-    the summary is missing, for another workload, or older than the kernel sources."""
+def flops(prob) -> float:
+    """Matrix work of a call: 2 flops per multiply-add, 576 for S^T and 512 for O^T per cached
+    token and query row."""
+    return float(np.sum(prob.cache_seqlens)) * prob.q_len * prob.num_heads * 2 * (576 + 512)
+
+
+def device_problem(name: str, kv: str, seed=None, device="cuda"):
+    """The named workload with its recipe's lengths and page table and N(0,1) values drawn on the
+    GPU (see the module docstring).  Returns (problem description, device tensors)."""
+    import torch
+    from mla_decode_attention_paged_amd import inputs as gen
+    lengths, block_table, num_pages, cfg, seed = gen.config_layout(name, seed)
+    B, S, H, P = cfg["batch"], cfg["q_len"], cfg["num_heads"], cfg["page_size"]
+    g = torch.Generator(device=device)
+    g.manual_seed(1000003 * seed + (1 if kv == "fp8" else 0))
+    rows = num_pages * P
+    chunk = 1 << 20
+    if kv == "bf16":
+        kvt = torch.empty((rows, 576), dtype=torch.bfloat16, device=device)
+        for s0 in range(0, rows, chunk):
+            e0 = min(rows, s0 + chunk)
+            kvt[s0:e0] = torch.randn((e0 - s0, 576), generator=g, device=device).to(torch.bfloat16)
+        kvt = kvt.view(num_pages, P, 576)
+    else:
+        kvt = torch.empty((rows, 656), dtype=torch.uint8, device=device)
+        for s0 in range(0, rows, chunk):
+            e0 = min(rows, s0 + chunk)
+            n = e0 - s0
+            x = torch.randn((n, 4, 128), generator=g, device=device)
+            amax = x.abs().amax(dim=2).clamp_min(2.0 ** -100)
+            scale = torch.exp2(torch.ceil(torch.log2(amax.double() / 448.0))).float()
+            kvt[s0:e0, :512] = (x / scale[:, :, None]).to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, 512)
+            kvt[s0:e0, 640:656] = scale.contiguous().view(torch.uint8).reshape(n, 16)
+            rope = torch.randn((n, 64), generator=g, device=device).to(torch.bfloat16)
+            kvt[s0:e0, 512:640] = rope.view(torch.uint8).reshape(n, 128)
+        kvt = kvt.view(num_pages, P, 656)
+    q = torch.randn((B, S, H, 576), generator=g, device=device).to(torch.bfloat16)
+    dev = {"q": q, "kv_cache": kvt, "block_table": torch.from_numpy(block_table).to(device),
+           "cache_seqlens": torch.from_numpy(lengths).to(device)}
+    prob = SimpleNamespace(name=name, batch=B, q_len=S, num_heads=H, page_size=P, num_pages=num_pages,
+                           max_pages_per_seq=int(block_table.shape[1]), out_fp32=bool(cfg.get("out_fp32", False)),
+                           kv_format=kv, cache_seqlens=lengths, block_table=block_table,
+                           softmax_scale=gen.SOFTMAX_SCALE, seed=seed)
+    return prob, dev
+
+
+def measured_traffic(key: str):
+    """HBM bytes per split-decode launch from the committed counter summary, or None when the
+    summary is missing, for another workload, or older than the kernel sources."""
     try:
         with open(PROFILE_COUNTERS) as fh:
             c = json.load(fh)
     except (OSError, ValueError):
         return None
     from mla_decode_attention_paged_amd.profiling import kernel_source_hash
-    entry = c.get(config)
+    entry = c.get(key)
     if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
 
 
-def compute_context(prob, kernel_us: float, call_s: float, config: str):
-    """Matrix work of the call (2 flops per multiply-add: 576 for S^T and 512 for O^T per
-    cached token and query row) as a rate, and, for the long workload, the pages' figure at
-    the same shape on other hardware (context only: another GPU, another flop count may be
-    meant)."""
-    R = prob.q_len * prob.num_heads
-    flops = float(np.sum(prob.cache_seqlens)) * R * 2 * (576 + 512)
-    out = {"flops_per_call": flops,
-           "kernel_tflops": round(flops / (kernel_us * 1e-6) / 1e12, 1),
-           "call_tflops": round(flops / call_s / 1e12, 1)}
-    if config == "long":
-        out["pages_figure"] = ("FlashMLA-ETAP 89 TFLOP/s against FlashMLA 32 TFLOP/s (2.78x) at 64K tokens, "
-                               "batch 16, on an NVIDIA H20 ([ETAP] 'Experimental results'); not comparable")
-    return out
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def cpu_baseline(prob, budget_s: float = 15.0):
-    """Time the oracle on whole sequences of the workload until about budget_s seconds."""
+def time_runner(r, stream, steps: int, flush=None, flushed_calls: int = 10):
+    """(mean us per call back-to-back, mean us of the split kernel alone, p50 us per call after
+    reading `flush` between calls)."""
+    import torch
+    from mla_decode_attention_paged_amd import binding as B
+    e0, e1 = _events()
+    e0.record(stream)
+    for _ in range(steps):
+        r()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call = e0.elapsed_time(e1) * 1e3 / steps
+    e0, e1 = _events()
+    e0.record(stream)
+    for _ in range(steps):
+        r(stages=B.MLA_STAGE_SPLIT)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern = e0.elapsed_time(e1) * 1e3 / steps
+    fl = []
+    if flush is not None:
+        for _ in range(flushed_calls):
+            flush.sum()
+            a, b = _events()
+            a.record(stream)
+            r()
+            b.record(stream)
+            torch.cuda.synchronize()
+            fl.append(a.elapsed_time(b) * 1e3)
+    return call, kern, (float(np.median(fl)) if fl else None)
+
+
+def config_table(stream, flush, steps: int = 20):
+    """Every workload with bf16 and FP8 cache rows."""
+    import torch
+    from mla_decode_attention_paged_amd.device import Runner
+    from mla_decode_attention_paged_amd import inputs as gen
+    table = {}
+    for name in gen.CONFIG_ORDER:
+        for kv in ("bf16", "fp8"):
+            print(f"[bench] config {name} {kv}", file=sys.stderr, flush=True)
+            prob, dev = device_problem(name, kv)
+            r = Runner(prob, dev=dev)
+            info = r.plan.info()
+            for _ in range(30):
+                r()
+            call, kern, flushed = time_runner(r, stream, steps, flush)
+            algo = algorithmic_bytes(prob)
+            entry = {
+                "us_per_call": round(call, 2), "kernel_us": round(kern, 2), "call_flushed_us": round(flushed, 2),
+                "algorithmic_bytes": algo,
+                "GBps_kernel": round(algo / (kern * 1e-6) / 1e9, 1),
+                "GBps_call_flushed": round(algo / (flushed * 1e-6) / 1e9, 1),
+                "frac_kernel": round(algo / (kern * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "frac_call_flushed": round(algo / (flushed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "kernel_tflops": round(flops(prob) / (kern * 1e-6) / 1e12, 1),
+                "kernel": KERNEL_NAME[info["rows_per_group"]], "rows_per_group": info["rows_per_group"],
+                "row_groups": info["row_groups"], "pieces": info["num_segments"], "partials": info["num_partials"],
+            }
+            traffic = measured_traffic(name if kv == "bf16" else f"{name}_fp8")
+            entry["traffic"] = traffic
+            table[f"{name}_{kv}"] = entry
+            del r, dev
+            torch.cuda.empty_cache()
+    return table
+
+
+def read_probe(stream, nbytes: int, grid: int, reps: int = 10):
+    """Best-of-reps GB/s of mla_stream_probe over a buffer of nbytes on `grid` work-groups."""
+    import torch
+    from mla_decode_attention_paged_amd import binding as B
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    B.mla_stream_probe(buf, grid)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        a, b = _events()
+        a.record(stream)
+        B.mla_stream_probe(buf, grid)
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3
+        best = t if best is None else min(best, t)
+    unit = 73728 * grid
+    moved = nbytes // unit * unit
+    del buf
+    return moved / best / 1e9
+
+
+def cpu_baseline(prob, dev, budget_s: float = 15.0):
+    """Time the oracle on whole sequences of the workload (copied to the host) until about
+    budget_s seconds."""
     from oracle import mla_oracle as orc
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    order = list(range(prob.batch))
-    done, t_total, tokens, rows_bytes = [], 0.0, 0, 0
-    for b in order:
+    q = dev["q"].view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    kv = dev["kv_cache"]
+    kv_host = (kv.cpu().numpy() if prob.kv_format == "fp8"
+               else kv.view(__import__("torch").int16).cpu().numpy().view(np.uint16))
+    done, t_total, tokens = [], 0.0, 0
+    for b in range(prob.batch):
         t0 = time.perf_counter()
-        orc.decode_sequence(prob.q[b], prob.kv_cache, prob.block_table[b], int(prob.cache_seqlens[b]),
-                            prob.softmax_scale, prob.page_size)
+        orc.decode_sequence(q[b], kv_host, prob.block_table[b], int(prob.cache_seqlens[b]), prob.softmax_scale,
+                            prob.page_size)
         t_total += time.perf_counter() - t0
         done.append(b)
         tokens += int(prob.cache_seqlens[b])
@@ -177,7 +319,7 @@ def layer_leg(prob, r, reps: int = 20):
         torch.cuda.synchronize()
         times = []
         for _ in range(5):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = _events()
             a.record(stream)
             g.replay()
             b.record(stream)
@@ -186,12 +328,11 @@ def layer_leg(prob, r, reps: int = 20):
         res[name] = float(np.median(times))
         del g
     nb = layer_bytes(prob)
-    out = {"us": {k: round(v, 2) for k, v in res.items()},
-           "algorithmic_bytes": nb,
-           "GBps": {k: round(nb[k] / (res[k] * 1e-6) / 1e9, 1) for k in nb},
-           "note": "graph-replayed means over back-to-back launches; the layer step is append + query "
-                   "preparation + decode + output projection"}
-    return out
+    return {"us": {k: round(v, 2) for k, v in res.items()},
+            "algorithmic_bytes": nb,
+            "GBps": {k: round(nb[k] / (res[k] * 1e-6) / 1e9, 1) for k in nb},
+            "note": "graph-replayed means over back-to-back launches; the layer step is append + query "
+                    "preparation + decode + output projection"}
 
 
 def main():
@@ -204,6 +345,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-layer", action="store_true", help="skip timing the steps around the decode")
+    ap.add_argument("--no-configs", action="store_true", help="skip the table of every workload")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="cache row storage: bf16 (1,152 B per token) or fp8 E4M3 rows (656 B per token)")
     args = ap.parse_args()
@@ -215,22 +357,22 @@ def main():
 
     import torch
     from mla_decode_attention_paged_amd import binding as B
-    from mla_decode_attention_paged_amd import inputs as gen
-    from mla_decode_attention_paged_amd.device import Runner
+    from mla_decode_attention_paged_amd.device import DevplanRunner, Runner, problem_struct
+    from mla_decode_attention_paged_amd.profiling import kernel_source_hash
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()  # fail loudly if the HIP library is missing
-    print(f"[bench] generating {args.config} inputs", file=sys.stderr, flush=True)
-    prob = gen.make_config(args.config, seed=args.seed, kv_format=args.kv)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"[bench] generating {args.config} inputs ({args.kv} cache) on the GPU", file=sys.stderr, flush=True)
+    prob, dev = device_problem(args.config, args.kv, args.seed)
     algo = algorithmic_bytes(prob)
     counters_key = args.config if args.kv == "bf16" else f"{args.config}_{args.kv}"
 
     t0 = time.perf_counter()
-    plan_probe = B.Plan(__import__("mla_decode_attention_paged_amd.device", fromlist=["x"]).problem_struct(prob),
-                        prob.cache_seqlens)
+    plan_probe = B.Plan(problem_struct(prob), prob.cache_seqlens)
     plan_us = (time.perf_counter() - t0) * 1e6
     del plan_probe
-    r = Runner(prob)
+    r = Runner(prob, dev=dev)
     stream = torch.cuda.current_stream()
     info = r.plan.info()
 
@@ -247,46 +389,24 @@ def main():
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
 
-    # per-call event timing (same stream), and the split-decode kernel alone
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # per-call event timing (same stream), the split-decode kernel alone, and flushed calls
+    ev = [_events() for _ in range(args.steps)]
     for a, b in ev:
         a.record(stream)
         r()
         b.record(stream)
     torch.cuda.synchronize()
     call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        r(stages=B.MLA_STAGE_SPLIT)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    split_us = e0.elapsed_time(e1) * 1e3 / args.steps
-
-    # flushed per-call time: reading 512 MB between calls evicts the 256 MB last-level cache
-    # (a read, so no dirty lines are left to be written back during the timed call)
-    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-    fl = []
-    for _ in range(min(args.steps, 20)):
-        flush.sum()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        r()
-        b.record(stream)
-        torch.cuda.synchronize()
-        fl.append(a.elapsed_time(b) * 1e3)
-    del flush
-
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    _, split_us, flushed_us = time_runner(r, stream, args.steps, flush, min(args.steps, 20))
     status = B.mla_read_status(r.ws)
 
-    # the same workload through the device-scheduled entry point (no host plan); FP8 and
-    # every R run there on the 16-row kernel
-    from mla_decode_attention_paged_amd.device import DevplanRunner
+    # the same workload through the device-scheduled entry point (no host plan)
     dr = DevplanRunner(prob, dev=r.dev)
     for _ in range(10):
         dr()
     torch.cuda.synchronize()
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0, d1 = _events()
     d0.record(stream)
     for _ in range(args.steps):
         dr()
@@ -295,31 +415,34 @@ def main():
     devplan_us = d0.elapsed_time(d1) * 1e3 / args.steps
     del dr
 
-    # read-bandwidth reference on this machine: a 1 GiB device-to-device copy (reads 1 GiB,
-    # writes 1 GiB), best of 10
-    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    cps = []
-    for _ in range(10):
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        dst.copy_(src)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        cps.append(c0.elapsed_time(c1) * 1e-3)
-    copy_gbs = 2 * src.numel() * 4 / min(cps) / 1e9
-    del src, dst
+    # read ceiling: the decode's KV bytes streamed into LDS by the same loads, same grid size
+    print("[bench] read probe", file=sys.stderr, flush=True)
+    kv_bytes = int(np.sum(prob.cache_seqlens)) * (656 if args.kv == "fp8" else 1152)
+    probe_gbs = read_probe(stream, max(kv_bytes, 73728 * cus), cus)
 
     layer = None
     if not args.no_layer:
         print("[bench] timing the steps around the decode", file=sys.stderr, flush=True)
         layer = layer_leg(prob, r)
+
+    table = None
+    if not args.no_configs:
+        table = config_table(stream, flush)
+    del flush
+
     value = algo / wall / 1e9
     achieved = algo / (split_us * 1e-6) / 1e9
     traffic = measured_traffic(counters_key)
+    fl = flops(prob)
+    compute = {"flops_per_call": fl, "kernel_tflops": round(fl / (split_us * 1e-6) / 1e12, 1),
+               "call_tflops": round(fl / wall / 1e12, 1)}
+    if args.config == "long":
+        compute["pages_figure"] = ("FlashMLA-ETAP 89 TFLOP/s against FlashMLA 32 TFLOP/s (2.78x) at 64K tokens, "
+                                   "batch 16, on an NVIDIA H20 ([ETAP] 'Experimental results'); not comparable")
+    metric = HEADLINE_METRIC if args.config == "long" else \
+        f"µs/call and achieved HBM GB/s (% of peak), {WORKLOAD_TEXT[args.config]}"
     result = {
-        "metric": "µs/call and achieved HBM GB/s (% of peak), MLA decode bs=16 H=16 ctx=64K",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -338,30 +461,34 @@ def main():
                    "name": args.config, "kv": args.kv, "batch": prob.batch,
                    "q_len": prob.q_len, "heads": prob.num_heads, "page_size": prob.page_size,
                    "ctx_tokens_total": int(prob.cache_seqlens.sum()), "seed": prob.seed,
-                   "parallelism": "single GPU, split-KV over 256 CUs"},
+                   "parallelism": f"single GPU, split-KV over {cus} CUs",
+                   "arithmetic": "bf16 matrix products with fp32 accumulation (FP8 rows widened to bf16 exactly)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "split_decode_kernel" if info["rows_per_group"] == 16 else "group_decode_kernel",
+                     "kernel": KERNEL_NAME[info["rows_per_group"]],
                      "kernel_us": round(split_us, 2),
                      "algorithmic_bytes_per_launch": algo,
-                     "copy_probe_GBps": round(copy_gbs, 1),
-                     "frac_of_copy_probe": round(achieved / copy_gbs, 4)},
+                     "read_probe_GBps": round(probe_gbs, 1),
+                     "frac_of_read_probe": round(achieved / probe_gbs, 4)},
         "timing_us": {"call_event_p10": round(float(np.percentile(call_us, 10)), 2),
                       "call_event_p50": round(float(np.percentile(call_us, 50)), 2),
                       "call_event_p90": round(float(np.percentile(call_us, 90)), 2),
-                      "call_flushed_p50": round(float(np.median(fl)), 2),
+                      "call_flushed_p50": round(flushed_us, 2),
                       "split_kernel_mean": round(split_us, 2),
                       "merge_and_gap_p50": round(float(np.percentile(call_us, 50)) - split_us, 2),
                       "plan_host_us": round(plan_us, 1),
                       "devplan_call_mean": round(devplan_us, 2)},
-        "plan": {k: info[k] for k in ("num_workers", "grid_size", "num_segments", "num_partials", "num_combine")},
+        "plan": {k: info[k] for k in ("num_workers", "grid_size", "num_segments", "num_partials", "num_combine",
+                                      "rows_per_group", "row_groups")},
         "status_word": status,
-        "compute": compute_context(prob, split_us, wall, args.config),
+        "kernel_source_hash": kernel_source_hash(),
+        "compute": compute,
+        "configs": table,
         "layer_steps": layer,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(prob, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(prob, r.dev, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

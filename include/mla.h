@@ -321,6 +321,12 @@ mla_status_t mla_out_absorb(const mla_problem_t* problem, const void* out_latent
  * Bit 1 is not used here (mla_kv_append's own status word uses it). */
 mla_status_t mla_read_status(const void* workspace, void* stream, int32_t* status_out);
 
+/* Measurement aid (this library's): read the first num_workgroups * floor(bytes / num_workgroups
+ * / 73,728) * 73,728 bytes of `buffer` (device, 1 KiB aligned) into LDS with the decode's own
+ * non-temporal 16-byte global->LDS loads, each work-group its contiguous share, computing nothing:
+ * the read ceiling the decode's KV stream is compared with.  Async on `stream`. */
+mla_status_t mla_stream_probe(const void* buffer, size_t bytes, int32_t num_workgroups, void* stream);
+
 void mla_plan_destroy(mla_plan_t plan);            /* NULL is a no-op */
 const char* mla_status_string(mla_status_t status); /* static string */
 const char* mla_last_error(void);                  /* thread-local detail of the last failure */

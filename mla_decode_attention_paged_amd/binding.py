@@ -72,6 +72,7 @@ _SIGS = {
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p, C.c_uint32]),
     "mla_debug_gather": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "mla_read_status": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(C.c_int32)]),
+    "mla_stream_probe": (C.c_int, [C.c_void_p, C.c_size_t, C.c_int32, C.c_void_p]),
     "mla_devplan_workspace_bytes": (C.c_size_t, [C.POINTER(mla_problem_t), C.c_int32]),
     "mla_devplan_prepare": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "mla_decode_devplan": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -345,6 +346,12 @@ def mla_decode_devplan_noalloc(problem: mla_problem_t, num_workers, q, kv_cache,
     _check(lib().mla_decode_devplan_noalloc(C.byref(p), num_workers, _ptr(q), _ptr(kv_cache), _ptr(block_table),
                                             _ptr(cache_seqlens), C.c_float(float(softmax_scale)), _ptr(out),
                                             _ptr(lse), _stream(stream)), "mla_decode_devplan_noalloc")
+
+
+def mla_stream_probe(buffer, num_workgroups, stream=None):
+    """Read `buffer` (a CUDA uint8 tensor) into LDS the way the decode reads its KV rows."""
+    _check(lib().mla_stream_probe(_ptr(buffer), _nbytes(buffer), int(num_workgroups), _stream(stream)),
+           "mla_stream_probe")
 
 
 def mla_read_status(workspace, stream=None) -> int:

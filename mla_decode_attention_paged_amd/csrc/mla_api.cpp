@@ -471,6 +471,18 @@ mla_status_t mla_decode_devplan_noalloc(const mla_problem_t* problem, int32_t nu
                             ws, MLA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+mla_status_t mla_stream_probe(const void* buffer, size_t bytes, int32_t num_workgroups, void* stream) {
+  if (!buffer) return fail(MLA_ERR_INVALID_ARGUMENT, "buffer is NULL");
+  if ((uintptr_t)buffer % 1024) return fail(MLA_ERR_INVALID_ARGUMENT, "buffer must be 1 KiB aligned");
+  if (num_workgroups < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "num_workgroups must be >= 1");
+  const int64_t per_wg = (int64_t)(bytes / (size_t)num_workgroups) / mla::kProbeUnit * mla::kProbeUnit;
+  if (per_wg == 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "bytes must cover at least %lld per work-group", (long long)mla::kProbeUnit);
+  const int e = mla::launch_stream_probe(buffer, per_wg, num_workgroups, stream);
+  if (e) return fail(MLA_ERR_HIP, "stream probe launch: %s", mla::hip_error_string(e));
+  return MLA_OK;
+}
+
 mla_status_t mla_read_status(const void* workspace, void* stream, int32_t* status_out) {
   if (!workspace || !status_out) return fail(MLA_ERR_INVALID_ARGUMENT, "workspace or status_out is NULL");
   int32_t v = 0;

@@ -156,6 +156,8 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
 int launch_merge_dev(const MergeArgs& a, bool out_fp32, void* stream);
 int launch_fill_zero(void* p, size_t bytes, void* stream);   // bytes: a multiple of 4
 int launch_merge(const MergeArgs& a, bool out_fp32, void* stream);
+int launch_stream_probe(const void* buf, int64_t per_wg, int grid, void* stream);
+constexpr int64_t kProbeUnit = (int64_t)kWaves * kBlock * kDqk * 2;   // 73,728: one 18 KB block per wave
 int launch_gather(const void* kv, const int32_t* block_table, void* rows_out, int32_t seq, int32_t length,
                   int64_t row_offset, int32_t page_size, int32_t bt_stride, int32_t num_pages, int32_t row_bytes,
                   void* stream);

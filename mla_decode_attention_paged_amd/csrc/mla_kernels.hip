@@ -1836,6 +1836,36 @@ void launch_split(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
   }
 }
 
+// Read ceiling of the decode's KV stream: every work-group moves its contiguous share of `buf`
+// into LDS with the same non-temporal 16-B global->LDS loads as the decode (each wave 18 KB blocks
+// through two stages, blocks w, w + 4, ... of its work-group's share) and computes nothing.
+constexpr int kProbeBlock = kBlockBytes;                 // 18,432 bytes, 18 loads of 1 KB
+__global__ void __launch_bounds__(kThreads) stream_probe_kernel(const uint8_t* buf, int64_t per_wg) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kWaves * 2 * kProbeBlock];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint8_t* base = buf + (int64_t)blockIdx.x * per_wg;
+  const int64_t nblk = per_wg / kProbeBlock;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem + (uint32_t)(wave * 2 * kProbeBlock);
+  const uint32_t voff = 16u * (uint32_t)lane;
+  int64_t k = 0;
+  for (int64_t j = wave; j < nblk; j += kWaves, ++k) {
+    const uint8_t* src = base + j * kProbeBlock;
+    const uint32_t stage = lds0 + (uint32_t)((k & 1) * kProbeBlock);
+#pragma unroll
+    for (int i = 0; i < kProbeBlock / 1024; ++i) {
+      uint32_t sv;
+      asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3 nt\n\ts_mov_b32 m0, %0"
+                   : "=&s"(sv)
+                   : "s"(__builtin_amdgcn_readfirstlane(stage + 1024u * i)), "v"(voff), "s"(src + 1024 * i)
+                   : "memory");
+    }
+    // the previous block has landed (18 loads per block; at most one block in flight behind)
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __global__ void __launch_bounds__(256) fill_zero_kernel(uint32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -1888,6 +1918,12 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
   } else {
     return (int)hipErrorInvalidValue;
   }
+  return (int)hipGetLastError();
+}
+
+int launch_stream_probe(const void* buf, int64_t per_wg, int grid, void* stream) {
+  hipLaunchKernelGGL(stream_probe_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, (const uint8_t*)buf,
+                     per_wg);
   return (int)hipGetLastError();
 }
 

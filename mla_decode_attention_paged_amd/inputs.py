@@ -132,6 +132,39 @@ def _fp8_rows(rng: np.random.Generator, n: int) -> np.ndarray:
     return rows
 
 
+def draw_layout(rng: np.random.Generator, batch: int, page_size: int, lengths=None, ragged_range=None,
+                extra_pages: int = 0, identity_pages: bool = False):
+    """Steps 1 and 2 of the draw order: the context lengths (drawn only when not given) and the
+    page table.  Returns (lengths int32 [B], block_table int32 [B, max_pages], num_pages)."""
+    if lengths is None:
+        lo, hi = ragged_range
+        lengths = rng.integers(lo, hi, endpoint=True, size=batch)
+    lengths = np.broadcast_to(np.asarray(lengths, dtype=np.int64), (batch,)).astype(np.int32)
+    pages_per = [(int(L) + page_size - 1) // page_size for L in lengths]
+    used = int(sum(pages_per))
+    num_pages = used + int(extra_pages)
+    max_pages = max(1, max(pages_per) if pages_per else 1)
+    perm = np.arange(num_pages) if identity_pages else rng.permutation(num_pages)
+    block_table = np.full((batch, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages_per):
+        block_table[b, :n] = perm[off:off + n]
+        off += n
+    return lengths, block_table, num_pages
+
+
+def config_layout(name: str, seed=None):
+    """The named workload's lengths and page table (its recipe's steps 1 and 2) and its shape:
+    (lengths, block_table, num_pages, dict of the config's other fields, seed)."""
+    cfg = dict(CONFIGS[name])
+    if seed is None:
+        seed = CONFIG_ORDER.index(name)
+    rng = np.random.default_rng(seed)
+    lengths, block_table, num_pages = draw_layout(rng, cfg["batch"], cfg["page_size"], cfg.get("lengths"),
+                                                  cfg.get("ragged_range"))
+    return lengths, block_table, num_pages, cfg, seed
+
+
 def make_problem(batch: int, q_len: int, num_heads: int, page_size: int,
                  lengths=None, *, seed: int = 0, ragged_range=None,
                  out_fp32: bool = False, tail: str = "normal",
@@ -147,20 +180,8 @@ def make_problem(batch: int, q_len: int, num_heads: int, page_size: int,
     identity_pages -- block_table maps pages in order (no permutation draw).
     """
     rng = np.random.default_rng(seed)
-    if lengths is None:
-        lo, hi = ragged_range
-        lengths = rng.integers(lo, hi, endpoint=True, size=batch)
-    lengths = np.broadcast_to(np.asarray(lengths, dtype=np.int64), (batch,)).astype(np.int32)
-    pages_per = [(int(L) + page_size - 1) // page_size for L in lengths]
-    used = int(sum(pages_per))
-    num_pages = used + int(extra_pages)
-    max_pages = max(1, max(pages_per) if pages_per else 1)
-    perm = np.arange(num_pages) if identity_pages else rng.permutation(num_pages)
-    block_table = np.full((batch, max_pages), -1, dtype=np.int32)
-    off = 0
-    for b, n in enumerate(pages_per):
-        block_table[b, :n] = perm[off:off + n]
-        off += n
+    lengths, block_table, num_pages = draw_layout(rng, batch, page_size, lengths, ragged_range, extra_pages,
+                                                  identity_pages)
     if kv_format == "bf16":
         kv = _normal_bf16(rng, num_pages * page_size * D_QK).reshape(num_pages, page_size, D_QK)
     elif kv_format == "fp8":

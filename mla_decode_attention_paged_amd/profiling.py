@@ -69,7 +69,8 @@ def stats(d, out_md, command):
             agg.setdefault(name, []).append(dur / 1e3)
         con.close()
     total = sum(sum(v) for v in agg.values())
-    lines = ["# rocprofv3 kernel statistics", "", "Command (run from /tmp with TMPDIR=/tmp):", "", "```", command,
+    lines = ["# rocprofv3 kernel statistics", "", f"Kernel source hash: {kernel_source_hash()}", "",
+             "Command (run from /tmp with TMPDIR=/tmp):", "", "```", command,
              "```", "", "| kernel | calls | avg us | min us | max us | total us | % of GPU time |",
              "|---|---|---|---|---|---|---|"]
     for name, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
@@ -157,7 +158,8 @@ def sq(kernel, blocks, out_md, commands, *dirs):
         raise SystemExit(f"no SQ counters for {kernel}")
     mean = {c: sums[c] / len(disp[c]) for c in sums}
     blocks = int(blocks)
-    lines = [f"# SQ counters of `{kernel}`", "", "Commands (run from /tmp with TMPDIR=/tmp):", "", "```", commands, "```",
+    lines = [f"# SQ counters of `{kernel}`", "", f"Kernel source hash: {kernel_source_hash()}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp):", "", "```", commands, "```",
              "", "| counter | mean per dispatch | per block |", "|---|---|---|"]
     for c in sorted(mean):
         per = f"{mean[c] / blocks:.1f}" if blocks > 0 else ""

@@ -29,6 +29,7 @@ int launch_kv_append(const LayerArgs&, void*) { no_kernels("kv_append"); }
 int launch_out_absorb(const LayerArgs&, bool, bool, void*) { no_kernels("out_absorb"); }
 const char* hip_error_string(int) { return "no kernels in the host check"; }
 int noalloc_scratch(void**) { no_kernels("noalloc_scratch"); }
+int launch_stream_probe(const void*, int64_t, int, void*) { no_kernels("stream_probe"); }
 }  // namespace mla
 
 #define CHECK(c)                                                              \
@@ -202,6 +203,9 @@ static bool validation_paths() {
         MLA_ERR_INVALID_ARGUMENT);
   CHECK(mla_out_absorb(&p, fake + 8, fake, fake, nullptr) == MLA_ERR_INVALID_ARGUMENT);
   for (int s = -1; s < 8; ++s) CHECK(mla_status_string((mla_status_t)s) != nullptr);
+  CHECK(mla_stream_probe(nullptr, 1 << 20, 256, nullptr) == MLA_ERR_INVALID_ARGUMENT);
+  CHECK(mla_stream_probe(fake + 16, 1 << 30, 256, nullptr) == MLA_ERR_INVALID_ARGUMENT);
+  CHECK(mla_stream_probe(fake, 1000, 256, nullptr) == MLA_ERR_INVALID_ARGUMENT);
   return true;
 }
 
