@@ -1267,6 +1267,77 @@ __device__ __forceinline__ void dma_wide_octet(const uint8_t* base, uint32_t vof
 #undef MLA_W1
 }
 
+// One global->LDS load of 1 KB: 16 B per lane from base + voff + OFF into LDS at m0 + OFF + 16 lane
+// (the instruction offset applies to both addresses).  Saves and restores M0; hidden from the
+// compiler's counters.
+template <bool NT, int OFF>
+__device__ __forceinline__ void dma_one(const uint8_t* base, uint32_t voff, uint32_t m0) {
+  uint32_t sv;
+  if constexpr (NT)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3 offset:%4 nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(sv)
+                 : "v"(voff), "s"(m0), "s"(base), "n"(OFF)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3 offset:%4\n\ts_mov_b32 m0, %0"
+                 : "=&s"(sv)
+                 : "v"(voff), "s"(m0), "s"(base), "n"(OFF)
+                 : "memory");
+}
+
+// FP8 rows in the wide kernel: one wave's token octet of a block as 6 loads of 1 KB.  Each lane
+// gathers 16-B units so that the wave's own 1 KB areas of the slot (at m0 + 4096 region) hold
+//   regions 1, 3, 5, 7: code pair j (columns 128 j .. 128 j + 127 of the 8 tokens: lane 8 r + y
+//                       loads bytes 128 j + 16 y of token r; vcode = row + 16 y, offset 128 j),
+//   region 6:           the four group scales of token L / 8 at 16 L (every lane of a token
+//                       loads the same 16 B),
+//   region 8:           the bf16 rope chunks, already in the bf16 layout (vrope as the bf16 DMA).
+// The wave then converts the codes in place (wide_decode_kernel, `convert`) into regions 0..7.
+// Offsets stay below 4096, so M0 steps per load: 4096, then +8064 three times (region 2 j + 1
+// minus the instruction offset 128 j), -3712 to region 6, +8192 to region 8.
+template <bool NT>
+__device__ __forceinline__ void dma_wide_f8(const uint8_t* base, uint32_t vcode, uint32_t vscale, uint32_t vrope,
+                                            uint32_t m0) {
+  uint32_t sv;
+#define MLA_WF8(NTS)                                                                              \
+  asm volatile("s_mov_b32 %0, m0\n\ts_add_u32 m0, %4, 4096\n\ts_nop 0\n\t"                   \
+               "global_load_lds_dwordx4 %1, %5" NTS "\n\t"                                     \
+               "s_add_u32 m0, m0, 8064\n\ts_nop 0\n\t"                                          \
+               "global_load_lds_dwordx4 %1, %5 offset:128" NTS "\n\t"                          \
+               "s_add_u32 m0, m0, 8064\n\ts_nop 0\n\t"                                          \
+               "global_load_lds_dwordx4 %1, %5 offset:256" NTS "\n\t"                          \
+               "s_add_u32 m0, m0, 8064\n\ts_nop 0\n\t"                                          \
+               "global_load_lds_dwordx4 %1, %5 offset:384" NTS "\n\t"                          \
+               "s_sub_u32 m0, m0, 3712\n\ts_nop 0\n\t"                                          \
+               "global_load_lds_dwordx4 %2, %5" NTS "\n\t"                                     \
+               "s_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"                                          \
+               "global_load_lds_dwordx4 %3, %5" NTS "\n\t"                                     \
+               "s_mov_b32 m0, %0"                                                              \
+               : "=&s"(sv)                                                                     \
+               : "v"(vcode), "v"(vscale), "v"(vrope), "s"(m0), "s"(base)                       \
+               : "memory", "scc")
+  if constexpr (NT)
+    MLA_WF8(" nt");
+  else
+    MLA_WF8("");
+#undef MLA_WF8
+}
+constexpr int kWF8Loads = 6;
+// Block k + 2's loads are spread over block k's 36 S^T steps (issued together, right after the
+// barrier, the four waves' loads queue behind each other): load j at step kWDma0 + kWDmaStride j.
+constexpr int kWDma0 = 1, kWDmaStride = 4;                 // bf16: 9 loads, steps 1 .. 33
+constexpr int kWDma0F8 = 4, kWDmaStrideF8 = 6;             // FP8: 6 loads, steps 4 .. 34
+static_assert(kWDma0 + 8 * kWDmaStride < 36 && kWDma0F8 + 5 * kWDmaStrideF8 < 36, "load steps");
+// Where the conversion of the next block sits among the S^T steps: its loads are waited for at
+// step kWCvWait (before any of block k + 2's loads is issued, so that the wait is for all loads
+// in flight), code pair j is read at step kWCvWait + 1 + kWCvStride j and written kWCvLag steps
+// later.
+constexpr int kWCvWait = 2;
+constexpr int kWCvStride = 6;
+constexpr int kWCvLag = 4;
+static_assert(kWCvWait + 1 + 3 * kWCvStride + kWCvLag < 36 && kWCvLag <= kWCvStride && kWCvWait < kWDma0F8,
+              "conversion steps");
+
 // S^T steps on a 32x32x16 bf16 MFMA with the accumulator in VGPRs: the 512 x 32 O^T tile fills
 // all 256 accumulation registers, and the builtin would borrow 16 of them (moving an O^T tile out
 // and back around every block).  acc = a b (first step, no accumulator input), acc += a b, and the
@@ -1283,8 +1354,9 @@ __device__ __forceinline__ void mfma32_vlast(f32x16_t& acc, const bf16x8_t& a, c
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc) : "v"(a), "v"(b));
 }
 
-template <bool OUT_F32, bool NT>
+template <bool OUT_F32, bool NT, bool FP8>
 __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) {
+  constexpr int kRowB = FP8 ? kF8Row : kRowBytesBf16;    // bytes per cache row
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kWSmem];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
 
@@ -1326,6 +1398,12 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
   const int dma_tok = 8 * wave + (lane >> 3);
   const uint32_t dma_col = 16u * (uint32_t)((lane & 7) ^ wswz(dma_tok));
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  // FP8 conversion (lane L = 8 r + x converts token r of the wave's octet): the bf16 unit it
+  // writes at 1024 wave + 16 L of region cg holds chunk c = 8 cg + xs, xs = x ^ wswz(token), i.e.
+  // codes 8 c .. 8 c + 7, which code pair cg / 2 holds at unit 8 r + 4 (cg % 2) + xs / 2, half xs % 2
+  const int cv_xs = (lane & 7) ^ wswz(dma_tok);
+  const int cv_rd = 1024 * wave + 16 * (8 * (lane >> 3) + (cv_xs >> 1)) + 8 * (cv_xs & 1);
+  const int cv_wr = 1024 * wave + 16 * lane;
 
   const CST_AS int32_t* worker_off = as_const(a.worker_off);
   const CST_AS int32_t* pieces = as_const(a.pieces);
@@ -1364,38 +1442,138 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
       __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
     }
 
-    // Block k's page walk: the rows of its two 16-token halves' first tokens (clamped to the
-    // piece; -1 for an out-of-range table entry).  A half never spans two pages (pieces start on
-    // 16-token boundaries and pages hold a multiple of 16 tokens).
+    // Block k's page walk: the table entries (physical pages) of its two 16-token halves'
+    // first tokens (clamped to the piece) and those tokens' rows within their pages.  A half
+    // never spans two pages (pieces start on 16-token boundaries and pages hold a multiple of 16
+    // tokens).  walk() only reads the two entries, with no branch or use between the reads, so
+    // that both are in flight together; publish() uses them after its barrier, so that they are
+    // in flight across its waits.  An entry outside [0, num_pages) marks its half out of range.
     struct Walk {
-      int64_t row[2];
+      int g[2];      // table entries
+      int off[2];    // rows within the page
     };
+    const CST_AS int32_t* const bt_row = block_table + (int64_t)b * a.bt_stride;
     auto walk = [&](int k) -> Walk {
       const int t0 = tb + kWBlock * k;
       const int t1 = min(t0 + 16, te - 1);
-      return Walk{{kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, t0),
-                   kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, t1)}};
+      int p0, p1;
+      if (a.page_shift >= 0) {
+        p0 = t0 >> a.page_shift;
+        p1 = t1 >> a.page_shift;
+      } else {
+        p0 = t0 / a.page_size;
+        p1 = t1 / a.page_size;
+      }
+      return Walk{{bt_row[p0], bt_row[p1]}, {t0 - p0 * a.page_size, t1 - p1 * a.page_size}};
     };
-    auto halves_ok = [&](const Walk& w) -> uint32_t { return (w.row[0] >= 0 ? 1u : 0u) | (w.row[1] >= 0 ? 2u : 0u); };
+    auto in_range = [&](int g) -> bool { return (uint32_t)g < (uint32_t)a.num_pages; };
+    auto halves_ok = [&](const Walk& w) -> uint32_t { return (in_range(w.g[0]) ? 1u : 0u) | (in_range(w.g[1]) ? 2u : 0u); };
     // This wave's octet of block k (half wave / 2, 8 (wave % 2) tokens into it): its SGPR row
     // base, page 0 for an out-of-range entry (the octet is then zeroed and masked).  Lanes past
     // the end re-read the last row of the piece.
     auto octet_base = [&](int k, const Walk& w) -> const uint8_t* {
-      const int64_t r = (wave >> 1) ? w.row[1] : w.row[0];
+      const int g = (wave >> 1) ? w.g[1] : w.g[0];
+      const int off = (wave >> 1) ? w.off[1] : w.off[0];
       const int t_half = min(tb + kWBlock * k + 16 * (wave >> 1), te - 1);     // the half's first row
       const int ts = min(tb + kWBlock * k + 8 * wave, te - 1);                  // the octet's first row
-      return kv8 + (r < 0 ? 0 : r + (ts - t_half)) * kRowBytesBf16;
+      return kv8 + (in_range(g) ? (int64_t)g * a.page_size + off + (ts - t_half) : 0) * kRowB;
     };
     auto octet_voff = [&](int k) -> uint32_t {
       const int tok0 = tb + kWBlock * k;
       const int ts = min(tok0 + 8 * wave, te - 1);
       const int t = min(tok0 + dma_tok, te - 1);
-      return (uint32_t)(t - ts) * kRowBytesBf16 + dma_col;
+      return (uint32_t)(t - ts) * kRowB + dma_col;
     };
     // NT: non-temporal loads (one row group: no other work-group re-reads these rows)
     auto issue = [&](int k, const uint8_t* base) {
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((k % kWSlots) * kWBlockBytes + 1024 * wave));
-      dma_wide_octet<NT>(base, octet_voff(k), m0);
+      if constexpr (FP8) {
+        // the row of this lane's token (its rope offset is the bf16 DMA's column offset + 512)
+        const uint32_t rv = octet_voff(k) - dma_col;
+        dma_wide_f8<NT>(base, rv + 16u * (uint32_t)(lane & 7), rv + 640u, rv + 512u + dma_col, m0);
+      } else {
+        dma_wide_octet<NT>(base, octet_voff(k), m0);
+      }
+    };
+    // The same loads one at a time (block k + 2's, spread over block k's S^T): `pend` holds the
+    // block's addresses from publish() on; part j is load j of dma_wide_octet / dma_wide_f8.
+    struct Pending {
+      const uint8_t* base;
+      uint32_t v[3];
+      uint32_t m0;
+    };
+    Pending pend{nullptr, {0u, 0u, 0u}, 0u};
+    auto plan_issue = [&](int k, const uint8_t* base) {
+      pend.base = base;
+      pend.m0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((k % kWSlots) * kWBlockBytes + 1024 * wave));
+      if constexpr (FP8) {
+        const uint32_t rv = octet_voff(k) - dma_col;
+        pend.v[0] = rv + 16u * (uint32_t)(lane & 7);
+        pend.v[1] = rv + 640u;
+        pend.v[2] = rv + 512u + dma_col;
+      } else {
+        pend.v[0] = octet_voff(k);
+      }
+    };
+    auto issue_part = [&](int j) {
+      if constexpr (FP8) {
+        switch (j) {
+          case 0: dma_one<NT, 0>(pend.base, pend.v[0], pend.m0 + 4096u); break;
+          case 1: dma_one<NT, 128>(pend.base, pend.v[0], pend.m0 + 12160u); break;
+          case 2: dma_one<NT, 256>(pend.base, pend.v[0], pend.m0 + 20224u); break;
+          case 3: dma_one<NT, 384>(pend.base, pend.v[0], pend.m0 + 28288u); break;
+          case 4: dma_one<NT, 0>(pend.base, pend.v[1], pend.m0 + 24576u); break;
+          default: dma_one<NT, 0>(pend.base, pend.v[2], pend.m0 + 32768u); break;
+        }
+      } else {
+        switch (j) {
+          case 0: dma_one<NT, 0>(pend.base, pend.v[0], pend.m0); break;
+          case 1: dma_one<NT, 128>(pend.base, pend.v[0], pend.m0 + 3968u); break;
+          case 2: dma_one<NT, 256>(pend.base, pend.v[0], pend.m0 + 2u * 3968u); break;
+          case 3: dma_one<NT, 384>(pend.base, pend.v[0], pend.m0 + 3u * 3968u); break;
+          case 4: dma_one<NT, 512>(pend.base, pend.v[0], pend.m0 + 4u * 3968u); break;
+          case 5: dma_one<NT, 640>(pend.base, pend.v[0], pend.m0 + 5u * 3968u); break;
+          case 6: dma_one<NT, 768>(pend.base, pend.v[0], pend.m0 + 6u * 3968u); break;
+          case 7: dma_one<NT, 896>(pend.base, pend.v[0], pend.m0 + 7u * 3968u); break;
+          default: dma_one<NT, 1024>(pend.base, pend.v[0], pend.m0 + 8u * 3968u); break;
+        }
+      }
+    };
+    // FP8: convert this wave's octet of block k (its loads have landed) in place into the bf16
+    // layout.  Code pair j becomes regions 2 j and 2 j + 1, with the group scale's exponent
+    // applied by the conversion (code * 2^e is exact in bf16); an out-of-range table entry
+    // (`ok` false: page 0 was read) gives zeros, rope included.  In three parts so that the
+    // caller can spread them over its MFMAs: scales, then per pair the reads and the writes
+    // (the writes of pair j overwrite only pairs already read, and the scales only at j = 3,
+    // after the data they depend on).
+    auto cv_scales = [&](int k) -> u32x4_t {
+      return lds_ld128(lds + (k % kWSlots) * kWBlockBytes + 24576 + cv_wr);
+    };
+    auto cv_read = [&](int k, int j) -> u32x4_t {
+      LDS_AS const uint8_t* st = lds + (k % kWSlots) * kWBlockBytes + 4096 * (2 * j + 1) + cv_rd;
+      const u32x2_t a0 = lds_ld64(st), a1 = lds_ld64(st + 64);
+      return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    };
+    auto cv_write = [&](int k, int j, const u32x4_t& raw, const u32x4_t& scl, bool ok) {
+      LDS_AS uint8_t* st = lds + (k % kWSlots) * kWBlockBytes + cv_wr;
+      const float sc = __uint_as_float(scl[j] & 0x7F800000u);
+      u32x4_t w[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          w[hh][2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[2 * hh + d], sc, false));
+          w[hh][2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[2 * hh + d], sc, true));
+        }
+      *(LDS_AS u32x4_t*)(st + 4096 * (2 * j)) = w[0];
+      *(LDS_AS u32x4_t*)(st + 4096 * (2 * j + 1)) = w[1];
+      if (!ok) {
+        // out of range (rare; ok is uniform): the same units again, zeroed (LDS writes of one
+        // wave land in order), and the rope with the last pair
+        *(LDS_AS u32x4_t*)(st + 4096 * (2 * j)) = u32x4_t{0u, 0u, 0u, 0u};
+        *(LDS_AS u32x4_t*)(st + 4096 * (2 * j + 1)) = u32x4_t{0u, 0u, 0u, 0u};
+        if (j == 3) *(LDS_AS u32x4_t*)(st + 32768) = u32x4_t{0u, 0u, 0u, 0u};
+      }
     };
 
     float m_run = -INFINITY;     // the row's largest scaled score so far (log2 units)
@@ -1428,19 +1606,23 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
         }
       // Publish block k: wait for this wave's octet, zero it if its table entry was out of
       // range, barrier (every wave's octet of block k is in LDS and every wave is done with
-      // block k - 2, whose slot then receives block k + 2).  Returns block k's halves' state.
+      // block k - 2, whose slot then receives block k + 2, loaded during block k's S^T).
+      // Returns block k's halves' state.
+      // FP8: the octet was converted (and zeroed where needed) before, by `convert` in the
+      // prologue or during block k - 1's S^T; only the LDS writes are waited for.
       auto publish = [&](int k) -> uint32_t {
         const bool nx = k + 2 < nblk;
-        const Walk nw = nx ? walk(k + 2) : Walk{{0, 0}};        // scalar table reads overlap the wait
-        const uint8_t* nbase = octet_base(k + 2, nw);
-        const uint32_t nok = nx ? halves_ok(nw) : 3u;
-        if (k + 1 < nblk)
-          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        Walk nw{{0, 0}, {0, 0}};
+        if (nx) nw = walk(k + 2);        // scalar table reads, consumed after the barrier
+        if constexpr (!FP8) {
+          if (k + 1 < nblk)
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         const int sl = k % kWSlots;
         const uint32_t hok = (okq >> (2 * sl)) & 3u;
-        if (((hok >> (wave >> 1)) & 1u) == 0) {
+        if (!FP8 && ((hok >> (wave >> 1)) & 1u) == 0) {
           // out-of-range table entry: this octet read page 0; zero its rows (V enters the
           // products; its scores are masked).  Flagged after the piece, outside the DMA waits.
           bad_page = true;
@@ -1453,9 +1635,9 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (nx) {
-          issue(k + 2, nbase);
+          plan_issue(k + 2, octet_base(k + 2, nw));     // issued during block k's S^T
           const int ns = (k + 2) % kWSlots;
-          okq = (okq & ~(3u << (2 * ns))) | (nok << (2 * ns));
+          okq = (okq & ~(3u << (2 * ns))) | (halves_ok(nw) << (2 * ns));
         }
         return hok;
       };
@@ -1474,10 +1656,35 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
         // the rope k-steps (kk >= 32) take their query operand from LDS, two steps ahead
         auto qload = [&](int kk) -> bf16x8_t { return __builtin_bit_cast(bf16x8_t, lds_ld128(qrope + 1024 * (kk - 32))); };
         bf16x8_t kr[kWRing], qr[2];
+        // FP8: block k + 1's octet is converted between the S^T steps (no vector work competes
+        // there): its loads are waited for at step kWCvWait (block k + 2's are issued later),
+        // then the scales and one code pair at a time
+        const bool cv = FP8 && k + 1 < nblk;
+        const bool cv_ok = ((okq >> (2 * ((k + 1) % kWSlots) + (wave >> 1))) & 1u) != 0;
+        u32x4_t cvs, cvr;
 #pragma unroll
         for (int j = 0; j < kWRing; ++j) kr[j] = kload(j);
 #pragma unroll
         for (int kk = 0; kk < kKSteps * 2; ++kk) {
+          if constexpr (FP8) {
+            if (cv) {
+              if (kk == kWCvWait) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // only block k + 1's loads are in flight
+                bad_page |= !cv_ok;
+                cvs = cv_scales(k + 1);
+              }
+              constexpr int r0 = kWCvWait + 1, w0 = r0 + kWCvLag;
+              if (kk >= r0 && kk < r0 + 4 * kWCvStride && (kk - r0) % kWCvStride == 0)
+                cvr = cv_read(k + 1, (kk - r0) / kWCvStride);
+              if (kk >= w0 && kk < w0 + 4 * kWCvStride && (kk - w0) % kWCvStride == 0)
+                cv_write(k + 1, (kk - w0) / kWCvStride, cvr, cvs, cv_ok);
+            }
+          }
+          if (k + 2 < nblk) {                 // block k + 2's loads, one every few steps
+            constexpr int d0 = FP8 ? kWDma0F8 : kWDma0, ds = FP8 ? kWDmaStrideF8 : kWDmaStride;
+            constexpr int nd = FP8 ? kWF8Loads : 9;
+            if (kk >= d0 && (kk - d0) % ds == 0 && (kk - d0) / ds < nd) issue_part((kk - d0) / ds);
+          }
           if (kk == 30 || kk == 31) qr[kk & 1] = qload(kk + 2);
           const bf16x8_t qv = kk < 32 ? qf[kk & 31] : qr[kk & 1];
           if (kk == 0)
@@ -1592,6 +1799,20 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
       };
 
       u32x4_t ph_prev[2], pl_prev[2];
+      if constexpr (FP8) {
+        if (nblk > 0) {
+          // block 0's octet (block 1's loads may still be in flight)
+          if (nblk > 1)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWF8Loads) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          const bool ok0 = ((okq >> (wave >> 1)) & 1u) != 0;
+          bad_page |= !ok0;
+          const u32x4_t scl = cv_scales(0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cv_write(0, j, cv_read(0, j), scl, ok0);
+        }
+      }
       if (nblk > 0) {
         const uint32_t hok = publish(0);
         const f32x16_t sa = scores(0, hok);
@@ -1836,6 +2057,29 @@ void launch_split(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
   }
 }
 
+// The wide kernel: non-temporal KV loads when one row group reads each token range
+template <bool FP8>
+void launch_wide_t(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
+  const bool nt = a.row_groups == 1;
+  if (out_fp32) {
+    if (nt)
+      hipLaunchKernelGGL((wide_decode_kernel<true, true, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((wide_decode_kernel<true, false, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
+  } else {
+    if (nt)
+      hipLaunchKernelGGL((wide_decode_kernel<false, true, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((wide_decode_kernel<false, false, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
+  }
+}
+void launch_wide(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
+  if (a.kv_fp8)
+    launch_wide_t<true>(a, out_fp32, grid, s);
+  else
+    launch_wide_t<false>(a, out_fp32, grid, s);
+}
+
 // Read ceiling of the decode's KV stream: every work-group moves its contiguous share of `buf`
 // into LDS with the same non-temporal 16-B global->LDS loads as the decode (each wave 18 KB blocks
 // through two stages, blocks w, w + 4, ... of its work-group's share) and computes nothing.
@@ -1884,7 +2128,9 @@ int launch_fill_zero(void* p, size_t bytes, void* stream) {
 int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream,
                   bool device_schedule) {
   hipStream_t s = (hipStream_t)stream;
-  if (device_schedule || a.kv_fp8) {
+  if (rows_per_group == 128 && !device_schedule) {
+    launch_wide(a, out_fp32, grid, s);
+  } else if (device_schedule || a.kv_fp8) {
     if (rows_per_group != 16) return (int)hipErrorInvalidValue;
     if (device_schedule)
       launch_split<true>(a, out_fp32, grid, s);
@@ -1902,19 +2148,6 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
       hipLaunchKernelGGL((group_decode_kernel<4, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((group_decode_kernel<4, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
-  } else if (rows_per_group == 128) {
-    const bool nt = a.row_groups == 1;
-    if (out_fp32) {
-      if (nt)
-        hipLaunchKernelGGL((wide_decode_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((wide_decode_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, a);
-    } else {
-      if (nt)
-        hipLaunchKernelGGL((wide_decode_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL((wide_decode_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, a);
-    }
   } else {
     return (int)hipErrorInvalidValue;
   }

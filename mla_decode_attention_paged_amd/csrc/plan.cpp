@@ -48,7 +48,7 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
   if (rows_per_group != 0)
     pl.rows_per_group = rows_per_group;
   else
-    pl.rows_per_group = (R % 128 == 0 && bf16) ? 128 : (R % 64 == 0 && bf16) ? 64 : 16;
+    pl.rows_per_group = R % 128 == 0 ? 128 : (R % 64 == 0 && bf16) ? 64 : 16;
   pl.row_groups = (int32_t)(R / pl.rows_per_group);
   pl.granule = kBlock;
 

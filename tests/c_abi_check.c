@@ -66,7 +66,11 @@ int main(void) {
   p.kv_dtype = MLA_KV_FP8_E4M3;
   opt.rows_per_group = 64;   /* the grouped kernel reads bf16 rows only */
   CHECK(mla_plan(&p, lens, &opt, &plan) == MLA_ERR_UNSUPPORTED);
-  opt.rows_per_group = 0;
+  opt.rows_per_group = 0;   /* FP8 rows at R = 128: the wide kernel, one row group */
+  CHECK(mla_plan(&p, lens, &opt, &plan) == MLA_OK);
+  CHECK(mla_plan_get_info(plan, &info) == MLA_OK && info.rows_per_group == 128 && info.row_groups == 1);
+  mla_plan_destroy(plan);
+  opt.rows_per_group = 16;
   CHECK(mla_plan(&p, lens, &opt, &plan) == MLA_OK);
   CHECK(mla_plan_get_info(plan, &info) == MLA_OK && info.rows_per_group == 16 && info.row_groups == 8);
   mla_plan_destroy(plan);

@@ -1,9 +1,12 @@
 """FP8 (E4M3) latent cache rows on the HIP path (through the C-ABI) against the fp64 oracle.
 
-The kernel converts the codes to bf16 in registers (K with the exponent of its group scale,
-V^T unscaled with each token's power-of-two scale folded into its softmax weight), which is
-exact and forms the same products as the bf16 path; so an fp8 cache and a bf16 cache holding
-the same values give bit-identical results, and the fp32-output bounds of the bf16 path apply.
+The 16-row kernel converts the codes to bf16 in registers (K with the exponent of its group
+scale, V^T unscaled with each token's power-of-two scale folded into its softmax weight); the
+128-row kernel converts each block once in LDS into the bf16 layout (code times the scale's
+power of two).  Both are exact and form the same products as the bf16 path of the same kernel;
+so an fp8 cache and a bf16 cache holding the same values give bit-identical results, and the
+fp32-output bounds of the bf16 path apply.  Tests with 128 heads run the 128-row kernel (the
+default when R is a multiple of 128).
 """
 import numpy as np
 import pytest
@@ -29,6 +32,20 @@ def run(prob, **kw):
 def oracle(prob, batch_idx=None, causal=False):
     return orc.decode(prob.q, prob.kv_cache, prob.block_table, prob.cache_seqlens, prob.softmax_scale,
                       prob.page_size, batch_indices=batch_idx, causal=causal)
+
+
+def with_page_zero_unmapped(prob):
+    """The same problem with physical page 0 swapped with an unmapped page and its latent codes
+    set to NaN (0x7F): the page a DMA reads for an out-of-range table entry then holds NaN."""
+    bt = prob.block_table.copy()
+    used = set(bt[bt >= 0].tolist())
+    u = next(p for p in range(prob.num_pages) if p not in used)
+    kv = prob.kv_cache.copy()
+    kv[[0, u]] = kv[[u, 0]]
+    bt[bt == 0] = u
+    kv[0, :, :512] = 0x7F
+    return gen.Problem(q=prob.q, kv_cache=kv, block_table=bt, cache_seqlens=prob.cache_seqlens,
+                       softmax_scale=prob.softmax_scale, page_size=prob.page_size, out_fp32=prob.out_fp32)
 
 
 def check(out, lse, ref_o, ref_l, out_fp32, what, wabs=None):
@@ -60,26 +77,31 @@ def test_fp8_gather_bit_exact(page):
         off += L
 
 
+@pytest.mark.parametrize("heads", [16, 128])
 @pytest.mark.parametrize("out_fp32", [True, False])
 @pytest.mark.parametrize("page", [16, 48, 64])
-def test_fp8_edge_lengths_nan_tails(page, out_fp32):
-    lengths = [1, 2, 15, 16, 17, 63, 64, 65, 1000, 5000]
-    prob = gen.make_problem(batch=len(lengths), q_len=1, num_heads=16, page_size=page, lengths=lengths, seed=52,
+def test_fp8_edge_lengths_nan_tails(page, out_fp32, heads):
+    lengths = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 1000, 5000]
+    prob = gen.make_problem(batch=len(lengths), q_len=1, num_heads=heads, page_size=page, lengths=lengths, seed=52,
                             tail="nan", extra_pages=3, out_fp32=out_fp32, kv_format="fp8")
-    out, lse = run(prob)
+    r = Runner(prob)
+    assert r.plan.info()["rows_per_group"] == (128 if heads == 128 else 16)
+    r()
+    out, lse = r.results()
     ref_o, ref_l = oracle(prob)
-    check(out, lse, ref_o, ref_l, out_fp32, f"fp8 edges P={page}", None if out_fp32 else softmax_abs_v(prob))
+    check(out, lse, ref_o, ref_l, out_fp32, f"fp8 edges P={page} H={heads}", None if out_fp32 else softmax_abs_v(prob))
 
 
+@pytest.mark.parametrize("heads", [16, 128])
 @pytest.mark.parametrize("out_fp32", [True, False])
-def test_fp8_many_pieces_per_work_group(out_fp32):
-    """Few work-groups, each walking many short FP8 sequences (the three stages reused
+def test_fp8_many_pieces_per_work_group(out_fp32, heads):
+    """Few work-groups, each walking many short FP8 sequences (the stages or slots reused
     from piece to piece), with empty and one-token sequences among them."""
     rng = np.random.default_rng(53)
     lengths = rng.integers(0, 120, size=300)
     lengths[::13] = 0
     lengths[3::19] = 1
-    prob = gen.make_problem(batch=300, q_len=1, num_heads=16, page_size=16, lengths=lengths.tolist(), seed=53,
+    prob = gen.make_problem(batch=300, q_len=1, num_heads=heads, page_size=16, lengths=lengths.tolist(), seed=53,
                             tail="nan", out_fp32=out_fp32, kv_format="fp8")
     r = Runner(prob, num_cus=16)
     assert max(np.diff(r.plan.segments()[1])) > 10
@@ -98,17 +120,19 @@ def test_fp8_more_query_rows(heads, q_len):
     check(out, lse, ref_o, ref_l, True, f"fp8 H={heads} S_q={q_len}")
 
 
+@pytest.mark.parametrize("heads", [16, 128])
 @pytest.mark.parametrize("force", [2, 3, 1000])
-def test_fp8_forced_splits(force):
-    prob = gen.make_problem(batch=3, q_len=1, num_heads=16, page_size=64, lengths=[4096, 100, 2500], seed=54,
+def test_fp8_forced_splits(force, heads):
+    prob = gen.make_problem(batch=3, q_len=1, num_heads=heads, page_size=64, lengths=[4096, 100, 2500], seed=54,
                             out_fp32=True, kv_format="fp8")
     out, lse = run(prob, force_splits=force)
     ref_o, ref_l = oracle(prob)
-    check(out, lse, ref_o, ref_l, True, f"fp8 force={force}")
+    check(out, lse, ref_o, ref_l, True, f"fp8 force={force} H={heads}")
 
 
-def test_fp8_causal_two_token():
-    prob = gen.make_problem(batch=5, q_len=2, num_heads=16, page_size=16, lengths=[1, 2, 17, 300, 3000], seed=55,
+@pytest.mark.parametrize("heads", [16, 64])
+def test_fp8_causal_two_token(heads):
+    prob = gen.make_problem(batch=5, q_len=2, num_heads=heads, page_size=16, lengths=[1, 2, 17, 300, 3000], seed=55,
                             tail="nan", extra_pages=1, out_fp32=True, kv_format="fp8")
     out, lse = run(prob, causal=True)
     ref_o, ref_l = oracle(prob, causal=True)
@@ -117,9 +141,10 @@ def test_fp8_causal_two_token():
     check(out, lse, ref_o, ref_l, True, "fp8 causal")
 
 
-def test_fp8_equals_bf16_cache_with_the_same_values():
+@pytest.mark.parametrize("heads", [16, 128])
+def test_fp8_equals_bf16_cache_with_the_same_values(heads):
     """Widening is exact and the arithmetic after it is the bf16 path's: bit-identical."""
-    prob = gen.make_problem(batch=4, q_len=1, num_heads=16, page_size=64, lengths=[3000, 64, 5000, 17], seed=56,
+    prob = gen.make_problem(batch=4, q_len=1, num_heads=heads, page_size=64, lengths=[3000, 64, 5000, 17], seed=56,
                             kv_format="fp8")
     wide = orc.widen_fp8_rows(prob.kv_cache.reshape(-1, 656)).astype(np.float32)
     bits = (wide.view(np.uint32) >> 16).astype(np.uint16)
@@ -143,12 +168,13 @@ def test_fp8_full_size(name):
     compare_every_sequence(out, lse, ref_o, ref_l, f"{name} fp8")
 
 
+@pytest.mark.parametrize("heads", [64, 128])
 @pytest.mark.parametrize("out_fp32", [True, False])
-def test_fp8_scales_with_mantissa_bits_use_the_exponent_only(out_fp32):
+def test_fp8_scales_with_mantissa_bits_use_the_exponent_only(out_fp32, heads):
     """Group scales that are not powers of two (1.5 * 2^e, 1.9375 * 2^e): only their exponent
     counts (the row format; the oracle decodes it that way).  Equal, bit for bit, to the same
     cache with the scales' mantissas cleared, and to the oracle within the usual bounds."""
-    prob = gen.make_problem(batch=3, q_len=1, num_heads=64, page_size=64, lengths=[2100, 333, 64], seed=57,
+    prob = gen.make_problem(batch=3, q_len=1, num_heads=heads, page_size=64, lengths=[2100, 333, 64], seed=57,
                             kv_format="fp8", out_fp32=out_fp32)
     kv = prob.kv_cache.copy()
     sc = np.ascontiguousarray(kv[..., 640:656]).view(np.uint32)
@@ -163,11 +189,13 @@ def test_fp8_scales_with_mantissa_bits_use_the_exponent_only(out_fp32):
     check(o1, l1, ref_o, ref_l, out_fp32, "scales with mantissa bits", None if out_fp32 else softmax_abs_v(odd))
 
 
-def test_fp8_out_of_range_block_table_entry_drops_its_tokens():
-    """A used table entry outside [0, num_pages): its 16-token blocks are masked out (their DMA
-    reads page 0), bit 0 of the status word is set, and the rest is exact."""
-    prob = gen.make_problem(batch=2, q_len=1, num_heads=16, page_size=64, lengths=[640, 600], seed=31,
-                            kv_format="fp8", out_fp32=True)
+@pytest.mark.parametrize("heads", [16, 128])
+def test_fp8_out_of_range_block_table_entry_drops_its_tokens(heads):
+    """A used table entry outside [0, num_pages): its tokens are masked out (their DMA reads
+    page 0), bit 0 of the status word is set, and the rest is exact."""
+    prob = with_page_zero_unmapped(gen.make_problem(batch=2, q_len=1, num_heads=heads, page_size=64,
+                                                    lengths=[640, 600], seed=31, extra_pages=1, kv_format="fp8",
+                                                    out_fp32=True))
     bt = prob.block_table.copy()
     bt[1, 3] = prob.num_pages + 5
     bad = gen.Problem(q=prob.q, kv_cache=prob.kv_cache, block_table=bt, cache_seqlens=prob.cache_seqlens,
@@ -179,3 +207,45 @@ def test_fp8_out_of_range_block_table_entry_drops_its_tokens():
     ref_o, ref_l = oracle(prob, [0])
     compare(out, lse, ref_o, ref_l, batch_idx=[0], what="fp8 unaffected sequence", tol=TIGHT)
     check_dropped_page(prob, out, lse, seq=1, page_idx=3, tol=TIGHT)
+
+
+@pytest.mark.parametrize("out_fp32", [True, False])
+def test_fp8_wide_and_16_row_kernels_agree(out_fp32):
+    """The 128-row kernel (the default at 128 heads) against the 16-row kernel forced on the same
+    FP8 problem: both within the oracle's bounds, and with fp32 output within 2 ulps of each
+    other's scale (the two sum the same products in different orders)."""
+    prob = gen.make_problem(batch=4, q_len=1, num_heads=128, page_size=64, lengths=[4000, 1, 700, 2049], seed=58,
+                            out_fp32=out_fp32, kv_format="fp8")
+    rw = Runner(prob)
+    r16 = Runner(prob, rows_per_group=16)
+    assert rw.plan.info()["rows_per_group"] == 128 and r16.plan.info()["rows_per_group"] == 16
+    rw()
+    r16()
+    ow, lw = rw.results()
+    o16, l16 = r16.results()
+    ref_o, ref_l = oracle(prob)
+    wabs = None if out_fp32 else softmax_abs_v(prob)
+    check(ow, lw, ref_o, ref_l, out_fp32, "fp8 128 rows", wabs)
+    check(o16, l16, ref_o, ref_l, out_fp32, "fp8 16 rows", wabs)
+    assert np.max(np.abs(lw - l16)) <= 1e-5
+
+
+def test_fp8_wide_dropped_half_block():
+    """Page size 16 at 128 heads: an out-of-range entry drops one 16-token half of a 32-token block
+    of the 128-row kernel (the first half in sequence 0, the second in sequence 1); page 0, which
+    the DMA reads instead, holds NaN codes.  The status bit is set and the rest is exact."""
+    prob = with_page_zero_unmapped(gen.make_problem(batch=2, q_len=1, num_heads=128, page_size=16,
+                                                    lengths=[640, 650], seed=59, tail="nan", extra_pages=2,
+                                                    out_fp32=True, kv_format="fp8"))
+    bt = prob.block_table.copy()
+    bt[0, 10] = -1
+    bt[1, 5] = prob.num_pages + 3
+    bad = gen.Problem(q=prob.q, kv_cache=prob.kv_cache, block_table=bt, cache_seqlens=prob.cache_seqlens,
+                      softmax_scale=prob.softmax_scale, page_size=16, out_fp32=True)
+    r = Runner(bad)
+    assert r.plan.info()["rows_per_group"] == 128
+    r()
+    out, lse = r.results()
+    assert B.mla_read_status(r.ws) & 1
+    check_dropped_page(prob, out, lse, seq=0, page_idx=10, tol=TIGHT)
+    check_dropped_page(prob, out, lse, seq=1, page_idx=5, tol=TIGHT)
