@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 6
+#define MLA_ABI_VERSION 7
 
 typedef enum {
   MLA_OK = 0,
@@ -197,10 +197,21 @@ mla_status_t mla_decode(mla_plan_t plan, const void* q, const void* kv_cache,
  * MLA_STAGE_SPLIT runs the split-decode kernel, MLA_STAGE_MERGE the merge of split
  * sequences (which reads the partials the last split stage wrote).
  * mla_decode == mla_decode_stages(..., MLA_STAGE_ALL).  Same arguments and errors
- * as mla_decode; stages outside MLA_STAGE_ALL is MLA_ERR_INVALID_ARGUMENT. */
+ * as mla_decode; stages outside MLA_STAGE_ALL is MLA_ERR_INVALID_ARGUMENT.
+ *
+ * MLA_STAGE_COMBINED (alone): one launch instead of two -- the split-decode kernel combines
+ * split sequences itself, the way the pages' single-work-group pipeline (FlashMLA-ETAP
+ * summary, "Implementation details") finishes a head group within one kernel.  Each piece's
+ * partial result is stored with device-scope (write-through) stores;
+ * the work-group that completes a (sequence, row group) last, elected by a device-scope
+ * counter in the workspace, reads the partials back with device-scope loads and writes out
+ * and lse; the counter is back at zero when the launch ends (mla_plan_upload writes zeros).
+ * Plans with 16 rows per group only (else MLA_ERR_UNSUPPORTED).  Results equal
+ * MLA_STAGE_ALL's up to the order of the combine's additions. */
 #define MLA_STAGE_SPLIT 1u
 #define MLA_STAGE_MERGE 2u
 #define MLA_STAGE_ALL 3u
+#define MLA_STAGE_COMBINED 4u
 mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_cache,
                                const int32_t* block_table, const int32_t* cache_seqlens,
                                float softmax_scale, void* out, float* lse,
@@ -241,6 +252,16 @@ mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_worker
                                 const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
                                 float softmax_scale, void* out, float* lse, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* mla_decode_devplan in one launch: the split-decode work-groups combine split sequences
+ * themselves, as MLA_STAGE_COMBINED does for a host plan (device-scope partial stores and
+ * loads, one device-scope counter per (sequence, row group) in the workspace, which
+ * mla_devplan_prepare clears and every launch leaves at zero).  Same arguments, workspace
+ * and errors as mla_decode_devplan; graph-capturable in the same way. */
+mla_status_t mla_decode_devplan_combined(const mla_problem_t* problem, int32_t num_workers, const void* q,
+                                         const void* kv_cache, const int32_t* block_table,
+                                         const int32_t* cache_seqlens, float softmax_scale, void* out, float* lse,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* The device-scheduled decode for callers that cannot allocate device memory (code under graph
  * capture, tight serving loops, harnesses that forbid allocation): the same computation and

@@ -25,6 +25,7 @@ MLA_KV_FP8_E4M3 = 1
 MLA_STAGE_SPLIT = 1
 MLA_STAGE_MERGE = 2
 MLA_STAGE_ALL = 3
+MLA_STAGE_COMBINED = 4
 
 
 class MlaError(RuntimeError):
@@ -78,6 +79,9 @@ _SIGS = {
     "mla_decode_devplan": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                      C.c_void_p]),
+    "mla_decode_devplan_combined": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_void_p,
+                                              C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p,
+                                              C.c_void_p, C.c_size_t, C.c_void_p]),
     "mla_decode_devplan_noalloc": (C.c_int, [C.POINTER(mla_problem_t), C.c_int32, C.c_void_p, C.c_void_p,
                                              C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p,
                                              C.c_void_p]),
@@ -305,7 +309,8 @@ class BoundDevplanDecode:
     stay alive and in place; the cache_seqlens tensor's contents may change between calls)."""
 
     def __init__(self, problem: mla_problem_t, num_workers, q, kv_cache, block_table, cache_seqlens,
-                 softmax_scale, out, lse, workspace):
+                 softmax_scale, out, lse, workspace, combined: bool = False):
+        """combined: mla_decode_devplan_combined (one launch) instead of mla_decode_devplan."""
         import torch
         p = problem
         _require(q, "q", (torch.bfloat16,), (p.batch, p.q_len, p.num_heads, 576))
@@ -319,7 +324,8 @@ class BoundDevplanDecode:
         _require(workspace, "workspace", (torch.uint8,))
         self._problem = mla_problem_t.from_buffer_copy(p)
         self._keep = (q, kv_cache, block_table, cache_seqlens, out, lse, workspace)
-        self._fn = lib().mla_decode_devplan
+        self._name = "mla_decode_devplan_combined" if combined else "mla_decode_devplan"
+        self._fn = getattr(lib(), self._name)
         self._args = (C.byref(self._problem), num_workers, _ptr(q), _ptr(kv_cache), _ptr(block_table),
                       _ptr(cache_seqlens), C.c_float(float(softmax_scale)), _ptr(out), _ptr(lse), _ptr(workspace),
                       C.c_size_t(_nbytes(workspace)))
@@ -327,7 +333,7 @@ class BoundDevplanDecode:
     def __call__(self, stream_handle: int):
         st = self._fn(*self._args, stream_handle)
         if st != MLA_OK:
-            raise MlaError(st, "mla_decode_devplan", last_error())
+            raise MlaError(st, self._name, last_error())
 
 
 def mla_decode_devplan_noalloc(problem: mla_problem_t, num_workers, q, kv_cache, block_table, cache_seqlens,

@@ -108,7 +108,7 @@ void forget_plan(uint64_t id) {
 // [status | per-sequence cut (4 x batch + 2 int32) | partial lse (2W x R) | partial out (2W x R x 512)].
 struct DevLayout {
   int32_t workers = 0, row_groups = 0;
-  size_t off_info = 0, off_lse = 0, off_o = 0, bytes = 0;
+  size_t off_info = 0, off_cnt = 0, off_lse = 0, off_o = 0, bytes = 0;
 };
 
 mla_status_t dev_layout(const mla_problem_t* p, int32_t num_workers, DevLayout& d) {
@@ -129,7 +129,10 @@ mla_status_t dev_layout(const mla_problem_t* p, int32_t num_workers, DevLayout& 
   }
   d.workers = w < 1 ? 1 : w;
   d.off_info = mla::kMetaOffset;
-  d.off_lse = align256(d.off_info + 4 * (4 * (size_t)p->batch + 2));
+  // per (sequence, row group) piece counters of the combining launch: cleared by
+  // mla_devplan_prepare, left at zero by every combining launch
+  d.off_cnt = align256(d.off_info + 4 * (4 * (size_t)p->batch + 2));
+  d.off_lse = align256(d.off_cnt + 4 * (size_t)p->batch * d.row_groups);
   d.off_o = align256(d.off_lse + 4 * 2 * (size_t)d.workers * R);
   d.bytes = align256(d.off_o + 4 * 2 * (size_t)d.workers * R * mla::kDv);
   return MLA_OK;
@@ -293,9 +296,12 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
                                const int32_t* cache_seqlens, float softmax_scale, void* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream, uint32_t stages) {
   if (!plan) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
-  if (stages == 0 || (stages & ~MLA_STAGE_ALL) != 0)
-    return fail(MLA_ERR_INVALID_ARGUMENT, "stages must be a non-empty subset of MLA_STAGE_ALL");
+  if (stages != MLA_STAGE_COMBINED && (stages == 0 || (stages & ~MLA_STAGE_ALL) != 0))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "stages must be a non-empty subset of MLA_STAGE_ALL, or MLA_STAGE_COMBINED");
   const mla::PlanImpl& p = plan->impl;
+  if (stages == MLA_STAGE_COMBINED && p.rows_per_group != 16)
+    return fail(MLA_ERR_UNSUPPORTED, "MLA_STAGE_COMBINED runs the 16-row kernel (this plan has %d rows per group)",
+                p.rows_per_group);
   if (!q || !kv_cache || !block_table || !cache_seqlens || !out || !workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
   if ((uintptr_t)q % 16 || (uintptr_t)kv_cache % 16 || (uintptr_t)out % 16)
@@ -339,6 +345,14 @@ mla_status_t mla_decode_stages(mla_plan_t plan, const void* q, const void* kv_ca
   a.causal = p.prob.causal;
   a.kv_fp8 = p.prob.kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 0;
   const bool f32 = p.prob.out_dtype == MLA_DTYPE_FP32;
+  if (stages == MLA_STAGE_COMBINED) {
+    if (p.grid == 0) return MLA_OK;
+    a.merge_cnt = (int32_t*)(ws + p.off_cnt);
+    a.seq_merge = (const int32_t*)(ws + p.off_seqm);
+    int e = mla::launch_decode(a, p.rows_per_group, f32, p.grid, stream);
+    if (e) return fail(MLA_ERR_HIP, "combining split-decode launch: %s", mla::hip_error_string(e));
+    return MLA_OK;
+  }
   if ((stages & MLA_STAGE_SPLIT) && p.grid > 0) {
     int e = mla::launch_decode(a, p.rows_per_group, f32, p.grid, stream);
     if (e) return fail(MLA_ERR_HIP, "split-decode launch: %s", mla::hip_error_string(e));
@@ -397,10 +411,11 @@ mla_status_t mla_devplan_prepare(const mla_problem_t* problem, int32_t num_worke
   return MLA_OK;
 }
 
-mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_workers, const void* q,
-                                const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
-                                float softmax_scale, void* out, float* lse, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+namespace {
+mla_status_t devplan_decode(const mla_problem_t* problem, int32_t num_workers, const void* q, const void* kv_cache,
+                            const int32_t* block_table, const int32_t* cache_seqlens, float softmax_scale,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                            bool combined) {
   DevLayout d;
   mla_status_t s = dev_layout(problem, num_workers, d);
   if (s != MLA_OK) return s;
@@ -438,8 +453,10 @@ mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_worker
   a.seq_info = (int32_t*)(ws + d.off_info);
   const int32_t grid = d.row_groups > 1 ? (d.workers + 7) / 8 * 8 * d.row_groups : d.workers;
   const bool f32 = p.out_dtype == MLA_DTYPE_FP32;
+  if (combined) a.merge_cnt = (int32_t*)(ws + d.off_cnt);
   int e = mla::launch_decode(a, 16, f32, grid, stream, true);
   if (e) return fail(MLA_ERR_HIP, "device-scheduled decode launch: %s", mla::hip_error_string(e));
+  if (combined) return MLA_OK;
   mla::MergeArgs m{};
   m.part_lse = a.part_lse;
   m.part_o = a.part_o;
@@ -451,6 +468,23 @@ mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_worker
   e = mla::launch_merge_dev(m, f32, stream);
   if (e) return fail(MLA_ERR_HIP, "device-scheduled merge launch: %s", mla::hip_error_string(e));
   return MLA_OK;
+}
+}  // namespace
+
+mla_status_t mla_decode_devplan(const mla_problem_t* problem, int32_t num_workers, const void* q,
+                                const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+                                float softmax_scale, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return devplan_decode(problem, num_workers, q, kv_cache, block_table, cache_seqlens, softmax_scale, out, lse,
+                        workspace, workspace_bytes, stream, false);
+}
+
+mla_status_t mla_decode_devplan_combined(const mla_problem_t* problem, int32_t num_workers, const void* q,
+                                         const void* kv_cache, const int32_t* block_table,
+                                         const int32_t* cache_seqlens, float softmax_scale, void* out, float* lse,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  return devplan_decode(problem, num_workers, q, kv_cache, block_table, cache_seqlens, softmax_scale, out, lse,
+                        workspace, workspace_bytes, stream, true);
 }
 
 mla_status_t mla_decode_devplan_noalloc(const mla_problem_t* problem, int32_t num_workers, const void* q,

@@ -61,6 +61,7 @@ struct PlanImpl {
   uint64_t plan_id = 0;                    // nonzero, unique per plan in the process
   // workspace layout
   size_t off_worker = 0, off_pieces = 0, off_merges = 0, off_lens = 0, meta_end = 0;
+  size_t off_seqm = 0, off_cnt = 0;        // combining in the decode launch: [B][2] slots, [B][row groups] counters
   size_t off_lse = 0, off_o = 0, ws_bytes = 0;
   std::vector<uint8_t> meta_host;          // bytes [0, meta_end) as uploaded
 };
@@ -108,6 +109,9 @@ struct DecodeArgs {
   int32_t kv_fp8;                // cache rows are 656-byte fp8 rows
   int32_t batch;
   int32_t* seq_info;             // device schedule: per-sequence cut [batch][4] + {T, W}
+  // Combining in the decode launch (16-row kernel): null = a merge launch follows.
+  int32_t* merge_cnt;            // [batch][row_groups] pieces done, zero between calls
+  const int32_t* seq_merge;      // host schedule: [batch][2] first slot and number of pieces
 };
 
 struct MergeArgs {

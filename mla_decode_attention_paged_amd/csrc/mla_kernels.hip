@@ -268,12 +268,146 @@ __device__ __forceinline__ u32x2_t lds_tr16(LDS_AS const uint8_t* p) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)p));
 }
 
+// Log-sum-exp merge of one batch of partial results into a running (M, L, acc): with
+// M' = max(M, l_u), acc and L are scaled by e^(M - M') and each partial u adds
+// w_u = e^(l_u - M') times its o (and w_u to L).  Partials with l = -inf (no tokens) add
+// nothing.
+template <int NB = kMergeBatch>
+__device__ __forceinline__ void merge_batch(const float (&l)[NB], const f32x4_t (&v)[NB], float& M, float& L,
+                                            f32x4_t& acc) {
+  float mb = M;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) mb = fmaxf(mb, l[u]);
+  if (mb == -INFINITY) return;
+  const float f = M > -INFINITY ? __expf(M - mb) : 0.f;
+  L *= f;
+  acc *= f;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const float w = (l[u] > -INFINITY) ? __expf(l[u] - mb) : 0.f;
+    L += w;
+    acc += w * v[u];
+  }
+  M = mb;
+}
+
+// ---- Combining split sequences in the decode launch (one launch instead of two).
+// Each piece's partial result goes out with device-scope stores (write-through past the
+// XCD's L2); once they have completed, the work-group adds one to a device-scope counter of
+// its (sequence, row group).  The one that brings it to the number of pieces resets it and
+// combines every piece's partial, read with device-scope loads, exactly as merge_kernel does.
+// No cache-wide write-back or invalidate is needed: only these stores and loads touch the
+// partials while the launch runs.
+constexpr int kAuxDevice = 16;     // cache policy of buffer loads / stores: sc1 (device scope)
+
+// Slots of the pieces of one sequence: piece 0 in `first`, piece j > 0 in off0 + step j -- host
+// schedule (off0 = first, step 1): first + j; device schedule (off0 = 2 wf, step 2): 2 wf +
+// first_inside, then 2 (wf + j).
+struct Pieces {
+  int32_t first, count, step, off0;
+};
+__device__ __forceinline__ int piece_slot(const Pieces& c, int j) { return j == 0 ? c.first : c.off0 + c.step * j; }
+
+// Buffer resource over slot s's partial rows (R x 512 floats)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const DecodeArgs& a, int s) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.part_o + (int64_t)s * a.rows * kDv, (short)0, a.rows * kDv * 4, 0x00020000);
+}
+
+// Thread (r, c) of 256 combines row 16 rgroup + r, columns 32 c .. 32 c + 31 over the pieces: first
+// the row's max M and sum L of e^(lse - M) from the pieces' lse, then for each 8-column group
+// the weighted sum of kCombineBatch pieces at a time (32 loads in flight per thread: the
+// loads are latency-bound, one work-group reads every piece), then out and lse.
+constexpr int kCombineBatch = 16;
+template <bool OUT_F32>
+__device__ __forceinline__ void combine_rows(const DecodeArgs& a, int b, int rgroup, const Pieces cm) {
+  const int R = a.rows;
+  const int row = 16 * rgroup + (int)(threadIdx.x >> 4);
+  const int c0 = 32 * (int)(threadIdx.x & 15);
+  auto lse_of = [&](int j) {
+    return __hip_atomic_load(a.part_lse + (int64_t)piece_slot(cm, j) * R + row, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // M and L over the pieces, kCombineBatch lse loads in flight at a time
+  float M = -INFINITY, L = 0.f;
+  for (int j0 = 0; j0 < cm.count; j0 += kCombineBatch) {
+    float l[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) l[u] = j0 + u < cm.count ? lse_of(j0 + u) : -INFINITY;
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) mb = fmaxf(mb, l[u]);
+    if (mb == -INFINITY) continue;
+    L = M > -INFINITY ? L * __expf(M - mb) : 0.f;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) L += l[u] > -INFINITY ? __expf(l[u] - mb) : 0.f;
+    M = mb;
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  for (int q = 0; q < 4; ++q) {                    // columns 32 c + 8 q .. + 7
+    const uint32_t off = (uint32_t)(row * kDv + c0 + 8 * q) * 4u;
+    f32x4_t acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    for (int j0 = 0; M > -INFINITY && j0 < cm.count; j0 += kCombineBatch) {
+      f32x4_t v0[kCombineBatch], v1[kCombineBatch];
+      float w[kCombineBatch];
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) {
+        const bool in = j0 + u < cm.count;
+        const int sl = in ? piece_slot(cm, j0 + u) : 0;
+        const __amdgpu_buffer_rsrc_t rs = partial_rsrc(a, sl);
+        v0[u] = in ? __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kAuxDevice))
+                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        v1[u] = in ? __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, kAuxDevice))
+                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const float l = in ? lse_of(j0 + u) : -INFINITY;
+        w[u] = l > -INFINITY ? __expf(l - M) : 0.f;     // pieces without tokens add nothing
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) {
+        acc0 += w[u] * v0[u];
+        acc1 += w[u] * v1[u];
+      }
+    }
+    acc0 *= inv;
+    acc1 *= inv;
+    const int64_t o = ((int64_t)b * R + row) * kDv + c0 + 8 * q;
+    if (OUT_F32) {
+      *(f32x4_t*)((float*)a.out + o) = acc0;
+      *(f32x4_t*)((float*)a.out + o + 4) = acc1;
+    } else {
+      *(u32x4_t*)((uint16_t*)a.out + o) = u32x4_t{bf16x2_rne(acc0[0], acc0[1]), bf16x2_rne(acc0[2], acc0[3]),
+                                                  bf16x2_rne(acc1[0], acc1[1]), bf16x2_rne(acc1[2], acc1[3])};
+    }
+  }
+  if ((threadIdx.x & 15) == 0 && a.lse) a.lse[(int64_t)b * R + row] = L > 0.f ? M + __logf(L) : -INFINITY;
+}
+
+// After a piece's partial is out: count it; the last piece's work-group combines.  `flag`:
+// 4 bytes of LDS not in use (the caller's stages are free between pieces).
+template <bool OUT_F32>
+__device__ __forceinline__ void combine_if_last_t(const DecodeArgs& a, int b, int rgroup, const Pieces cm,
+                                                  LDS_AS int32_t* flag) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): this thread's device-scope stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t* cnt = a.merge_cnt + (int64_t)b * a.row_groups + rgroup;
+    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == cm.count - 1 ? 1 : 0;
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+    *flag = last;
+  }
+  __syncthreads();
+  const bool last = *flag != 0;
+  __syncthreads();
+  if (last) combine_rows<OUT_F32>(a, b, rgroup, cm);
+}
+
 // Split-decode kernel: 16 query rows per work-group (R = 16 * row groups).  FP8: the cache
 // rows are 656-byte fp8 rows (see kF8Row); each wave streams its blocks through three fp8
 // stages and builds the MFMA operands from the codes in registers (see the FP8 loop).
 // DEV: no host schedule; the work-groups cut the batch's blocks among themselves from the
 // device cache_seqlens and combine split sequences in the same launch (see below).
-template <bool OUT_F32, bool FP8, bool DEV>
+// COMB: split sequences are combined in this launch (a.merge_cnt; see combine_if_last_t).
+template <bool OUT_F32, bool FP8, bool DEV, bool COMB>
 __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a) {
   // the stages while blocks stream; the four waves' states (kMergeBytes) when a piece ends
   __shared__ __attribute__((aligned(1024))) uint8_t smem[FP8 ? kSplitSmemFp8 : kSplitSmemBf16];
@@ -718,6 +852,10 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
             pkd[1] = bf16x2_rne(acc[2], acc[3]);
             *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
           }
+        } else if constexpr (COMB) {
+          // device-scope (write-through) store: read back by another work-group in this launch
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc), partial_rsrc(a, slot),
+                                                 (uint32_t)(grow * kDv + d) * 4u, 0, kAuxDevice);
         } else {
           *(f32x4_t*)(a.part_o + ((int64_t)slot * R + grow) * kDv + d) = acc;
         }
@@ -726,6 +864,8 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         const float lse = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
         if (slot < 0) {
           if (a.lse) a.lse[(int64_t)b * R + grow] = lse;
+        } else if constexpr (COMB) {
+          __hip_atomic_store(a.part_lse + (int64_t)slot * R + grow, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
           a.part_lse[(int64_t)slot * R + grow] = lse;
         }
@@ -737,7 +877,16 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   if constexpr (!DEV) {
     const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
     for (int pi = p_begin; pi < p_end; ++pi)
-      run_piece(pieces[4 * pi + 0], pieces[4 * pi + 1], pieces[4 * pi + 2], pieces[4 * pi + 3]);
+    {
+      const int b = pieces[4 * pi + 0], slot = pieces[4 * pi + 3];
+      run_piece(b, pieces[4 * pi + 1], pieces[4 * pi + 2], slot);
+      // combined in this launch: the sequence's slots are seq_merge[b][0] + 0 .. count - 1
+      if (COMB && slot >= 0) {
+        const int first = a.seq_merge[2 * b];
+        combine_if_last_t<OUT_F32>(a, b, rgroup, Pieces{first, a.seq_merge[2 * b + 1], 1, first},
+                                   (LDS_AS int32_t*)smem);
+      }
+    }
     return;
   } else {
     // ---- device schedule.  The batch's 16-token blocks, sequence after sequence, form
@@ -799,6 +948,12 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
         *(int4*)(a.seq_info + 4 * bcur) = info;
       }
       run_piece(bcur, (int)(lo - p0) * kBlock, (int)(hi - p0) * kBlock, slot);
+      if (COMB && slot >= 0) {
+        // the pieces of the sequence: work-groups wf..wl, slots 2w (2 wf + 1 when it begins inside wf's range)
+        const int wf = wpos(p0), wl = wpos(p1 - 1);
+        combine_if_last_t<OUT_F32>(a, bcur, rgroup, Pieces{2 * wf + (p0 > wstart(wf) ? 1 : 0), wl - wf + 1, 2, 2 * wf},
+                                   (LDS_AS int32_t*)smem);
+      }
     }
     if (worker == 0 && rgroup == 0 && threadIdx.x == 0) {
       a.seq_info[4 * B + 0] = (int32_t)T;                 // schedule header: T and W
@@ -1898,27 +2053,6 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
   }
 }
 
-// Log-sum-exp merge of one batch of partial results into a running (M, L, acc): with
-// M' = max(M, l_u), acc and L are scaled by e^(M - M') and each partial u adds
-// w_u = e^(l_u - M') times its o (and w_u to L).  Partials with l = -inf (no tokens) add
-// nothing.
-__device__ __forceinline__ void merge_batch(const float (&l)[kMergeBatch], const f32x4_t (&v)[kMergeBatch],
-                                            float& M, float& L, f32x4_t& acc) {
-  float mb = M;
-#pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, l[u]);
-  if (mb == -INFINITY) return;
-  const float f = M > -INFINITY ? __expf(M - mb) : 0.f;
-  L *= f;
-  acc *= f;
-#pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) {
-    const float w = (l[u] > -INFINITY) ? __expf(l[u] - mb) : 0.f;
-    L += w;
-    acc += w * v[u];
-  }
-  M = mb;
-}
 
 // Merge of split sequences.  One work-group per (sequence, 16 query rows, 64
 // output columns): thread (r, q) merges row r, columns 4q..4q+3 of the slice over
@@ -2042,19 +2176,27 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* kv, const in
 }
 
 
-template <bool DEV>
-void launch_split(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
+template <bool DEV, bool COMB>
+void launch_split_t(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
   if (a.kv_fp8) {
     if (out_fp32)
-      hipLaunchKernelGGL((split_decode_kernel<true, true, DEV>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split_decode_kernel<true, true, DEV, COMB>), dim3(grid), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((split_decode_kernel<false, true, DEV>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split_decode_kernel<false, true, DEV, COMB>), dim3(grid), dim3(kThreads), 0, s, a);
   } else {
     if (out_fp32)
-      hipLaunchKernelGGL((split_decode_kernel<true, false, DEV>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split_decode_kernel<true, false, DEV, COMB>), dim3(grid), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((split_decode_kernel<false, false, DEV>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split_decode_kernel<false, false, DEV, COMB>), dim3(grid), dim3(kThreads), 0, s, a);
   }
+}
+// a.merge_cnt set: the launch combines split sequences itself (no merge launch follows)
+template <bool DEV>
+void launch_split(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
+  if (a.merge_cnt)
+    launch_split_t<DEV, true>(a, out_fp32, grid, s);
+  else
+    launch_split_t<DEV, false>(a, out_fp32, grid, s);
 }
 
 // The wide kernel: non-temporal KV loads when one row group reads each token range

@@ -185,7 +185,12 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
   pl.off_pieces = align_up(pl.off_worker + 4 * pl.worker_off.size(), 16);
   pl.off_merges = align_up(pl.off_pieces + sizeof(Piece) * pl.pieces.size(), 16);
   pl.off_lens = align_up(pl.off_merges + sizeof(MergeItem) * pl.merges.size(), 16);
-  pl.meta_end = align_up(pl.off_lens + 4 * (size_t)B, 256);
+  // combining in the decode launch: each sequence's first slot and number of pieces (0 when it
+  // is not split), and one counter per (sequence, row group), uploaded as zeros; the kernel
+  // leaves every counter at zero when its launch ends
+  pl.off_seqm = align_up(pl.off_lens + 4 * (size_t)B, 16);
+  pl.off_cnt = align_up(pl.off_seqm + 8 * (size_t)B, 16);
+  pl.meta_end = align_up(pl.off_cnt + 4 * (size_t)B * pl.row_groups, 256);
   pl.off_lse = pl.meta_end;
   pl.off_o = align_up(pl.off_lse + 4 * (size_t)pl.num_partials * R, 256);
   pl.ws_bytes = align_up(pl.off_o + 4 * (size_t)pl.num_partials * R * kDv, 256);
@@ -199,6 +204,14 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
     std::memcpy(pl.meta_host.data() + pl.off_pieces, pl.pieces.data(), sizeof(Piece) * pl.pieces.size());
   if (!pl.merges.empty())
     std::memcpy(pl.meta_host.data() + pl.off_merges, pl.merges.data(), sizeof(MergeItem) * pl.merges.size());
+  {
+    std::vector<int32_t> seqm(2 * (size_t)B, 0);
+    for (const MergeItem& mi : pl.merges) {
+      seqm[2 * (size_t)mi.seq] = mi.slot_begin;
+      seqm[2 * (size_t)mi.seq + 1] = mi.num_slots;
+    }
+    std::memcpy(pl.meta_host.data() + pl.off_seqm, seqm.data(), 8 * (size_t)B);
+  }
   (void)err;
   return MLA_OK;
 }

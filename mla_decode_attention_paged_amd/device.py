@@ -58,10 +58,11 @@ class Runner:
 
 
 class DevplanRunner:
-    """Device-scheduled decode (mla_decode_devplan) for one problem: no host plan; the
-    device cache_seqlens may be rewritten between calls."""
+    """Device-scheduled decode (mla_decode_devplan, or mla_decode_devplan_combined with
+    combined=True) for one problem: no host plan; the device cache_seqlens may be rewritten
+    between calls."""
 
-    def __init__(self, prob, dev=None, num_workers=0, device="cuda", causal=False):
+    def __init__(self, prob, dev=None, num_workers=0, device="cuda", causal=False, combined=False):
         import torch
         self.prob = prob
         self.dev = dev if dev is not None else to_device(prob, device)
@@ -76,7 +77,8 @@ class DevplanRunner:
         self.lse = torch.empty((prob.batch, prob.q_len, prob.num_heads), dtype=torch.float32, device=device)
         d = self.dev
         self._bound = B.BoundDevplanDecode(self.problem, num_workers, d["q"], d["kv_cache"], d["block_table"],
-                                           d["cache_seqlens"], prob.softmax_scale, self.out, self.lse, self.ws)
+                                           d["cache_seqlens"], prob.softmax_scale, self.out, self.lse, self.ws,
+                                           combined=combined)
 
     def __call__(self, stream=None):
         import torch

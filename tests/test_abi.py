@@ -23,7 +23,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) >= 12
     for n in names:
         assert hasattr(lib, n), f"libmla.so does not export {n}"
-    assert B.abi_version() == 6
+    assert B.abi_version() == 7
 
 
 def test_status_strings():
@@ -111,7 +111,13 @@ def test_decode_validation_happens_before_any_launch():
     assert call(wsb=ws_bytes - 1) == B.MLA_ERR_WORKSPACE_TOO_SMALL
     assert call(scale=float("nan")) == B.MLA_ERR_INVALID_ARGUMENT
     assert call(stages=0) == B.MLA_ERR_INVALID_ARGUMENT
-    assert call(stages=4) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(stages=8) == B.MLA_ERR_INVALID_ARGUMENT
+    assert call(stages=B.MLA_STAGE_COMBINED | B.MLA_STAGE_SPLIT) == B.MLA_ERR_INVALID_ARGUMENT
+    # the combining launch runs the 16-row kernel only: refused for a 128-row plan before anything else
+    wide = B.Plan(B.make_problem(2, 1, 128, 64, 16, 8), [300, 500], num_cus=256)
+    assert wide.info()["rows_per_group"] == 128
+    assert lib.mla_decode_stages(wide.handle, fake, fake, fake, fake, 0.1, fake, fake, fake, wide.workspace_bytes,
+                                 None, B.MLA_STAGE_COMBINED) == B.MLA_ERR_UNSUPPORTED
     assert lib.mla_decode(None, fake, fake, fake, fake, 0.1, fake, fake, fake, ws_bytes, None) == \
         B.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_plan_upload(h, None, ws_bytes, None) == B.MLA_ERR_INVALID_ARGUMENT
