@@ -106,11 +106,13 @@ typedef struct {
   int32_t force_splits;       /* 0 = cost model; k > 0 = cut every sequence into min(k, blocks)
                                  near-equal parts, one work-group each (testing the merge) */
   int32_t rows_per_group;     /* 0 = automatic (128 when R is a multiple of 128; else, with a bf16
-                                 cache, 64 when R is a multiple of 64; else 16);
+                                 cache, 64 when R is a multiple of 64, else 32 when R is a multiple
+                                 of 32; else 16);
                                  16, 32, 64 or 128 = query rows per work-group (16: the 16-row
-                                 kernel in R/16 row groups; 32, 64: the grouped kernel, bf16 cache
-                                 only; 128: the wide kernel, 32 rows per wave on 32x32 MFMA tiles,
-                                 bf16 or FP8 rows; R must be a multiple) -- a tuning and testing knob */
+                                 kernel in R/16 row groups; 32: the 32-row kernel and 64: the
+                                 grouped kernel, bf16 cache only; 128: the wide kernel, 32 rows per
+                                 wave on 32x32 MFMA tiles, bf16 or FP8 rows; R must be a multiple)
+                                 -- a tuning and testing knob */
   int32_t reserved[5];        /* must be zero */
 } mla_plan_options_t;
 

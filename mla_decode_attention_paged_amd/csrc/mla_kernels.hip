@@ -2054,6 +2054,404 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
 }
 
 
+// ---------------------------------------------------------------------------------------------
+// 32-row split-decode kernel (R = 32 per work-group, two-token queries over 16 heads): the token
+// split of the 16-row kernel -- each wave takes blocks w, w + 4, ... of the piece through two
+// LDS stages of its own -- with all 32 query rows in every wave, so one work-group reads each KV
+// row once for 32 rows (two 16-row work-groups read it twice, the second time from L2).
+//   S^T = K Q^T     two 16x16x32 tiles (rows 0..15, 16..31) sharing each K operand: 36 MFMAs
+//   P^T             per tile exp2(s - m), moved into the 32x32x16 B-operand layout with one
+//                   v_permlane16_swap per dword (lane (i, h): row i, tokens 8h .. 8h + 7)
+//   O^T += V^T P^T  M = 32 columns, N = 32 rows, K = 16 tokens: 16 MFMAs (32 with fp32 output);
+//                   O^T (512 x 32) fills the 256 accumulation registers
+// The query's first 10 k-steps stay in VGPRs; its last 8 (192 latent and the 64 rope columns, the
+// same for every wave) sit in the 16 KB of LDS beside the stages.  K and V^T operands stream
+// through small register rings; a wave's stage is refilled with its block after next when the
+// block's last V^T read has been issued.  Weights are taken against a per-row reference without
+// rescaling (as in the 128-row kernel; a wave whose scores leave the slack runs its blocks again).
+// When a piece ends the four waves' states are combined through LDS, 16 rows at a time.
+// S^T steps on a 16x16x32 bf16 MFMA with the accumulator in VGPRs (O^T holds all 256
+// accumulation registers): acc = a b, acc += a b, and the last step with 16 wait states so
+// that vector instructions may read acc right after it.
+__device__ __forceinline__ void mfma16_vfirst(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_vacc(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_vlast(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+constexpr int k32QReg = 10;                              // query k-steps in VGPRs
+#ifndef MLA_K32_WAVES
+#define MLA_K32_WAVES 2
+#endif
+constexpr int k32Waves = MLA_K32_WAVES;                  // waves per work-group
+constexpr int k32QLds = kSmemBytes;                      // after the 4 x 2 stages: [8 k-steps][2 tiles][64 lanes] x 16 B
+constexpr int k32Smem = k32QLds + (kKSteps - k32QReg) * 2 * 1024;   // 163,840: all of the LDS
+
+// NW waves per work-group (2 or 4) share the 8 block stages: 8 / NW each, so a wave has
+// 8 / NW - 1 blocks in flight while it computes one.
+template <bool OUT_F32, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) split32_decode_kernel(DecodeArgs a) {
+  static_assert(NW == 2 || NW == 4, "2 or 4 waves");
+  constexpr int SPW = 2 * kWaves / NW;             // stages per wave
+  constexpr int NT = 64 * NW;                      // threads
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[k32Smem];
+  LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;          // S^T tile layout: row n of the tile, tokens 4g .. 4g + 3
+  int worker, rgroup;
+  if (a.row_groups == 1) {
+    worker = blockIdx.x;
+    rgroup = 0;
+  } else {
+    // the row groups of one token range land on the same XCD (ids are dealt round-robin to 8 XCDs)
+    const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+    rgroup = y % a.row_groups;
+    worker = (y / a.row_groups) * 8 + x;
+  }
+  if (worker >= a.num_workers) return;
+  if (!schedule_matches(a)) return;
+  const int R = a.rows;
+  const int row0 = 32 * rgroup;                    // this work-group's 32 query rows
+  const bool stream = a.row_groups == 1;           // KV loads: non-temporal when no other row group re-reads
+
+  // Block layout (as the 16-row kernel): chunk c of token t at 2048 (c / 8) + 128 t + 16 ((c % 8) ^ row_swz(t)).
+  // K, k-step kk: token n, chunk 4 kk + g.
+  const int k_even = 128 * n + 16 * (g ^ row_swz(n));
+  const int k_odd = k_even ^ 64;
+  // V^T, 32-column tile cc, part jp: lane 4e + qq of 16-lane group g reads token 8 (g / 2) + 4 jp + e,
+  // columns 32 cc + 16 (g % 2) + 4 qq .. + 3 (chunk 4 cc + 2 (g % 2) + qq / 2, 8 B); the transpose
+  // hands lane (i, h) column 32 cc + i of tokens 8 h + 4 jp + 0 .. 3.
+  int v_off[2][2];       // [cc % 2][jp]; + 2048 (cc / 2)
+  {
+    const int e = n >> 2, qq = n & 3;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+        const int t = 8 * (g >> 1) + 4 * jp + e;
+        const int c = 4 * par + 2 * (g & 1) + (qq >> 1);
+        v_off[par][jp] = 128 * t + 16 * (c ^ row_swz(t)) + 8 * (qq & 1);
+      }
+  }
+  const int ld_tok0 = lane >> 3, ld_tok1 = 8 + (lane >> 3);
+  const int ld_col0 = 8 * ((lane & 7) ^ row_swz(ld_tok0)), ld_col1 = 8 * ((lane & 7) ^ row_swz(ld_tok1));
+  LDS_AS uint8_t* const stages = lds + wave * SPW * kBlockBytes;   // this wave's SPW stages
+  LDS_AS uint8_t* const qlds = lds + k32QLds + 16 * lane;      // + 1024 (2 (kk - k32QReg) + tile)
+
+  const CST_AS int32_t* worker_off = as_const(a.worker_off);
+  const CST_AS int32_t* pieces = as_const(a.pieces);
+  const CST_AS int32_t* seqlens = as_const(a.seqlens);
+  const CST_AS int32_t* block_table = as_const(a.block_table);
+
+  const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
+  for (int pi = p_begin; pi < p_end; ++pi) {
+    const int b = pieces[4 * pi + 0], tb = pieces[4 * pi + 1], slot = pieces[4 * pi + 3];
+    check_planned_length(a, b, pieces[4 * pi + 2], seqlens[b]);
+    const int L = seqlens[b];
+    const int te = min(pieces[4 * pi + 2], L);
+    const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
+    // the tokens row 16 t + n sees (causal: the first L - (q_len - 1 - row / num_heads))
+    int lim[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) lim[t] = a.causal ? min(te, L - (a.q_len - 1 - (row0 + 16 * t + n) / a.num_heads)) : te;
+    const int my_n = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;
+    auto blk_of = [&](int k) { return wave + NW * k; };
+
+    // query rows as B operands: lane (n, g) holds row 16 t + n, columns 32 kk + 8 g .. + 7; k-steps
+    // below k32QReg in VGPRs, the others in LDS (wave w writes k-steps k32QReg + (8 / NW) w ..;
+    // every wave reads all of them after the barrier below)
+    bf16x8_t qf[2][k32QReg];
+    {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint16_t* qrow = a.q + ((int64_t)b * R + row0 + 16 * t + n) * kDqk + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < k32QReg; ++kk) qf[t][kk] = *(const bf16x8_t*)(qrow + 32 * kk);
+#pragma unroll
+        for (int j = 0; j < (kKSteps - k32QReg) / NW; ++j) {
+          const int kk = k32QReg + (kKSteps - k32QReg) / NW * wave + j;
+          *(LDS_AS u32x4_t*)(qlds + 1024 * (2 * (kk - k32QReg) + t)) = *(const u32x4_t*)(qrow + 32 * kk);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0): the query loads (a wait the compiler sees)
+    }
+    __syncthreads();
+
+    float m_ref[2], lsum[2];                 // reference max per tile row (log2 units); this lane's share of sum p
+    float m_run[2] = {-INFINITY, -INFINITY}; // the row's largest scaled score so far
+    bool bad_page = false;                   // a block of this wave read an out-of-range table entry
+    f32x16_t o[16];
+
+    struct Src {
+      const uint8_t* row0;
+      uint32_t vo[2];
+    };
+    auto source = [&](int k, bool& ok) -> Src {
+      const int tok0 = tb + kBlock * blk_of(k);
+      int64_t base = kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok0);
+      ok = base >= 0;
+      if (!ok) base = 0;
+      const int last = te - 1 - tok0;
+      Src r{};
+      r.row0 = (const uint8_t*)(a.kv + base * kDqk);
+      r.vo[0] = (uint32_t)(min(ld_tok0, last) * kRowBytesBf16 + 2 * ld_col0);
+      r.vo[1] = (uint32_t)(min(ld_tok1, last) * kRowBytesBf16 + 2 * ld_col1);
+      return r;
+    };
+    auto issue = [&](const Src& src, LDS_AS uint8_t* stage) {
+      const uint32_t l = (uint32_t)(uintptr_t)stage;
+      if (stream)
+        dma_bf16_block<true>(src.row0, src.vo[0], src.vo[1], l);
+      else
+        dma_bf16_block<false>(src.row0, src.vo[0], src.vo[1], l);
+    };
+    // P^T for the 32x32x16 MFMA from the tiles' weights (lane (n, g): row 16 t + n, tokens
+    // 4g .. 4g + 3, packed as two bf16x2 words): one permlane16_swap per word gives lane (i, h)
+    // the words of row i, tokens 8h .. 8h + 3 (first) and 8h + 4 .. 8h + 7 (second).
+    auto pt_operand = [&](const uint32_t (&w0)[2], const uint32_t (&w1)[2]) -> bf16x8_t {
+      const auto s0 = __builtin_amdgcn_permlane16_swap(w0[0], w1[0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(w0[1], w1[1], false, false);
+      return __builtin_bit_cast(bf16x8_t, u32x4_t{s0[0], s1[0], s0[1], s1[1]});
+    };
+    // O^T += V^T P^T with p = exp2(s - m_ref); fp32 output: p as bf16 hi + lo, two MFMAs per tile.
+    // The V^T operands of stage st stream through a ring of three, each read three MFMAs ahead.
+    auto vload = [&](LDS_AS const uint8_t* st, int cc) -> bf16x8_t {
+      const u32x2_t v0 = lds_tr16(st + 2048 * (cc >> 1) + v_off[cc & 1][0]);
+      const u32x2_t v1 = lds_tr16(st + 2048 * (cc >> 1) + v_off[cc & 1][1]);
+      return __builtin_bit_cast(bf16x8_t, u32x4_t{v0[0], v0[1], v1[0], v1[1]});
+    };
+    auto accumulate = [&](const float (&s)[2][4], LDS_AS const uint8_t* st) {
+      uint32_t hw[2][2], lw[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float p[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          p[q] = __builtin_amdgcn_exp2f(s[t][q] - m_ref[t]);
+          lsum[t] += p[q];
+        }
+        const u32x4_t hl = split_hi_lo(p[0], p[1], p[2], p[3]);
+        hw[t][0] = hl[0];
+        hw[t][1] = hl[1];
+        lw[t][0] = hl[2];
+        lw[t][1] = hl[3];
+      }
+      const bf16x8_t ph = pt_operand(hw[0], hw[1]);
+      bf16x8_t pl;
+      if constexpr (OUT_F32) pl = pt_operand(lw[0], lw[1]);
+      constexpr int kVRing = 3;
+      bf16x8_t vr[kVRing];
+#pragma unroll
+      for (int j = 0; j < kVRing; ++j) vr[j] = vload(st, j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc) {
+        const bf16x8_t vv = vr[cc % kVRing];
+        if (cc + kVRing < 16) vr[cc % kVRing] = vload(st, cc + kVRing);
+        o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, ph, o[cc], 0, 0, 0);
+        if constexpr (OUT_F32) o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pl, o[cc], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // Weights without rescaling (as the 128-row kernel): each row's reference is the maximum of
+    // this wave's first block; a wave whose later scores exceed it by more than kWSlack runs its
+    // blocks again with the true maximum, so the accumulators are only ever touched by MFMAs.
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) o[c][q] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        m_ref[t] = pass ? fmaxf(m_run[t], kNegBig) : kNegBig;
+        lsum[t] = 0.f;
+      }
+      bool have_ref = pass > 0, ovf = false;
+      uint32_t okq = 0;              // bit s: the table entry of the block now in stage s was in range
+#pragma unroll
+      for (int s0 = 0; s0 < SPW; ++s0) {
+        bool ok = true;
+        if (s0 < my_n) issue(source(s0, ok), stages + s0 * kBlockBytes);
+        okq |= (ok ? 1u : 0u) << s0;
+      }
+      for (int k = 0; k < my_n; ++k) {
+        const int sl = k % SPW;
+        LDS_AS uint8_t* st = stages + sl * kBlockBytes;
+        bool nok = true;
+        const bool nx = k + SPW < my_n;
+        Src nsrc{};
+        if (nx) nsrc = source(k + SPW, nok);
+        // block k has landed once at most the loads of the blocks after it are in flight
+        const int after = min(SPW - 1, my_n - 1 - k);
+        if (after >= 3)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kLoadsPerBlock) : "memory");
+        else if (after == 2)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kLoadsPerBlock) : "memory");
+        else if (after == 1)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerBlock) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const bool ok = (okq >> sl) & 1u;
+        okq = (okq & ~(1u << sl)) | ((nok ? 1u : 0u) << sl);   // the stage's next occupant
+        if (!ok) {
+          // out-of-range table entry: the block read page 0; it takes the same path with its rows
+          // zeroed (V enters the products) and every score masked, so the accumulators keep one
+          // definition per step
+          bad_page = true;
+#pragma unroll
+          for (int u = 0; u < kBlockBytes / 1024; ++u)
+            *(LDS_AS u32x4_t*)(st + 1024 * u + 16 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+        }
+        // S^T with the K operands streamed
+        f32x4_t sacc[2];
+        {
+          auto kload = [&](int kk) -> bf16x8_t {
+            return __builtin_bit_cast(bf16x8_t, lds_ld128(st + ((kk & 1) ? k_odd : k_even) + 2048 * (kk >> 1)));
+          };
+          // the query operands in LDS are the same for every block: an address the compiler cannot
+          // see through keeps it from hoisting their loads out of the block loop (into registers)
+          uint32_t qa = (uint32_t)(uintptr_t)qlds;
+          asm volatile("" : "+v"(qa));
+          LDS_AS const uint8_t* const qb = (LDS_AS const uint8_t*)(uintptr_t)qa;
+          auto qload = [&](int kk, int t) -> bf16x8_t {
+            return __builtin_bit_cast(bf16x8_t, lds_ld128(qb + 1024 * (2 * (kk - k32QReg) + t)));
+          };
+          constexpr int kRing = 4;
+          bf16x8_t kr[kRing], qr[2][2];        // K: kRing steps ahead; LDS query operands: two steps ahead
+#pragma unroll
+          for (int j = 0; j < kRing; ++j) kr[j] = kload(j);
+#pragma unroll
+          for (int kk = 0; kk < kKSteps; ++kk) {
+            const bf16x8_t kv = kr[kk % kRing];
+            if (kk + kRing < kKSteps) kr[kk % kRing] = kload(kk + kRing);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const bf16x8_t qv = kk < k32QReg ? qf[t][kk < k32QReg ? kk : 0] : qr[kk & 1][t];
+              if (kk == 0)
+                mfma16_vfirst(sacc[t], kv, qv);
+              else if (kk == kKSteps - 1)
+                mfma16_vlast(sacc[t], kv, qv);
+              else
+                mfma16_vacc(sacc[t], kv, qv);
+            }
+            if (kk + 2 >= k32QReg && kk + 2 < kKSteps) {     // (after this step's use of the slot)
+#pragma unroll
+              for (int t = 0; t < 2; ++t) qr[kk & 1][t] = qload(kk + 2, t);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        const int tok0 = tb + kBlock * blk_of(k);
+        float sc[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int nvalid = ok ? lim[t] - tok0 : 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sc[t][q] = (4 * g + q < nvalid) ? sacc[t][q] * a.scale_log2 : -INFINITY;
+          const float mx = wave_max_over_groups(fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
+          m_run[t] = fmaxf(m_run[t], mx);
+          if (!have_ref) m_ref[t] = fmaxf(mx, kNegBig);
+          ovf |= mx > m_ref[t] + kWSlack;
+        }
+        have_ref = true;
+        accumulate(sc, st);
+        if (nx) issue(nsrc, st);        // every read of the stage has been issued (the load waits for them)
+      }
+      if (pass > 0 || !__any(ovf)) break;
+    }
+
+    if (bad_page && lane == 0)
+      __hip_atomic_fetch_or(a.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- combine the waves' states and write.  NW / 2 rounds through LDS: waves 2 r, 2 r + 1
+    // write all 32 rows (so that every wave reads its accumulators once), then thread (row
+    // tid / SEG, columns 4 (tid % SEG) + 4 SEG j) folds them into its running sum.
+    const int i = lane & 31;
+    float m_o, l_o;                        // this lane's O^T row i: its reference and weight sum
+    {
+      const float l0 = wave_sum_over_groups(lsum[0]), l1 = wave_sum_over_groups(lsum[1]);
+      const float ma = __shfl(m_ref[0], i & 15), mb = __shfl(m_ref[1], i & 15);
+      const float la = __shfl(l0, i & 15), lb = __shfl(l1, i & 15);
+      m_o = i < 16 ? ma : mb;
+      l_o = i < 16 ? la : lb;
+    }
+    __syncthreads();   // stages no longer read
+    LDS_AS float* buf = (LDS_AS float*)smem;                     // [2 waves][32 rows][516]
+    LDS_AS float* sm_m = buf + 2 * 32 * kMergeStride;            // [2][32]
+    LDS_AS float* sm_l = sm_m + 64;                              // [2][32]
+    constexpr int SEG = NT / 32;                 // threads per row
+    constexpr int NCOL = kDv / (4 * SEG);        // float4 columns per thread
+    const int r = threadIdx.x / SEG, seg = threadIdx.x % SEG;
+    f32x4_t acc[NCOL];
+    float M = kNegBig, Ls = 0.f;
+#pragma unroll
+    for (int round = 0; round < NW / 2; ++round) {
+      if ((wave >> 1) == round) {
+        const int w2 = wave & 1;
+        if (lane < 32) {
+          sm_m[32 * w2 + i] = m_o;
+          sm_l[32 * w2 + i] = l_o;
+        }
+        // lane (i, h): row i, columns 32 cc + 8 jj + 4 h + 0..3 in o[cc][4 jj + 0..3]
+        LDS_AS float* my = buf + (32 * w2 + i) * kMergeStride + 4 * (lane >> 5);
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            *(LDS_AS f32x4_t*)(my + 32 * cc + 8 * jj) = f32x4_t{o[cc][4 * jj], o[cc][4 * jj + 1], o[cc][4 * jj + 2], o[cc][4 * jj + 3]};
+          __builtin_amdgcn_sched_barrier(0);   // one tile at a time out of the accumulators
+        }
+      }
+      __syncthreads();
+      const float m0 = sm_m[r], m1 = sm_m[32 + r];
+      const float Mn = fmaxf(M, fmaxf(m0, m1));
+      const float fa = M <= kNegBig ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      const float f0 = m0 <= kNegBig ? 0.f : __builtin_amdgcn_exp2f(m0 - Mn);
+      const float f1 = m1 <= kNegBig ? 0.f : __builtin_amdgcn_exp2f(m1 - Mn);
+      Ls = Ls * fa + f0 * sm_l[r] + f1 * sm_l[32 + r];
+#pragma unroll
+      for (int j = 0; j < NCOL; ++j) {
+        const int d = 4 * seg + 4 * SEG * j;
+        const f32x4_t x0 = *(LDS_AS const f32x4_t*)(buf + r * kMergeStride + d);
+        const f32x4_t x1 = *(LDS_AS const f32x4_t*)(buf + (32 + r) * kMergeStride + d);
+        acc[j] = round == 0 ? f0 * x0 + f1 * x1 : acc[j] * fa + f0 * x0 + f1 * x1;
+      }
+      M = Mn;
+      __syncthreads();
+    }
+    const float inv = Ls > 0.f ? 1.0f / Ls : 0.f;
+#pragma unroll
+    for (int j = 0; j < NCOL; ++j) {
+      const int d = 4 * seg + 4 * SEG * j;
+      const f32x4_t v = acc[j] * inv;
+      if (slot < 0) {
+        const int64_t off = ((int64_t)b * R + row0 + r) * kDv + d;
+        if (OUT_F32) {
+          *(f32x4_t*)((float*)a.out + off) = v;
+        } else {
+          *(u32x2_t*)((uint16_t*)a.out + off) = u32x2_t{bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+        }
+      } else {
+        *(f32x4_t*)(a.part_o + ((int64_t)slot * R + row0 + r) * kDv + d) = v;
+      }
+    }
+    if (seg == 0) {
+      const float lse = Ls > 0.f ? (M + __log2f(Ls)) * 0.69314718055994530942f : -INFINITY;
+      if (slot < 0) {
+        if (a.lse) a.lse[(int64_t)b * R + row0 + r] = lse;
+      } else {
+        a.part_lse[(int64_t)slot * R + row0 + r] = lse;
+      }
+    }
+  }
+}
+
 // Merge of split sequences.  One work-group per (sequence, 16 query rows, 64
 // output columns): thread (r, q) merges row r, columns 4q..4q+3 of the slice over
 // all of the sequence's partial results, so every partial byte is read once and
@@ -2282,9 +2680,9 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
     launch_split<false>(a, out_fp32, grid, s);
   } else if (rows_per_group == 32) {
     if (out_fp32)
-      hipLaunchKernelGGL((group_decode_kernel<2, true, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split32_decode_kernel<true, k32Waves>), dim3(grid), dim3(64 * k32Waves), 0, s, a);
     else
-      hipLaunchKernelGGL((group_decode_kernel<2, false, true>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((split32_decode_kernel<false, k32Waves>), dim3(grid), dim3(64 * k32Waves), 0, s, a);
   } else if (rows_per_group == 64) {
     if (out_fp32)
       hipLaunchKernelGGL((group_decode_kernel<4, true, false>), dim3(grid), dim3(kThreads), 0, s, a);

@@ -66,8 +66,8 @@ def test_plan_covers_every_token_once(name):
         plan = make_plan(lens, heads=heads, q_len=q_len)
         seg, off, info = check_plan(plan, lens)
         R = heads * q_len
-        # bf16 cache: 128 rows per work-group when they fit, else 64, else 16
-        assert info["rows_per_group"] == (128 if R % 128 == 0 else 64 if R % 64 == 0 else 16)
+        # bf16 cache: 128 rows per work-group when they fit, else 64, else 32, else 16
+        assert info["rows_per_group"] == (128 if R % 128 == 0 else 64 if R % 64 == 0 else 32 if R % 32 == 0 else 16)
         assert info["row_groups"] == R // info["rows_per_group"]
         workers = 256 // info["row_groups"]
         assert info["num_workers"] <= max(1, workers)
@@ -152,10 +152,11 @@ def test_rows_per_group_rejected():
 
 def test_default_rows_per_group():
     """128 rows per work-group when R is a multiple of 128; else, with a bf16 cache, 64 when R is a
-    multiple of 64; else 16."""
-    for heads, q_len, kv, want in [(16, 1, 0, 16), (16, 2, 0, 16), (48, 1, 0, 16), (64, 1, 0, 64), (128, 1, 0, 128),
+    multiple of 64, else 32 when R is a multiple of 32; else 16."""
+    for heads, q_len, kv, want in [(16, 1, 0, 16), (16, 2, 0, 32), (48, 1, 0, 16), (64, 1, 0, 64), (128, 1, 0, 128),
                                    (32, 2, 0, 64), (64, 1, 1, 16), (128, 1, 1, 128), (128, 2, 0, 128), (128, 2, 1, 128),
-                                   (64, 2, 0, 128), (64, 2, 1, 128), (96, 2, 0, 64), (96, 2, 1, 16)]:
+                                   (64, 2, 0, 128), (64, 2, 1, 128), (96, 2, 0, 64), (96, 2, 1, 16), (16, 2, 1, 16),
+                                   (32, 1, 0, 32), (48, 2, 0, 32), (8, 4, 0, 32)]:
         prob = B.make_problem(1, q_len, heads, 64, 1, 1, kv_fp8=bool(kv))
         info = B.Plan(prob, [10], num_cus=256).info()
         assert info["rows_per_group"] == want, (heads, q_len, kv, info["rows_per_group"])
