@@ -2459,7 +2459,12 @@ __global__ void __launch_bounds__(64 * NW, 1) split32_decode_kernel(DecodeArgs a
 constexpr int kMergeCols = 64;
 template <bool OUT_F32>
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
-  if (*as_const(a.ws_plan_id) != a.plan_id) return;   // another plan's schedule: the split launch flagged it
+  // The plan id in the workspace is read alongside the first loads rather than before them:
+  // the workspace is at least this plan's size (the host checks it), so the merge table and,
+  // with the uniform layout, the partials are in bounds whatever schedule it holds.  Table
+  // entries are used as addresses, and anything is stored, only once the id matches (another
+  // plan's schedule: the split launch flagged it).
+  const uint64_t pid = *as_const(a.ws_plan_id);
   const int R = a.rows;
   const int col_groups = kDv / kMergeCols;
   const int per_item = (R / 16) * col_groups;
@@ -2476,6 +2481,8 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     b = merges[4 * item + 0];
     s0 = merges[4 * item + 1];
     ns = merges[4 * item + 2];
+    asm volatile("" ::"s"(b), "s"(s0), "s"(ns));    // the table reads go out with the id's
+    if (pid != a.plan_id) return;
   }
   const int r = rg * 16 + (threadIdx.x >> 4);
   const int d = cg * kMergeCols + 4 * (threadIdx.x & 15);
@@ -2496,6 +2503,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
     }
     merge_batch(l, v, M, L, acc);
   }
+  if (pid != a.plan_id) return;
   const f32x4_t v = acc * (L > 0.f ? 1.0f / L : 0.f);
   const int64_t off = ((int64_t)b * R + r) * kDv + d;
   if (OUT_F32) {
@@ -2597,10 +2605,13 @@ void launch_split(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
     launch_split_t<DEV, false>(a, out_fp32, grid, s);
 }
 
-// The wide kernel: non-temporal KV loads when one row group reads each token range
+// The wide kernel: non-temporal KV loads when one row group reads each token range and the rows
+// are bf16.  FP8 rows (656 B) are not 64-B aligned and each wave gathers its octet by region, so
+// neighbouring loads share cache lines; with non-temporal loads those lines left the L2 between
+// the two loads and were fetched twice (6% more HBM bytes on the ragged 128-head workload).
 template <bool FP8>
 void launch_wide_t(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
-  const bool nt = a.row_groups == 1;
+  const bool nt = a.row_groups == 1 && !FP8;
   if (out_fp32) {
     if (nt)
       hipLaunchKernelGGL((wide_decode_kernel<true, true, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
