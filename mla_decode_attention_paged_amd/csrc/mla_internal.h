@@ -56,6 +56,7 @@ struct PlanImpl {
   std::vector<Piece> pieces;
   std::vector<MergeItem> merges;
   int32_t merge_uniform = 0;               // ns when item b merges slots [b*ns, (b+1)*ns) for every b
+  int32_t merge_max_ns = 0;                // the largest number of pieces of a merged sequence
   std::vector<int64_t> worker_cost;
   int32_t num_partials = 0;
   uint64_t plan_id = 0;                    // nonzero, unique per plan in the process
@@ -125,6 +126,7 @@ struct MergeArgs {
   int32_t rows;
   int32_t num_merges;
   int32_t uniform_ns;            // > 0: item i is sequence i with slots [i*ns, (i+1)*ns)
+  int32_t max_ns;                // the largest piece count of a merged sequence (batch size)
   const int32_t* seq_info;       // device schedule (merge_dev_kernel)
   int32_t batch;
 };

@@ -2457,7 +2457,7 @@ __global__ void __launch_bounds__(64 * NW, 1) split32_decode_kernel(DecodeArgs a
 // all of the sequence's partial results, so every partial byte is read once and
 // all loads of a thread are independent.
 constexpr int kMergeCols = 64;
-template <bool OUT_F32>
+template <bool OUT_F32, int NB>
 __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   // The plan id in the workspace is read alongside the first loads rather than before them:
   // the workspace is at least this plan's size (the host checks it), so the merge table and,
@@ -2488,20 +2488,22 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   const int d = cg * kMergeCols + 4 * (threadIdx.x & 15);
   const float* lse_col = a.part_lse + (int64_t)s0 * R + r;                 // stride R per slot
   const float* o_col = a.part_o + ((int64_t)s0 * R + r) * kDv + d;         // stride R*512 per slot
-  // one pass: kMergeBatch partial results (their lse and 4 columns of o) are loaded at once,
-  // so the loads of a batch overlap; the running max moves per batch
+  // one pass: NB partial results (their lse and 4 columns of o) are loaded at once, so the
+  // loads of a batch overlap; the running max moves per batch.  NB is the plan's largest piece
+  // count rounded up to 4, 8 or 16: a smaller batch holds fewer registers, so more waves (and
+  // more loads) are resident when there are many sequences with few pieces each.
   float M = -INFINITY, L = 0.f;
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; s += kMergeBatch) {
-    float l[kMergeBatch];
-    f32x4_t v[kMergeBatch];
+  for (int s = 0; s < ns; s += NB) {
+    float l[NB];
+    f32x4_t v[NB];
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const bool in = s + u < ns;
       l[u] = in ? lse_col[(int64_t)(s + u) * R] : -INFINITY;
       v[u] = in ? *(const f32x4_t*)(o_col + (int64_t)(s + u) * R * kDv) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    merge_batch(l, v, M, L, acc);
+    merge_batch<NB>(l, v, M, L, acc);
   }
   if (pid != a.plan_id) return;
   const f32x4_t v = acc * (L > 0.f ? 1.0f / L : 0.f);
@@ -2722,13 +2724,22 @@ int launch_merge_dev(const MergeArgs& a, bool out_fp32, void* stream) {
   return (int)hipGetLastError();
 }
 
+template <int NB>
+void launch_merge_t(const MergeArgs& a, bool out_fp32, int grid, hipStream_t s) {
+  if (out_fp32)
+    hipLaunchKernelGGL((merge_kernel<true, NB>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<false, NB>), dim3(grid), dim3(256), 0, s, a);
+}
 int launch_merge(const MergeArgs& a, bool out_fp32, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int grid = a.num_merges * (a.rows / 16) * (kDv / kMergeCols);
-  if (out_fp32)
-    hipLaunchKernelGGL((merge_kernel<true>), dim3(grid), dim3(256), 0, s, a);
+  if (a.max_ns <= 4)
+    launch_merge_t<4>(a, out_fp32, grid, s);
+  else if (a.max_ns <= 8)
+    launch_merge_t<8>(a, out_fp32, grid, s);
   else
-    hipLaunchKernelGGL((merge_kernel<false>), dim3(grid), dim3(256), 0, s, a);
+    launch_merge_t<16>(a, out_fp32, grid, s);
   return (int)hipGetLastError();
 }
 

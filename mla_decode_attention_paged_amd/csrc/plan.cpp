@@ -149,6 +149,7 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
       MergeItem mi{b, slots, splits[b], 0};
       pl.merges.push_back(mi);
       slots += splits[b];
+      pl.merge_max_ns = std::max(pl.merge_max_ns, splits[b]);
     }
   }
   pl.num_partials = slots;
