@@ -1013,15 +1013,10 @@ __device__ __forceinline__ void dma_group_share(const uint16_t* src, uint32_t ld
 //
 // RG = 4 (64 rows): wave rg owns query rows 16*rg..16*rg+15 and all 512 output columns,
 // computes S^T over both blocks of the step and O^T += V^T P^T on 16x16x32 MFMA with
-// K = 32 tokens.  RG = 2 (32 rows) takes the token split below.
-//
-// TS (token split, RG = 2 only): wave w owns rows 16 (w & 1) .. + 15, all 512 columns, and
-// block w >> 1 of every step, with its own online-softmax state, so the two row groups share
-// each step's LDS data without repeating S^T; the two waves of a row group are merged
-// through LDS at the end of a piece.
-template <int RG, bool OUT_F32, bool TS>
+// K = 32 tokens.
+template <int RG, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a) {
-  static_assert(TS ? RG == 2 : RG == kWaves, "32 rows: token split; 64 rows: one row group per wave");
+  static_assert(RG == kWaves, "64 rows: one row group per wave");
   constexpr int SB = 2;                                 // blocks per step
   constexpr int SLOTS = kWaves * kStages / SB;          // step slots (4)
   constexpr int LOADS = kLoadsPerBlock * SB / kWaves;   // DMA instructions per wave and step (9)
@@ -1033,8 +1028,7 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int rg = TS ? (wave & 1) : wave;
-  const int th = TS ? (wave >> 1) : 0;                  // TS: the block of each step this wave takes
+  const int rg = wave;
 
   int worker, rgroup;
   if (a.row_groups == 1) {
@@ -1152,33 +1146,6 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
       }
     };
 
-    // TS: O^T += V^T P^T over the 16 tokens of one block (sb), as in the 16-row kernel:
-    // bf16 weights on a 16x16x16 MFMA (bf16 output) or hi + lo on a 16x16x32 MFMA against
-    // V^T repeated twice (fp32 output)
-    auto accumulate1 = [&](LDS_AS const uint8_t* sb, const float (&s)[8]) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
-        lsum += p[i];
-      }
-      LDS_AS const uint8_t* vp = sb + v_lane;
-      if constexpr (OUT_F32) {
-        const u32x4_t pp = split_hi_lo(p[0], p[1], p[2], p[3]);
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) {
-          const u32x2_t va = lds_tr16(vp + 512 * mb);
-          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u32x4_t{va[0], va[1], va[0], va[1]}),
-                                                          __builtin_bit_cast(bf16x8_t, pp), o[mb], 0, 0, 0);
-        }
-      } else {
-        const i16x4_t pp = __builtin_bit_cast(i16x4_t, u32x2_t{bf16x2_rne(p[0], p[1]), bf16x2_rne(p[2], p[3])});
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb)
-          o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, lds_tr16(vp + 512 * mb)), pp,
-                                                            o[mb], 0, 0, 0);
-      }
-    };
 
     for (int k = 0; k < SLOTS - 1 && k < steps; ++k) issue_step(k);
     int k = 0;
@@ -1209,20 +1176,6 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         if (use1 && kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok1) < 0) use1 = false;
         if ((blk0 < nblk && !use0) || (blk0 + 1 < nblk && !use1)) {
           if (lane == 0) __hip_atomic_fetch_or(a.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if constexpr (TS) {
-          // this wave's block of the step; an unused block is skipped (no other wave of the
-          // row group reads it)
-          if (!(th ? use1 : use0)) continue;
-          st = lds + (k % SLOTS) * (SB * kBlockBytes) + th * kBlockBytes;
-          scores(st, lim - (th ? tok1 : tok0), s);
-          mx = wave_max_over_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-          if (__any(mx > m_ref + kRescaleSlack)) {
-            rescale = true;
-            break;
-          }
-          accumulate1(st, s);
-          continue;
         }
         if (!use0 && !use1) continue;
         st = lds + (k % SLOTS) * (SB * kBlockBytes);
@@ -1255,71 +1208,12 @@ __global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a)
         lsum *= f;
 #pragma unroll
         for (int mb = 0; mb < MBW; ++mb) o[mb] *= f;
-        if constexpr (TS)
-          accumulate1(st, s);
-        else
-          accumulate(st, s);
+        accumulate(st, s);
         ++k;
       }
     }
 
-    if constexpr (TS) {
-      // ---- merge the two waves of each row group (rows 16 rg + n; wave rg took the first
-      // block of every step, wave rg + 2 the second) and write
-      const float lrow = wave_sum_over_groups(lsum);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();                                // slots no longer read
-      asm volatile("" ::: "memory");
-      LDS_AS float* buf = (LDS_AS float*)smem;                     // [4 waves][16 rows][516]
-      LDS_AS float* sm_m = buf + kWaves * 16 * kMergeStride;       // [4][16]
-      LDS_AS float* sm_l = sm_m + kWaves * 16;                     // [4][16]
-      if (g == 0) {
-        sm_m[wave * 16 + n] = m_ref;
-        sm_l[wave * 16 + n] = lrow;
-      }
-      {
-        LDS_AS float* my = buf + (wave * 16 + n) * kMergeStride + 4 * g;
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) *(LDS_AS f32x4_t*)(my + 16 * mb) = o[mb];
-      }
-      __syncthreads();
-      const int rr = threadIdx.x >> 3, dseg = threadIdx.x & 7;     // row of the 32, 4-column piece
-      const int w0 = rr >> 4, w1 = w0 + 2, rn = rr & 15;
-      const float m0 = sm_m[w0 * 16 + rn], m1 = sm_m[w1 * 16 + rn];
-      const float M = fmaxf(m0, m1);
-      const float f0 = (m0 <= kNegBig) ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
-      const float f1 = (m1 <= kNegBig) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-      const float L = f0 * sm_l[w0 * 16 + rn] + f1 * sm_l[w1 * 16 + rn];
-      const float inv = L > 0.f ? 1.0f / L : 0.f;
-      const int grow = rgroup * 16 * RG + rr;
-#pragma unroll
-      for (int j = 0; j < kDv / 32; ++j) {
-        const int d = 4 * dseg + 32 * j;
-        const f32x4_t v = (f0 * *(LDS_AS const f32x4_t*)(buf + (w0 * 16 + rn) * kMergeStride + d) +
-                           f1 * *(LDS_AS const f32x4_t*)(buf + (w1 * 16 + rn) * kMergeStride + d)) * inv;
-        if (slot < 0) {
-          const int64_t off = ((int64_t)b * R + grow) * kDv + d;
-          if (OUT_F32) {
-            *(f32x4_t*)((float*)a.out + off) = v;
-          } else {
-            u32x2_t pkd;
-            pkd[0] = bf16x2_rne(v[0], v[1]);
-            pkd[1] = bf16x2_rne(v[2], v[3]);
-            *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
-          }
-        } else {
-          *(f32x4_t*)(a.part_o + ((int64_t)slot * R + grow) * kDv + d) = v;
-        }
-      }
-      if (dseg == 0) {
-        const float lse = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
-        if (slot < 0) {
-          if (a.lse) a.lse[(int64_t)b * R + grow] = lse;
-        } else {
-          a.part_lse[(int64_t)slot * R + grow] = lse;
-        }
-      }
-    } else {
+    {
     // ---- write: every wave holds its 16 rows complete
       const float l = wave_sum_over_groups(lsum);
       const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -2698,9 +2592,9 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
       hipLaunchKernelGGL((split32_decode_kernel<false, k32Waves>), dim3(grid), dim3(64 * k32Waves), 0, s, a);
   } else if (rows_per_group == 64) {
     if (out_fp32)
-      hipLaunchKernelGGL((group_decode_kernel<4, true, false>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((group_decode_kernel<4, true>), dim3(grid), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((group_decode_kernel<4, false, false>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((group_decode_kernel<4, false>), dim3(grid), dim3(kThreads), 0, s, a);
   } else {
     return (int)hipErrorInvalidValue;
   }
