@@ -53,7 +53,7 @@ WORKLOAD_TEXT = {
     "long": "long-context paged MLA decode: batch 16, q_len 1, 16 heads, 65536 tokens each, page 64, bf16 out",
     "ragged": "ragged paged MLA decode: batch 64, q_len 1, 128 heads, lengths U[1024, 65536], page 64, bf16 out",
 }
-KERNEL_NAME = {16: "split_decode_kernel", 32: "split32_decode_kernel", 64: "group_decode_kernel",
+KERNEL_NAME = {16: "split_decode_kernel", 32: "split32_decode_kernel", 64: "wide_decode_kernel",
                128: "wide_decode_kernel"}
 FLUSH_BYTES = 512 << 20          # read between calls: more than the 256 MB last-level cache
 

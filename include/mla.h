@@ -105,14 +105,15 @@ typedef struct {
   int32_t num_cus;            /* compute units to plan for; 0 = ask the current HIP device */
   int32_t force_splits;       /* 0 = cost model; k > 0 = cut every sequence into min(k, blocks)
                                  near-equal parts, one work-group each (testing the merge) */
-  int32_t rows_per_group;     /* 0 = automatic (128 when R is a multiple of 128; else, with a bf16
-                                 cache, 64 when R is a multiple of 64, else 32 when R is a multiple
+  int32_t rows_per_group;     /* 0 = automatic (128 when R is a multiple of 128, else 64 when R is
+                                 a multiple of 64, else with a bf16 cache 32 when R is a multiple
                                  of 32; else 16);
                                  16, 32, 64 or 128 = query rows per work-group (16: the 16-row
-                                 kernel in R/16 row groups; 32: the 32-row kernel and 64: the
-                                 grouped kernel, bf16 cache only; 128: the wide kernel, 32 rows per
-                                 wave on 32x32 MFMA tiles, bf16 or FP8 rows; R must be a multiple)
-                                 -- a tuning and testing knob */
+                                 kernel in R/16 row groups; 32: the 32-row kernel, bf16 cache
+                                 only; 64 and 128: the wide kernel, 32 rows per wave on 32x32 MFMA
+                                 tiles, bf16 or FP8 rows; R must be a multiple)
+                                 -- a tuning and testing knob; MLA_ERR_UNSUPPORTED for 32 with an
+                                 FP8 cache or R not a multiple */
   int32_t reserved[5];        /* must be zero */
 } mla_plan_options_t;
 

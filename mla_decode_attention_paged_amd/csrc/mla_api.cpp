@@ -188,8 +188,8 @@ mla_status_t mla_plan(const mla_problem_t* problem, const int32_t* cache_seqlens
       return fail(MLA_ERR_INVALID_ARGUMENT, "options.rows_per_group must be 0, 16, 32, 64 or 128");
     if (rpg > 16 && R % rpg != 0)
       return fail(MLA_ERR_UNSUPPORTED, "rows_per_group %d needs R a multiple of it", rpg);
-    if ((rpg == 32 || rpg == 64) && problem->kv_dtype == MLA_KV_FP8_E4M3)
-      return fail(MLA_ERR_UNSUPPORTED, "rows_per_group %d needs a bf16 cache (fp8 rows: 16 or 128)", rpg);
+    if (rpg == 32 && problem->kv_dtype == MLA_KV_FP8_E4M3)
+      return fail(MLA_ERR_UNSUPPORTED, "rows_per_group 32 needs a bf16 cache (fp8 rows: 16, 64 or 128)");
   }
   if (opt.num_cus < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "options.num_cus must be >= 0");
   if (opt.force_splits < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "options.force_splits must be >= 0");

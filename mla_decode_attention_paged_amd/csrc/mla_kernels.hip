@@ -75,10 +75,6 @@ constexpr int kMergeBytes = kWaves * 16 * (kMergeStride + 2) * 4;   // 132,608
 constexpr int kSplitSmemBf16 = kSmemBytes > kMergeBytes ? kSmemBytes : kMergeBytes;
 constexpr int kSplitSmemFp8 = kSmemFp8 > kMergeBytes ? kSmemFp8 : kMergeBytes;
 
-// Chunk-major block layout of the grouped kernel (16-B units): chunk c of token t sits at
-// 16 * c + (t ^ ((c & 1) * kSwz)).
-constexpr int kSwz = 8;
-
 // Physical row of logical token t of sequence b (the page walk).  Returns -1
 // when the block-table entry is outside [0, num_pages).  page_shift = log2(page_size)
 // when the page size is a power of two (shift and mask), else -1 (a division).
@@ -974,286 +970,9 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   }
 }
 
-// Nine loads of one wave's share of a grouped-kernel step: load i reads 16 B per lane at
-// src + 64 i and writes 1 KB at lds + 1024 i.  The instruction offset (64 i) applies to
-// both addresses, so M0 steps by 960 between loads.  As dma_bf16_block: opens with
-// s_waitcnt lgkmcnt(0), saves and restores M0, is hidden from the compiler's counters.
-template <bool NT>
-__device__ __forceinline__ void dma_group_share(const uint16_t* src, uint32_t lds) {
-  uint32_t sv;
-#define MLA_GROUP_DMA(NTS)                                                                        \
-  asm volatile(                                                                                   \
-      "s_waitcnt lgkmcnt(0)\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"               \
-      "global_load_lds_dwordx4 %1, off" NTS "\n\t"                                                \
-      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:64" NTS "\n\t"  \
-      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:128" NTS "\n\t" \
-      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:192" NTS "\n\t" \
-      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:256" NTS "\n\t" \
-      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:320" NTS "\n\t" \
-      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:384" NTS "\n\t" \
-      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:448" NTS "\n\t" \
-      "s_add_u32 m0, m0, 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:512" NTS "\n\t" \
-      "s_mov_b32 m0, %0"                                                                          \
-      : "=&s"(sv)                                                                                 \
-      : "v"(src), "s"(lds)                                                                        \
-      : "memory", "scc")
-  if constexpr (NT)
-    MLA_GROUP_DMA(" nt");
-  else
-    MLA_GROUP_DMA("");
-#undef MLA_GROUP_DMA
-}
-
-// Grouped split-decode kernel for 16 * RG query rows per work-group.  The four
-// waves consume the same KV stream.  Each step is 32 tokens (two 16-token blocks);
-// the work-group keeps four step slots in LDS (three steps in flight), filled by
-// global->LDS DMA split evenly over the waves (9 loads each per step), and moves from
-// step to step behind one barrier that publishes the step's data and frees the slot
-// read in the previous step.
-//
-// RG = 4 (64 rows): wave rg owns query rows 16*rg..16*rg+15 and all 512 output columns,
-// computes S^T over both blocks of the step and O^T += V^T P^T on 16x16x32 MFMA with
-// K = 32 tokens.
-template <int RG, bool OUT_F32>
-__global__ void __launch_bounds__(kThreads, 1) group_decode_kernel(DecodeArgs a) {
-  static_assert(RG == kWaves, "64 rows: one row group per wave");
-  constexpr int SB = 2;                                 // blocks per step
-  constexpr int SLOTS = kWaves * kStages / SB;          // step slots (4)
-  constexpr int LOADS = kLoadsPerBlock * SB / kWaves;   // DMA instructions per wave and step (9)
-  constexpr int MBW = kVBlocks;                         // 16-column output blocks per wave
-  static_assert(LOADS * kWaves == kLoadsPerBlock * SB && LOADS == 9 && SB == 2 && MBW % 8 == 0, "layout");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
-  LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  const int rg = wave;
-
-  int worker, rgroup;
-  if (a.row_groups == 1) {
-    worker = blockIdx.x;
-    rgroup = 0;
-  } else {
-    const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
-    rgroup = y % a.row_groups;
-    worker = (y / a.row_groups) * 8 + x;
-  }
-  if (worker >= a.num_workers) return;
-  if (!schedule_matches(a)) return;
-  const int R = a.rows;
-  const bool stream = a.row_groups == 1;   // KV loads: non-temporal when no other row group re-reads
-  const int row0 = rgroup * 16 * RG + 16 * rg;
-
-  const int k_lane = (g * 16 + (n ^ ((g & 1) * kSwz))) * 16;
-  const int e = n >> 2, qq = n & 3;
-  const int v_lane = ((qq >> 1) * 16 + ((4 * g + e) ^ ((qq >> 1) * kSwz))) * 16 + (qq & 1) * 8;
-  const int ld_token = n ^ ((g & 1) * kSwz);
-
-  const CST_AS int32_t* worker_off = as_const(a.worker_off);
-  const CST_AS int32_t* pieces = as_const(a.pieces);
-  const CST_AS int32_t* seqlens = as_const(a.seqlens);
-  const CST_AS int32_t* block_table = as_const(a.block_table);
-
-  const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
-  for (int pi = p_begin; pi < p_end; ++pi) {
-    const int b = pieces[4 * pi + 0];
-    const int tb = pieces[4 * pi + 1];
-    check_planned_length(a, b, pieces[4 * pi + 2], seqlens[b]);
-    const int te = min(pieces[4 * pi + 2], seqlens[b]);
-    const int slot = pieces[4 * pi + 3];
-    const int nblk = te > tb ? (te - tb + kBlock - 1) / kBlock : 0;
-    const int steps = (nblk + SB - 1) / SB;
-    // end of the tokens this lane's query row sees (causal: the first L - (q_len - 1 - i))
-    const int lim = a.causal ? min(te, seqlens[b] - (a.q_len - 1 - (row0 + n) / a.num_heads)) : te;
-
-    bf16x8_t qf[kKSteps];
-    {
-      const uint16_t* qrow = a.q + ((int64_t)b * R + row0 + n) * kDqk + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = *(const bf16x8_t*)(qrow + 32 * kk);
-    }
-    float m_ref = kNegBig, lsum = 0.f;
-    f32x4_t o[MBW];
-#pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) o[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // this lane's DMA source row for block blk of the piece (blocks past the end and
-    // out-of-range table entries read an in-bounds row; they are not used)
-    auto source = [&](int blk) -> const uint16_t* {
-      const int bb = min(blk, nblk - 1);
-      const int tok0 = tb + kBlock * bb;
-      int64_t base = kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok0);
-      if (base < 0) base = 0;
-      const int t = min(ld_token, te - 1 - tok0);
-      return a.kv + (base + t) * kDqk + 8 * g;
-    };
-    // Wave w moves block w / 2 of the step, 64-B chunk steps 9 (w % 2) .. 9 (w % 2) + 8 (each
-    // load: 16 tokens x 4 chunks of 16 B).
-    auto issue_step = [&](int k) {
-      const int j = wave >> 1, jj0 = LOADS * (wave & 1);
-      const uint16_t* src = source(k * SB + j) + 32 * jj0;
-      const uint32_t dst = (uint32_t)(uintptr_t)(lds + (k % SLOTS) * (SB * kBlockBytes) + j * kBlockBytes + 1024 * jj0);
-      if (stream)
-        dma_group_share<true>(src, dst);
-      else
-        dma_group_share<false>(src, dst);
-    };
-    // S^T = K Q^T for one 16-token block: this lane's 4 scaled scores (log2 units)
-    auto scores = [&](LDS_AS uint8_t* st, int nvalid, float* s) {
-      f32x4_t sacc = f32x4_t{0.f, 0.f, 0.f, 0.f}, acc2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      LDS_AS const uint8_t* kp = st + k_lane;
-#pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) {
-        f32x4_t& acc = (kk & 1) ? acc2 : sacc;
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lds_ld128(kp + 1024 * kk)), qf[kk],
-                                                      acc, 0, 0, 0);
-      }
-      sacc += acc2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = (4 * g + i < nvalid) ? sacc[i] * a.scale_log2 : -INFINITY;
-    };
-    // O^T += V^T P^T for this wave's columns over the step's 32 tokens.  The contraction
-    // index k = 8g + j is token 4g + j of the first block (j < 4) or 4g + j - 4 of the
-    // second: what the S^T layout leaves in this lane and what one transpose read per
-    // block delivers (an unused block's V^T columns were zeroed in the slot).
-    // p = exp2(s - m_ref) goes in as bf16 (bf16 output) or as bf16 hi + lo, two MFMAs
-    // (fp32 output, about 16 mantissa bits).
-    auto accumulate = [&](LDS_AS uint8_t* st, const float (&s)[8]) {
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
-        lsum += p[i];
-      }
-      u32x4_t ph, pl;
-      if constexpr (OUT_F32) {
-        const u32x4_t q0 = split_hi_lo(p[0], p[1], p[2], p[3]), q1 = split_hi_lo(p[4], p[5], p[6], p[7]);
-        ph = u32x4_t{q0[0], q0[1], q1[0], q1[1]};
-        pl = u32x4_t{q0[2], q0[3], q1[2], q1[3]};
-      } else {
-        ph = u32x4_t{bf16x2_rne(p[0], p[1]), bf16x2_rne(p[2], p[3]), bf16x2_rne(p[4], p[5]), bf16x2_rne(p[6], p[7])};
-      }
-      LDS_AS const uint8_t* vp0 = st + v_lane;
-      LDS_AS const uint8_t* vp1 = st + kBlockBytes + v_lane;
-#pragma unroll
-      for (int mb = 0; mb < MBW; ++mb) {
-        const u32x2_t va = lds_tr16(vp0 + 512 * mb), vb = lds_tr16(vp1 + 512 * mb);
-        const bf16x8_t vv = __builtin_bit_cast(bf16x8_t, u32x4_t{va[0], va[1], vb[0], vb[1]});
-        o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, ph), o[mb], 0, 0, 0);
-        if constexpr (OUT_F32)
-          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8_t, pl), o[mb], 0, 0, 0);
-      }
-    };
-
-
-    for (int k = 0; k < SLOTS - 1 && k < steps; ++k) issue_step(k);
-    int k = 0;
-    while (k < steps) {
-      float s[8], mx = 0.f;
-      bool rescale = false, use0 = false, use1 = false;
-      LDS_AS uint8_t* st = lds;
-      for (; k < steps; ++k) {
-        if (steps - 1 - k >= 2) {
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
-        } else if (steps - 1 - k == 1) {
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-        } else {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        // step k is in LDS (each wave waited for its own DMA) and every wave is done with
-        // step k-1, whose slot the prefetch below overwrites.  A bare s_barrier: a fenced
-        // __syncthreads would also wait for the prefetches still in flight.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (k + SLOTS - 1 < steps) issue_step(k + SLOTS - 1);
-        const int blk0 = k * SB;
-        const int tok0 = tb + kBlock * blk0, tok1 = tok0 + kBlock;
-        use0 = blk0 < nblk;
-        use1 = blk0 + 1 < nblk;
-        if (use0 && kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok0) < 0) use0 = false;
-        if (use1 && kv_row_of(block_table, a.bt_stride, a.page_size, a.page_shift, a.num_pages, b, tok1) < 0) use1 = false;
-        if ((blk0 < nblk && !use0) || (blk0 + 1 < nblk && !use1)) {
-          if (lane == 0) __hip_atomic_fetch_or(a.status, kStatusBadPage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (!use0 && !use1) continue;
-        st = lds + (k % SLOTS) * (SB * kBlockBytes);
-        if (!use0 || !use1) {
-          // rare: one block of the step is past the end or has an out-of-range table entry
-          // (its rows may hold anything): zero that block's 512 V^T columns, 2 chunks of 16
-          // tokens x 16 B per 16-column block (every wave reads them all and writes the same
-          // zeros first)
-          LDS_AS uint8_t* zb = st + (use0 ? kBlockBytes : 0);
-          for (int u = lane; u < 32 * MBW; u += 64) *(LDS_AS u32x4_t*)(zb + 16 * u) = u32x4_t{0u, 0u, 0u, 0u};
-        }
-        scores(st, use0 ? lim - tok0 : 0, s);
-        scores(st + kBlockBytes, use1 ? lim - tok1 : 0, s + 4);
-        float m8 = s[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) m8 = fmaxf(m8, s[i]);
-        mx = wave_max_over_groups(m8);
-        if (__any(mx > m_ref + kRescaleSlack)) {
-          rescale = true;
-          break;
-        }
-        accumulate(st, s);
-      }
-      if (!rescale) break;
-      // rare path: the running max grew past the slack; move the reference and rescale
-      {
-        const bool need = mx > m_ref + kRescaleSlack;
-        const float f = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
-        m_ref = need ? mx : m_ref;
-        lsum *= f;
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) o[mb] *= f;
-        accumulate(st, s);
-        ++k;
-      }
-    }
-
-    {
-    // ---- write: every wave holds its 16 rows complete
-      const float l = wave_sum_over_groups(lsum);
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      const int grow = row0 + n;
-#pragma unroll
-      for (int mb = 0; mb < MBW; ++mb) {
-        const int d = 16 * mb + 4 * g;
-        const f32x4_t v = o[mb] * inv;
-        if (slot < 0) {
-          const int64_t off = ((int64_t)b * R + grow) * kDv + d;
-          if (OUT_F32) {
-            *(f32x4_t*)((float*)a.out + off) = v;
-          } else {
-            u32x2_t pkd;
-            pkd[0] = bf16x2_rne(v[0], v[1]);
-            pkd[1] = bf16x2_rne(v[2], v[3]);
-            *(u32x2_t*)((uint16_t*)a.out + off) = pkd;
-          }
-        } else {
-          *(f32x4_t*)(a.part_o + ((int64_t)slot * R + grow) * kDv + d) = v;
-        }
-      }
-      if (g == 0) {
-        const float lse = l > 0.f ? (m_ref + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
-        if (slot < 0) {
-          if (a.lse) a.lse[(int64_t)b * R + grow] = lse;
-        } else {
-          a.part_lse[(int64_t)slot * R + grow] = lse;
-        }
-      }
-    }
-    // the next piece's prefetch reuses the slots: every wave must be done reading them
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
-// Wide split-decode kernel: 128 query rows per work-group, 32 per wave, on 32x32x16 bf16 MFMA.
+// Wide split-decode kernel: 128 query rows per work-group, 32 per wave, on 32x32x16 bf16 MFMA
+// (or 64 rows, each set of 32 shared by two waves that split the output columns; see CW below).
 //
 // The four waves consume every 32-token block of a piece from a shared ring of four LDS slots
 // (three blocks in flight while one is computed); wave w moves token octet w of each block
@@ -1403,9 +1122,15 @@ __device__ __forceinline__ void mfma32_vlast(f32x16_t& acc, const bf16x8_t& a, c
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc) : "v"(a), "v"(b));
 }
 
-template <bool OUT_F32, bool NT, bool FP8>
+template <bool OUT_F32, bool NT, bool FP8, int CW>
 __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) {
   constexpr int kRowB = FP8 ? kF8Row : kRowBytesBf16;    // bytes per cache row
+  // CW waves share each set of 32 rows, each computing the rows' S^T and its own NC of the 16
+  // 32-column O^T tiles: 128 rows per work-group (CW = 1) or 64 (CW = 2).  (With 32 rows, four
+  // waves repeating S^T cost more than the 32-row kernel's split of the tokens.)
+  static_assert(CW == 1 || CW == 2, "waves per 32 rows");
+  constexpr int NC = 16 / CW;                 // O^T tiles per wave
+  constexpr int RW = kWaves / CW;             // 32-row sets per work-group
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kWSmem];
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
 
@@ -1426,8 +1151,9 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
   if (worker >= a.num_workers) return;
   if (!schedule_matches(a)) return;
   const int R = a.rows;
-  const int rbase = rgroup * 128 + 32 * wave;
+  const int rbase = rgroup * (32 * RW) + 32 * (wave / CW);
   const int row = rbase + i;
+  const int tile0 = NC * (wave % CW);         // this wave's first O^T tile (32 columns each)
   LDS_AS uint8_t* const qrope = lds + kWQRope + 4096 * wave + 16 * lane;   // this lane's rope operands
 
   // LDS read offsets within a block.  K, k-step kk: token i, chunk 2 kk + h, at
@@ -1631,11 +1357,11 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
     // is 1 in float32 either way), so that the masked-token score s_hide scales to -inf
     const float c_log2 = fabsf(a.scale_log2) >= 0x1p-100f ? a.scale_log2 : copysignf(0x1p-100f, a.scale_log2);
     const float s_hide = c_log2 > 0.f ? -INFINITY : INFINITY;
-    f32x16_t o[16];
+    f32x16_t o[NC];
     float m_ref, lsum;
     for (int pass = 0;; ++pass) {
 #pragma unroll
-      for (int c = 0; c < 16; ++c)
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int q = 0; q < 16; ++q) o[c][q] = 0.f;
       m_ref = pass ? fmaxf(m_run, kNegBig) : kNegBig;
@@ -1760,6 +1486,9 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
       // lsum, returned as bf16 P^T operands for the two token halves u (K index 8h + 4jp + r is
       // token 16u + 8jp + 4h + r, held in sa[8u + 4jp + r]); pl: the bf16 remainders (fp32 output)
       auto softmax = [&](const f32x16_t& sa, bool first, u32x4_t (&ph)[2], u32x4_t (&pl)[2]) {
+        // sc is rounded before both the maximum and exp2(sc - m_ref) (no fused multiply-add), so
+        // the row's largest score gets a weight of exactly 1
+#pragma clang fp contract(off)
         float sc[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) sc[q] = sa[q] * c_log2;
@@ -1792,15 +1521,18 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
         }
       };
       // O^T += V^T P^T for block kp (P^T in php / plp), with the softmax of the next block's
-      // scores sa spread over its 32 steps (tile t = 16u + cc, u the token half).  V^T tiles
-      // stream through a ring of kWVRing operands; each step is one MFMA (two with fp32 output),
-      // the next tile's two transpose reads and a slice of the softmax, fenced so that the
-      // compiler keeps this order (the MFMAs then run under the softmax's vector work).
+      // scores sa spread over its 2 NC steps (step t: token half u = t / NC, this wave's tile
+      // tile0 + t % NC).  V^T tiles stream through a ring of kWVRing operands; each step is one
+      // MFMA (two with fp32 output), the next tile's two transpose reads and slices of the
+      // softmax (29 in all: one per step with 16 tiles, spread evenly otherwise), fenced so that
+      // the compiler keeps this order (the MFMAs then run under the softmax's vector work).
       auto update = [&](int kp, const u32x4_t (&php)[2], const u32x4_t (&plp)[2], const f32x16_t& sa,
                         u32x4_t (&ph)[2], u32x4_t (&pl)[2]) {
-        LDS_AS const uint8_t* st = lds + (kp % kWSlots) * kWBlockBytes;
+        constexpr int T = 2 * NC;
+        // tile0 is even: its column pair starts 4096 (tile0 / 2) into the block
+        LDS_AS const uint8_t* st = lds + (kp % kWSlots) * kWBlockBytes + 2048 * tile0;
         auto vload = [&](int t) -> bf16x8_t {
-          const int u = t >> 4, cc = t & 15;
+          const int u = t / NC, cc = t % NC;
           const int off = 4096 * (cc >> 1) + 2048 * u;
           const u32x2_t v0 = lds_tr16(st + (vb[0] ^ (64 * (cc & 1))) + off);
           const u32x2_t v1 = lds_tr16(st + (vb[1] ^ (64 * (cc & 1))) + off);
@@ -1810,39 +1542,45 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
 #pragma unroll
         for (int j = 0; j < kWVRing; ++j) vr[j] = vload(j);
         float sc[16], mx = -INFINITY;
-        __builtin_amdgcn_sched_barrier(0);
+        auto slice = [&](int sl) {
+#pragma clang fp contract(off)
+          if (sl < 4) {
 #pragma unroll
-        for (int t = 0; t < 32; ++t) {
-          const int u = t >> 4, cc = t & 15;
-          const bf16x8_t vv = vr[t % kWVRing];
-          o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, __builtin_bit_cast(bf16x8_t, php[u]), o[cc], 0, 0, 0);
-          if constexpr (OUT_F32)
-            o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, __builtin_bit_cast(bf16x8_t, plp[u]), o[cc], 0, 0, 0);
-          if (t + kWVRing < 32) vr[t % kWVRing] = vload(t + kWVRing);
-          // the softmax slice of this step
-          if (t < 4) {
-#pragma unroll
-            for (int q = 4 * t; q < 4 * t + 4; ++q) {
+            for (int q = 4 * sl; q < 4 * sl + 4; ++q) {
               sc[q] = sa[q] * c_log2;
               mx = fmaxf(mx, sc[q]);
             }
-          } else if (t == 4) {
+          } else if (sl == 4) {
             const int xi = __float_as_int(mx);
             const auto sw = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
             mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
             m_run = fmaxf(m_run, mx);
             ovf |= mx > m_ref + kWSlack;
-          } else if (t < 21) {
-            const int q = t - 5;
+          } else if (sl < 21) {
+            const int q = sl - 5;
             sc[q] = __builtin_amdgcn_exp2f(sc[q] - m_ref);
             lsum += sc[q];
-          } else if (t < 29) {
-            const int e = t - 21, uu = e >> 2, e2 = e & 3;      // pair e2 of half uu
+          } else if (sl < 29) {
+            const int e = sl - 21, uu = e >> 2, e2 = e & 3;      // pair e2 of half uu
             const float a0 = sc[8 * uu + 2 * e2], a1 = sc[8 * uu + 2 * e2 + 1];
             ph[uu][e2] = bf16x2_rne(a0, a1);
             if constexpr (OUT_F32)
               pl[uu][e2] = bf16x2_rne(a0 - __uint_as_float(ph[uu][e2] << 16), a1 - __uint_as_float(ph[uu][e2] & 0xFFFF0000u));
           }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const int u = t / NC, cc = t % NC;
+          const bf16x8_t vv = vr[t % kWVRing];
+          o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, __builtin_bit_cast(bf16x8_t, php[u]), o[cc], 0, 0, 0);
+          if constexpr (OUT_F32)
+            o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, __builtin_bit_cast(bf16x8_t, plp[u]), o[cc], 0, 0, 0);
+          if (t + kWVRing < T) vr[t % kWVRing] = vload(t + kWVRing);
+          // the softmax slices of this step
+          const int s0 = T == 32 ? t : 29 * t / T, s1 = T == 32 ? t + 1 : 29 * (t + 1) / T;
+#pragma unroll
+          for (int sl = s0; sl < s1; ++sl) slice(sl);
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -1912,10 +1650,10 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
         // lane (i, h) holds columns 32cc + 8jj + 4h + 0..3 of row i as o[cc][4jj + 0..3]; the
         // destination is the wave's first row (uniform) plus a 32-bit lane offset
         if (slot < 0 && !OUT_F32) {
-          uint8_t* dst = (uint8_t*)((uint16_t*)a.out + ((int64_t)b * R + rbase) * kDv);
+          uint8_t* dst = (uint8_t*)((uint16_t*)a.out + ((int64_t)b * R + rbase) * kDv + 32 * tile0);
           const uint32_t lo = (uint32_t)i * (2 * kDv) + 8u * h;
 #pragma unroll
-          for (int cc = 0; cc < 16; ++cc) {
+          for (int cc = 0; cc < NC; ++cc) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
               *(u32x2_t*)(dst + lo + 64 * cc + 16 * jj) =
@@ -1924,11 +1662,11 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
             __builtin_amdgcn_sched_barrier(0);   // one tile at a time out of the accumulators
           }
         } else {
-          uint8_t* dst = (uint8_t*)(slot < 0 ? (float*)a.out + ((int64_t)b * R + rbase) * kDv
-                                             : a.part_o + ((int64_t)slot * R + rbase) * kDv);
+          uint8_t* dst = (uint8_t*)((slot < 0 ? (float*)a.out + ((int64_t)b * R + rbase) * kDv
+                                              : a.part_o + ((int64_t)slot * R + rbase) * kDv) + 32 * tile0);
           const uint32_t lo = (uint32_t)i * (4 * kDv) + 16u * h;
 #pragma unroll
-          for (int cc = 0; cc < 16; ++cc) {
+          for (int cc = 0; cc < NC; ++cc) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
               *(f32x4_t*)(dst + lo + 128 * cc + 32 * jj) =
@@ -1936,7 +1674,7 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        if (h == 0) {
+        if (h == 0 && wave % CW == 0) {     // the CW waves of a row set hold the same m and l
           const float lse = l > 0.f ? (m_ref + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
           float* lbase = slot < 0 ? a.lse + ((int64_t)b * R + rbase) : a.part_lse + ((int64_t)slot * R + rbase);
           if (slot >= 0 || a.lse) *(float*)((uint8_t*)lbase + 4u * (uint32_t)i) = lse;
@@ -2505,26 +2243,28 @@ void launch_split(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
 // are bf16.  FP8 rows (656 B) are not 64-B aligned and each wave gathers its octet by region, so
 // neighbouring loads share cache lines; with non-temporal loads those lines left the L2 between
 // the two loads and were fetched twice (6% more HBM bytes on the ragged 128-head workload).
-template <bool FP8>
+template <bool FP8, int CW>
 void launch_wide_t(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
   const bool nt = a.row_groups == 1 && !FP8;
   if (out_fp32) {
     if (nt)
-      hipLaunchKernelGGL((wide_decode_kernel<true, true, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((wide_decode_kernel<true, true, FP8, CW>), dim3(grid), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((wide_decode_kernel<true, false, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((wide_decode_kernel<true, false, FP8, CW>), dim3(grid), dim3(kThreads), 0, s, a);
   } else {
     if (nt)
-      hipLaunchKernelGGL((wide_decode_kernel<false, true, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((wide_decode_kernel<false, true, FP8, CW>), dim3(grid), dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((wide_decode_kernel<false, false, FP8>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((wide_decode_kernel<false, false, FP8, CW>), dim3(grid), dim3(kThreads), 0, s, a);
   }
 }
-void launch_wide(const DecodeArgs& a, bool out_fp32, int grid, hipStream_t s) {
-  if (a.kv_fp8)
-    launch_wide_t<true>(a, out_fp32, grid, s);
-  else
-    launch_wide_t<false>(a, out_fp32, grid, s);
+// 128 or 64 rows per work-group: each set of 32 rows computed by one or two waves
+void launch_wide(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, hipStream_t s) {
+  if (rows_per_group == 128) {
+    if (a.kv_fp8) launch_wide_t<true, 1>(a, out_fp32, grid, s); else launch_wide_t<false, 1>(a, out_fp32, grid, s);
+  } else {
+    if (a.kv_fp8) launch_wide_t<true, 2>(a, out_fp32, grid, s); else launch_wide_t<false, 2>(a, out_fp32, grid, s);
+  }
 }
 
 // Read ceiling of the decode's KV stream: every work-group moves its contiguous share of `buf`
@@ -2575,8 +2315,8 @@ int launch_fill_zero(void* p, size_t bytes, void* stream) {
 int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int grid, void* stream,
                   bool device_schedule) {
   hipStream_t s = (hipStream_t)stream;
-  if (rows_per_group == 128 && !device_schedule) {
-    launch_wide(a, out_fp32, grid, s);
+  if ((rows_per_group == 128 || rows_per_group == 64) && !device_schedule) {
+    launch_wide(a, rows_per_group, out_fp32, grid, s);
   } else if (device_schedule || a.kv_fp8) {
     if (rows_per_group != 16) return (int)hipErrorInvalidValue;
     if (device_schedule)
@@ -2590,11 +2330,6 @@ int launch_decode(const DecodeArgs& a, int rows_per_group, bool out_fp32, int gr
       hipLaunchKernelGGL((split32_decode_kernel<true, k32Waves>), dim3(grid), dim3(64 * k32Waves), 0, s, a);
     else
       hipLaunchKernelGGL((split32_decode_kernel<false, k32Waves>), dim3(grid), dim3(64 * k32Waves), 0, s, a);
-  } else if (rows_per_group == 64) {
-    if (out_fp32)
-      hipLaunchKernelGGL((group_decode_kernel<4, true>), dim3(grid), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((group_decode_kernel<4, false>), dim3(grid), dim3(kThreads), 0, s, a);
   } else {
     return (int)hipErrorInvalidValue;
   }

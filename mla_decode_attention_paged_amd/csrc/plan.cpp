@@ -38,19 +38,22 @@ mla_status_t build_plan(const mla_problem_t& p, const int32_t* seqlens, int32_t 
   pl.rows = (int32_t)R;
   // Query rows per work-group: 16 (the 16-row kernel, one wave per 16-token block, in R/16
   // row groups whose work-groups share a token range on one XCD), 32 (the 32-row kernel: each
-  // wave takes its own 16-token blocks for all 32 rows), 64 (the grouped kernel: four waves
-  // share each 32-token step in LDS) or 128 (the wide kernel: 32 rows per wave on 32x32x16 MFMA
-  // tiles, every KV byte read from LDS once per 32 rows).  When not asked for: 128 if R is a
-  // multiple of 128; else, with a bf16 cache, 64 if R is a multiple of 64, else 32 if R is a
-  // multiple of 32; else 16.  Measured on MI355X at R = 128 (ragged workload): about 730 us
-  // with 128 rows, 1,150 us with 64, 1,380 us with 16; at R = 32 (two-token workload, split
-  // launch) 105 us with 32 rows against 119 us with 16.  Larger R comes in as more row groups
-  // over the same token ranges.
+  // wave takes its own 16-token blocks for all 32 rows; bf16 rows), 64 or 128 (the wide kernel:
+  // four waves share each 32-token block in LDS, 32 rows per wave on 32x32x16 MFMA tiles; with
+  // 64 rows two waves share each set of 32 rows and split its output columns).  When not asked
+  // for: 128 if R is a multiple of 128, else 64 if R is a multiple of 64, else (bf16 rows) 32 if
+  // R is a multiple of 32, else 16.  Measured on MI355X at R = 128 (ragged workload): about
+  // 700-730 us with 128 rows, 1,380 us with 16; at R = 64 (batch 32 x 16K tokens) 134 us with
+  // 64 rows against 168 us for a four-wave kernel with 16 rows per wave (FP8 rows: 136 us
+  // against 168 us with 16 rows); at R = 32 (two-token workload, split launch) 105 us with 32
+  // rows against 119 us with 16 (FP8 rows: 94 us with 16 rows against 127 us for the wide
+  // kernel with four waves per 32 rows).  Larger R comes in as more row groups over the same
+  // token ranges.
   const bool bf16 = p.kv_dtype != MLA_KV_FP8_E4M3;
   if (rows_per_group != 0)
     pl.rows_per_group = rows_per_group;
   else
-    pl.rows_per_group = R % 128 == 0 ? 128 : (R % 64 == 0 && bf16) ? 64 : (R % 32 == 0 && bf16) ? 32 : 16;
+    pl.rows_per_group = R % 128 == 0 ? 128 : R % 64 == 0 ? 64 : (R % 32 == 0 && bf16) ? 32 : 16;
   pl.row_groups = (int32_t)(R / pl.rows_per_group);
   pl.granule = kBlock;
 

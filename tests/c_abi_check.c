@@ -64,8 +64,12 @@ int main(void) {
   CHECK(mla_plan(&p, lens, &opt, &plan) == MLA_ERR_UNSUPPORTED && plan == NULL);
   p.num_heads = 128;
   p.kv_dtype = MLA_KV_FP8_E4M3;
-  opt.rows_per_group = 64;   /* the grouped kernel reads bf16 rows only */
+  opt.rows_per_group = 32;   /* the 32-row kernel reads bf16 rows only */
   CHECK(mla_plan(&p, lens, &opt, &plan) == MLA_ERR_UNSUPPORTED);
+  opt.rows_per_group = 64;   /* FP8 rows, 64 per work-group: the wide kernel, two row groups */
+  CHECK(mla_plan(&p, lens, &opt, &plan) == MLA_OK);
+  CHECK(mla_plan_get_info(plan, &info) == MLA_OK && info.rows_per_group == 64 && info.row_groups == 2);
+  mla_plan_destroy(plan);
   opt.rows_per_group = 0;   /* FP8 rows at R = 128: the wide kernel, one row group */
   CHECK(mla_plan(&p, lens, &opt, &plan) == MLA_OK);
   CHECK(mla_plan_get_info(plan, &info) == MLA_OK && info.rows_per_group == 128 && info.row_groups == 1);

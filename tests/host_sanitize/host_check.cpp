@@ -82,10 +82,10 @@ static bool fuzz_one(int iter) {
   std::memset(&opt, 0, sizeof opt);
   opt.num_cus = 1 + (int32_t)rnd(rnd(4) == 0 ? 16 : 1024);
   opt.force_splits = rnd(6) == 0 ? 1 + (int32_t)rnd(1000) : 0;
-  const int rpg_opts[] = {0, 16, 32, 64};
-  opt.rows_per_group = rpg_opts[rnd(4)];
+  const int rpg_opts[] = {0, 16, 32, 64, 128};
+  opt.rows_per_group = rpg_opts[rnd(5)];
   const bool rpg_ok = opt.rows_per_group <= 16 ||
-                      (R % opt.rows_per_group == 0 && p.kv_dtype == MLA_KV_BF16);
+                      (R % opt.rows_per_group == 0 && (opt.rows_per_group != 32 || p.kv_dtype == MLA_KV_BF16));
   mla_plan_t plan = nullptr;
   const mla_status_t st = mla_plan(&p, lens.data(), &opt, &plan);
   if (!rpg_ok) {

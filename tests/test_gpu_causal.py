@@ -58,9 +58,9 @@ def test_causal_edge_lengths(heads, q_len, out_fp32):
                                           (128, 2, 64)])
 @pytest.mark.parametrize("out_fp32", [True, False])
 def test_causal_rows_per_group(heads, q_len, rpg, out_fp32):
-    """The causal limit in every kernel layout asked for explicitly: the grouped kernel's
-    token split (32 rows) and its 64-row form, and the 16-row kernel where the default
-    would be the grouped kernel."""
+    """The causal limit in every kernel layout asked for explicitly: the 32-row kernel, the wide
+    kernel with 64 rows (two waves per 32 rows) and 128, and the 16-row kernel where the default
+    would be a wider one."""
     prob = gen.make_problem(batch=len(EDGE_LENGTHS), q_len=q_len, num_heads=heads, page_size=16,
                             lengths=EDGE_LENGTHS, seed=24, tail="nan", extra_pages=2, out_fp32=out_fp32)
     r = Runner(prob, causal=True, rows_per_group=rpg)

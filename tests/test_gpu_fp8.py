@@ -210,22 +210,24 @@ def test_fp8_out_of_range_block_table_entry_drops_its_tokens(heads):
 
 
 @pytest.mark.parametrize("out_fp32", [True, False])
-def test_fp8_wide_and_16_row_kernels_agree(out_fp32):
-    """The 128-row kernel (the default at 128 heads) against the 16-row kernel forced on the same
-    FP8 problem: both within the oracle's bounds, and with fp32 output within 2 ulps of each
-    other's scale (the two sum the same products in different orders)."""
-    prob = gen.make_problem(batch=4, q_len=1, num_heads=128, page_size=64, lengths=[4000, 1, 700, 2049], seed=58,
-                            out_fp32=out_fp32, kv_format="fp8")
+@pytest.mark.parametrize("heads,q_len", [(128, 1), (64, 1), (32, 2)])
+def test_fp8_wide_and_16_row_kernels_agree(out_fp32, heads, q_len):
+    """The wide kernel (the default at 128 and 64 rows) against the 16-row kernel forced on the
+    same FP8 problem: both within the oracle's bounds, and their lse within 1e-5 of each other
+    (the two sum the same products in different orders)."""
+    prob = gen.make_problem(batch=4, q_len=q_len, num_heads=heads, page_size=64, lengths=[4000, 1, 700, 2049],
+                            seed=58, out_fp32=out_fp32, kv_format="fp8")
     rw = Runner(prob)
     r16 = Runner(prob, rows_per_group=16)
-    assert rw.plan.info()["rows_per_group"] == 128 and r16.plan.info()["rows_per_group"] == 16
+    R = heads * q_len
+    assert rw.plan.info()["rows_per_group"] == R and r16.plan.info()["rows_per_group"] == 16
     rw()
     r16()
     ow, lw = rw.results()
     o16, l16 = r16.results()
     ref_o, ref_l = oracle(prob)
     wabs = None if out_fp32 else softmax_abs_v(prob)
-    check(ow, lw, ref_o, ref_l, out_fp32, "fp8 128 rows", wabs)
+    check(ow, lw, ref_o, ref_l, out_fp32, f"fp8 {R} rows", wabs)
     check(o16, l16, ref_o, ref_l, out_fp32, "fp8 16 rows", wabs)
     assert np.max(np.abs(lw - l16)) <= 1e-5
 

@@ -188,8 +188,8 @@ def test_edge_lengths_nan_tails(page, out_fp32):
                                           (64, 80, "fp8")])
 def test_non_power_of_two_pages(heads, page, kv):
     """Page sizes that are multiples of 16 but not powers of two take the division in the
-    page walk (powers of two take a shift): the grouped kernel, the 16-row kernel at R = 32
-    and the FP8 path."""
+    page walk (powers of two take a shift): the wide kernel (128 rows), the 32-row kernel and the
+    FP8 path in the wide kernel (64 rows)."""
     prob = gen.make_problem(batch=3, q_len=1, num_heads=heads, page_size=page, lengths=[page * 7 + 5, 33, 2000],
                             seed=23, tail="nan", extra_pages=2, kv_format=kv)
     out, lse = run(prob)
@@ -198,8 +198,11 @@ def test_non_power_of_two_pages(heads, page, kv):
 
 
 @pytest.mark.parametrize("out_fp32", [False, True])
-def test_single_token_returns_v_row(out_fp32):
-    prob = gen.make_problem(batch=4, q_len=2, num_heads=16, page_size=64, lengths=[1, 1, 1, 1], seed=6,
+@pytest.mark.parametrize("heads,q_len", [(16, 1), (16, 2), (32, 2), (128, 1)])
+def test_single_token_returns_v_row(out_fp32, heads, q_len):
+    """One cached token: its weight is exactly 1, so every row of the output is its V row, bit for
+    bit (R = 16, 32, 64 and 128: each work-group width)."""
+    prob = gen.make_problem(batch=4, q_len=q_len, num_heads=heads, page_size=64, lengths=[1, 1, 1, 1], seed=6,
                             tail="nan", out_fp32=out_fp32)
     out, lse = run(prob)
     for b in range(prob.batch):
@@ -255,10 +258,10 @@ def test_many_pieces_per_work_group(out_fp32):
 
 @pytest.mark.parametrize("heads,rpg", [(64, 64), (32, 32), (128, 64), (128, 128)])
 @pytest.mark.parametrize("out_fp32", [True, False])
-def test_grouped_kernel_many_pieces(heads, rpg, out_fp32):
-    """The grouped kernel walking many pieces per work-group (the slots and exchange
-    buffers reused from piece to piece), with empty, one-token and page-crossing
-    sequences among them."""
+def test_wide_and_32_row_kernels_many_pieces(heads, rpg, out_fp32):
+    """The 32-row and wide kernels (64 and 128 rows) walking many pieces per work-group (the
+    slots and exchange buffers reused from piece to piece), with empty, one-token and
+    page-crossing sequences among them."""
     rng = np.random.default_rng(12)
     lengths = rng.integers(0, 300, size=90)
     lengths[::17] = 0
@@ -271,7 +274,7 @@ def test_grouped_kernel_many_pieces(heads, rpg, out_fp32):
     r()
     out, lse = r.results()
     ref_o, ref_l = oracle(prob)
-    check_short_contexts(out, lse, ref_o, ref_l, out_fp32, f"grouped many pieces H={heads} rpg={rpg}",
+    check_short_contexts(out, lse, ref_o, ref_l, out_fp32, f"many pieces H={heads} rpg={rpg}",
                          None if out_fp32 else softmax_abs_v(prob))
 
 
@@ -287,9 +290,10 @@ def test_more_query_rows(heads, q_len):
                                           (64, 2, 64), (128, 1, 16), (64, 1, 16), (128, 2, 64), (128, 2, 16),
                                           (128, 1, 128), (64, 2, 128), (128, 2, 128), (16, 8, 128)])
 @pytest.mark.parametrize("out_fp32", [True, False])
-def test_grouped_kernel(heads, q_len, rpg, out_fp32):
-    """Rows per work-group asked for through the plan option: the grouped kernel (32 or 64),
-    and the 16-row kernel in several row groups where 64 would be chosen by default."""
+def test_rows_per_group_option(heads, q_len, rpg, out_fp32):
+    """Rows per work-group asked for through the plan option: the 32-row kernel, the wide kernel
+    with 64 rows (two waves per 32 rows) and 128, in several row groups, and the 16-row kernel
+    where a wider one would be chosen by default."""
     prob = gen.make_problem(batch=4, q_len=q_len, num_heads=heads, page_size=64, lengths=[700, 2000, 33, 1],
                             seed=18, tail="nan", extra_pages=1, out_fp32=out_fp32)
     r = Runner(prob, rows_per_group=rpg)
@@ -297,7 +301,7 @@ def test_grouped_kernel(heads, q_len, rpg, out_fp32):
     r()
     out, lse = r.results()
     ref_o, ref_l = oracle(prob)
-    check_short_contexts(out, lse, ref_o, ref_l, out_fp32, f"grouped H={heads} S_q={q_len} rpg={rpg}",
+    check_short_contexts(out, lse, ref_o, ref_l, out_fp32, f"H={heads} S_q={q_len} rpg={rpg}",
                          None if out_fp32 else softmax_abs_v(prob))
 
 
@@ -399,8 +403,8 @@ def test_out_of_range_block_table_entry_is_flagged():
 
 @pytest.mark.parametrize("heads,rpg", [(128, 0), (128, 64), (32, 32), (64, 16)])
 def test_out_of_range_entry_drops_one_block(heads, rpg):
-    """Page size 16 (one block per page): an out-of-range entry makes one block of a 32-token
-    step of the grouped kernel unused (the first block of a step in sequence 0, the second in
+    """Page size 16 (one block per page): an out-of-range entry makes one 16-token half of a
+    32-token block of the wide kernel unused (the first half in sequence 0, the second in
     sequence 1); its tokens are dropped and the status bit is set.  Unmapped pages hold NaN."""
     prob = gen.make_problem(batch=2, q_len=1, num_heads=heads, page_size=16, lengths=[640, 650], seed=22,
                             tail="nan", extra_pages=2)

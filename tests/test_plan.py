@@ -139,11 +139,10 @@ def test_rows_per_group_rejected():
     with pytest.raises(B.MlaError):
         B.Plan(prob, [10], num_cus=256, rows_per_group=24)
     fp8 = B.make_problem(1, 1, 128, 64, 1, 1, kv_fp8=True)
-    for rpg in (32, 64):
-        with pytest.raises(B.MlaError) as ei:
-            B.Plan(fp8, [10], num_cus=256, rows_per_group=rpg)  # the grouped kernel reads bf16 rows only
-        assert ei.value.status == B.MLA_ERR_UNSUPPORTED
-    for rpg in (16, 128):                                       # FP8 rows: the 16-row and the wide kernel
+    with pytest.raises(B.MlaError) as ei:
+        B.Plan(fp8, [10], num_cus=256, rows_per_group=32)       # the 32-row kernel reads bf16 rows only
+    assert ei.value.status == B.MLA_ERR_UNSUPPORTED
+    for rpg in (16, 64, 128):                                   # FP8 rows: the 16-row and the wide kernel
         assert B.Plan(fp8, [10], num_cus=256, rows_per_group=rpg).info()["rows_per_group"] == rpg
     with pytest.raises(B.MlaError) as ei:
         B.Plan(B.make_problem(1, 1, 64, 64, 1, 1), [10], num_cus=256, rows_per_group=128)   # R = 64
@@ -151,11 +150,12 @@ def test_rows_per_group_rejected():
 
 
 def test_default_rows_per_group():
-    """128 rows per work-group when R is a multiple of 128; else, with a bf16 cache, 64 when R is a
-    multiple of 64, else 32 when R is a multiple of 32; else 16."""
+    """128 rows per work-group when R is a multiple of 128, else 64 when R is a multiple of 64; else,
+    with a bf16 cache, 32 when R is a multiple of 32; else 16."""
     for heads, q_len, kv, want in [(16, 1, 0, 16), (16, 2, 0, 32), (48, 1, 0, 16), (64, 1, 0, 64), (128, 1, 0, 128),
-                                   (32, 2, 0, 64), (64, 1, 1, 16), (128, 1, 1, 128), (128, 2, 0, 128), (128, 2, 1, 128),
-                                   (64, 2, 0, 128), (64, 2, 1, 128), (96, 2, 0, 64), (96, 2, 1, 16), (16, 2, 1, 16),
+                                   (32, 2, 0, 64), (64, 1, 1, 64), (128, 1, 1, 128), (128, 2, 0, 128), (128, 2, 1, 128),
+                                   (64, 2, 0, 128), (64, 2, 1, 128), (96, 2, 0, 64), (96, 2, 1, 64), (16, 2, 1, 16),
+                                   (48, 2, 1, 16),
                                    (32, 1, 0, 32), (48, 2, 0, 32), (8, 4, 0, 32)]:
         prob = B.make_problem(1, q_len, heads, 64, 1, 1, kv_fp8=bool(kv))
         info = B.Plan(prob, [10], num_cus=256).info()
