@@ -1,5 +1,8 @@
-// gfx950 kernels for paged MLA decode: split decode, merge of split results,
-// and a debug gather that shares the decode kernel's page walk.
+// gfx950 kernels for paged MLA decode: split decode (three kernels by query rows per
+// work-group: split_decode_kernel for 16, split32_decode_kernel for 32, wide_decode_kernel for
+// 64 and 128), merge of split results (merge_kernel, or inside split_decode_kernel when one
+// launch is asked for), a read-only stream probe, and a debug gather that shares the decode
+// kernel's page walk.
 //
 // Split-decode kernel, one work-group (4 waves) per piece list from the planner.
 // Each wave streams its own 16-token KV blocks (blocks w, w+4, w+8, ... of a
