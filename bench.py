@@ -14,7 +14,9 @@ in HBM.  Prints one JSON line:
   timing_us    = per-call event percentiles, the cache-flushed per-call time, the device-scheduled
                  entry point (mla_decode_devplan) on the same inputs
   configs      = every workload (tiny, paged, two_token, long, ragged) with bf16 and with FP8 cache
-                 rows: call and kernel time, flushed call time, GB/s and fraction of 8 TB/s
+                 rows: call and kernel time, flushed call time, GB/s and fraction of 8 TB/s, the
+                 kernel's TFLOP/s and fraction of the 2.5 PFLOP/s bf16 matrix peak (the other bound
+                 at 128 rows), and the counters' HBM bytes where they were taken
   compute      = the call's matrix work as TFLOP/s, and for the long workload the pages' H20 figure
                  at that shape (context only)
   cpu_baseline = the fp64 oracle on a bounded sample of the headline workload, on this host's
@@ -55,6 +57,7 @@ WORKLOAD_TEXT = {
 }
 KERNEL_NAME = {16: "split_decode_kernel", 32: "split32_decode_kernel", 64: "wide_decode_kernel",
                128: "wide_decode_kernel"}
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of MI355X (the second bound at 128 rows)
 FLUSH_BYTES = 512 << 20          # read between calls: more than the 256 MB last-level cache
 
 
@@ -192,6 +195,7 @@ def config_table(stream, flush, steps: int = 20):
                 "frac_kernel": round(algo / (kern * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "frac_call_flushed": round(algo / (flushed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "kernel_tflops": round(flops(prob) / (kern * 1e-6) / 1e12, 1),
+                "frac_mfma_kernel": round(flops(prob) / (kern * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                 "kernel": KERNEL_NAME[info["rows_per_group"]], "rows_per_group": info["rows_per_group"],
                 "row_groups": info["row_groups"], "pieces": info["num_segments"], "partials": info["num_partials"],
             }
