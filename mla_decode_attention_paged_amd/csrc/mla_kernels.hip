@@ -98,7 +98,8 @@ __device__ __forceinline__ int64_t kv_row_of(TablePtr block_table, int bt_stride
 }
 
 // Host schedule: the workspace must hold the schedule of the plan the launch was made from
-// (its id is written by the upload).  Otherwise nothing is read from it: the status word gets
+// (its id is written by the upload).  Otherwise nothing but the worker's piece range (two words
+// inside the workspace, read alongside the id) is read from it: the status word gets
 // kStatusPlanMismatch and every work-group returns.
 __device__ __forceinline__ bool schedule_matches(const DecodeArgs& a) {
   if (*as_const(a.ws_plan_id) == a.plan_id) return true;
@@ -428,7 +429,6 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
     worker = (y / a.row_groups) * 8 + x;
   }
   if (worker >= a.num_workers) return;
-  if (!DEV && !schedule_matches(a)) return;
   const int row0 = rgroup * 16;
   const int R = a.rows;
   const bool stream = a.row_groups == 1;   // KV loads: non-temporal when no other row group re-reads
@@ -874,7 +874,10 @@ __global__ void __launch_bounds__(kThreads, 1) split_decode_kernel(DecodeArgs a)
   };
 
   if constexpr (!DEV) {
+    // the worker's piece range is read together with the plan id (both lie inside the workspace
+    // whatever schedule it holds); the pieces themselves only once the id matches
     const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
+    if (!schedule_matches(a)) return;
     for (int pi = p_begin; pi < p_end; ++pi)
     {
       const int b = pieces[4 * pi + 0], slot = pieces[4 * pi + 3];
@@ -1152,7 +1155,6 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
     worker = (y / a.row_groups) * 8 + x;
   }
   if (worker >= a.num_workers) return;
-  if (!schedule_matches(a)) return;
   const int R = a.rows;
   const int rbase = rgroup * (32 * RW) + 32 * (wave / CW);
   const int row = rbase + i;
@@ -1189,7 +1191,9 @@ __global__ void __launch_bounds__(kThreads, 1) wide_decode_kernel(DecodeArgs a) 
   const CST_AS int32_t* block_table = as_const(a.block_table);
   const uint8_t* const kv8 = (const uint8_t*)a.kv;
 
+  // the piece range is read with the plan id, the pieces once the id matches
   const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
+  if (!schedule_matches(a)) return;
   for (int pi = p_begin; pi < p_end; ++pi) {
     const int b = pieces[4 * pi + 0];
     const int tb = pieces[4 * pi + 1];
@@ -1750,7 +1754,6 @@ __global__ void __launch_bounds__(64 * NW, 1) split32_decode_kernel(DecodeArgs a
     worker = (y / a.row_groups) * 8 + x;
   }
   if (worker >= a.num_workers) return;
-  if (!schedule_matches(a)) return;
   const int R = a.rows;
   const int row0 = 32 * rgroup;                    // this work-group's 32 query rows
   const bool stream = a.row_groups == 1;           // KV loads: non-temporal when no other row group re-reads
@@ -1784,7 +1787,9 @@ __global__ void __launch_bounds__(64 * NW, 1) split32_decode_kernel(DecodeArgs a
   const CST_AS int32_t* seqlens = as_const(a.seqlens);
   const CST_AS int32_t* block_table = as_const(a.block_table);
 
+  // the piece range is read with the plan id, the pieces once the id matches
   const int p_begin = worker_off[worker], p_end = worker_off[worker + 1];
+  if (!schedule_matches(a)) return;
   for (int pi = p_begin; pi < p_end; ++pi) {
     const int b = pieces[4 * pi + 0], tb = pieces[4 * pi + 1], slot = pieces[4 * pi + 3];
     check_planned_length(a, b, pieces[4 * pi + 2], seqlens[b]);
