@@ -171,8 +171,11 @@ def time_runner(r, stream, steps: int, flush=None, flushed_calls: int = 10):
     return call, kern, (float(np.median(fl)) if fl else None)
 
 
-def config_table(stream, flush, steps: int = 20):
-    """Every workload with bf16 and FP8 cache rows."""
+def config_table(stream, flush, steps: int = 20, warm_ms: float = 100.0, rep_ms: float = 20.0, reps: int = 3):
+    """Every workload with bf16 and FP8 cache rows.  Each is warmed up for about `warm_ms` of
+    back-to-back calls (the first tens of calls after a switch of workload run slower while the
+    clocks settle), then timed `reps` times over at least `steps` calls and `rep_ms`; the
+    medians of the reps are reported."""
     import torch
     from mla_decode_attention_paged_amd.device import Runner
     from mla_decode_attention_paged_amd import inputs as gen
@@ -183,9 +186,22 @@ def config_table(stream, flush, steps: int = 20):
             prob, dev = device_problem(name, kv)
             r = Runner(prob, dev=dev)
             info = r.plan.info()
-            for _ in range(30):
+            for _ in range(10):
                 r()
-            call, kern, flushed = time_runner(r, stream, steps, flush)
+            e0, e1 = _events()
+            e0.record(stream)
+            for _ in range(10):
+                r()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per_call_ms = max(e0.elapsed_time(e1) / 10, 1e-3)
+            for _ in range(max(30, int(warm_ms / per_call_ms))):
+                r()
+            n = max(steps, int(rep_ms / per_call_ms))
+            runs = [time_runner(r, stream, n) for _ in range(reps)]
+            call = float(np.median([x[0] for x in runs]))
+            kern = float(np.median([x[1] for x in runs]))
+            flushed = time_runner(r, stream, 1, flush)[2]
             algo = algorithmic_bytes(prob)
             entry = {
                 "us_per_call": round(call, 2), "kernel_us": round(kern, 2), "call_flushed_us": round(flushed, 2),
