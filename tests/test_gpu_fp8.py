@@ -130,7 +130,7 @@ def test_fp8_forced_splits(force, heads):
     check(out, lse, ref_o, ref_l, True, f"fp8 force={force} H={heads}")
 
 
-@pytest.mark.parametrize("heads", [16, 64])
+@pytest.mark.parametrize("heads", [16, 32, 64])
 def test_fp8_causal_two_token(heads):
     prob = gen.make_problem(batch=5, q_len=2, num_heads=heads, page_size=16, lengths=[1, 2, 17, 300, 3000], seed=55,
                             tail="nan", extra_pages=1, out_fp32=True, kv_format="fp8")
