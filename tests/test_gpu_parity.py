@@ -236,8 +236,11 @@ def test_page_permutation_bit_identical():
     assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
 
 
-@pytest.mark.parametrize("force", [1, 2, 3, 1000])
+@pytest.mark.parametrize("force", [1, 2, 3, 4, 5, 8, 9, 16, 17, 1000])
 def test_forced_split_counts_agree(force):
+    """Every sequence cut into min(force, blocks) pieces: the merge reads its partials in batches
+    of 4, 8 or 16 (the plan's largest piece count rounded up), so 4/5, 8/9 and 16/17 pieces sit
+    on both sides of each batch size, and 1000 takes several batches of 16."""
     prob = gen.make_problem(batch=3, q_len=1, num_heads=16, page_size=64, lengths=[4096, 100, 2500], seed=9)
     out, lse = run(prob, force_splits=force)
     ref_o, ref_l = oracle(prob)
